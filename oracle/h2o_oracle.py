@@ -27,7 +27,7 @@ Readings taken where the pages are silent or garbled:
   whose position is older than P - W; victims are the k smallest by
   (score, slot index); chunk token i goes to the i-th smallest freed slot;
 * a newly inserted token starts with its own in-chunk summed weight as score;
-* h2o-norm divides the score by the age t - t(j) with t = P + S.
+* h2o-norm divides the score by the age t - t(j) with t = P + S, in float32.
 """
 from __future__ import annotations
 
@@ -128,9 +128,12 @@ def selection_scores(state: H2OState, S: int, score_mode: str = "h2o"):
     if score_mode == "h2o":
         return state.phi
     if score_mode == "h2o_norm":
+        # The ratio decides which slot is evicted, so it is formed in float32, the
+        # precision the kernel forms it in (IEEE division of the float32 score by the
+        # exact float32 age).
         t_now = state.P + S
-        age = (t_now - state.pos).astype(np.float64)
-        return state.phi / age
+        age = (t_now - state.pos).astype(np.float32)
+        return (state.phi.astype(np.float32) / age).astype(np.float64)
     raise ValueError(score_mode)
 
 
