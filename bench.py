@@ -1,0 +1,214 @@
+"""Throughput of the H2O chunk path: attention + summed weights + score update +
+eviction/insert, over a whole synthetic sequence, on one MI355X.
+
+A step is one full sequence of the workload pushed through the three C-ABI calls
+chunk by chunk from an empty cache (default: Qwen3-4B attention shape, 32 query /
+8 KV heads, head_dim 128, bf16, chunk 1024, cache 8192, recent window 256, 64k
+tokens = 64 chunks).  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  `value` is F6 TFLOP/s: 6*d*Hq*(visible query/key pairs),
+i.e. QK^T and PV for the output plus the QK^T recompute for the summed weights.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "H2O chunk-attn+score+evict TFLOP/s & tokens/s (chunk 1k, 64k ctx), % roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_chunk1k_ctx64k_traffic.txt")
+ATTN_SOURCE = os.path.join(ROOT, "h2o_sparse_attention_amd", "csrc", "attn_bf16.hip")
+
+
+def pairs_per_head(n_before: int, S: int) -> int:
+    """Visible (query, key) pairs of one chunk for one query head."""
+    return S * n_before + S * (S + 1) // 2
+
+
+def chunk_schedule(wl):
+    n = 0
+    out = []
+    for _ in range(wl.n_chunks):
+        out.append(n)
+        n = min(wl.capacity, n + wl.chunk)
+    return out
+
+
+def source_digest() -> str:
+    return hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(launch_flops_unused=None):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE):
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256_16") != source_digest():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The fp64 oracle on steady (full-cache) chunks of the same workload."""
+    import oracle
+    import workloads as W
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"),
+                      default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    c = 16
+    s = W.steady_state(wl, 0, start=c * wl.chunk, seed=0)
+    x = W.chunk_inputs(wl, 0, c)
+    flops = 0.0
+    chunks = 0
+    t0 = time.perf_counter()
+    while True:
+        st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+        oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window)
+        chunks += 1
+        flops += 6.0 * wl.head_dim * wl.n_q_heads * pairs_per_head(wl.capacity, wl.chunk)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{chunks} steady chunk(s) of {wl.name} (full cache, "
+                      f"{wl.capacity}+{wl.chunk} keys, fp64 NumPy), {dt:.1f} s",
+            "tokens_per_s": chunks * wl.chunk / dt, "ms_per_chunk": dt / chunks * 1e3}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import h2o_sparse_attention_amd as h2o
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    assert not wl.decode and wl.layers == 1, "bench runs a single-layer prefill workload"
+    dev = torch.device("cuda:0")
+    dims = h2o.H2ODims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity,
+                       wl.recent_window, wl.dtype)
+    dt = dims.torch_dtype
+    t_gen = time.perf_counter()
+    inputs = []
+    for c in range(wl.n_chunks):
+        x = W.chunk_inputs(wl, 0, c)
+        inputs.append(tuple(torch.from_numpy(x[k]).to(dev, dt) for k in ("q", "k", "v")))
+    print(f"[bench] generated {wl.n_chunks} chunks in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+    cache = h2o.H2OCache(dims, dev)
+    B, Hq, Hkv, D, NC, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity, wl.chunk
+    bufs = {"out": torch.empty(B, Hq, S, D, dtype=dt, device=dev),
+            "lse": torch.empty(B, Hq, S, dtype=torch.float32, device=dev),
+            "colsum_cache": torch.empty(B, Hkv, NC, dtype=torch.float32, device=dev),
+            "colsum_new": torch.empty(B, Hkv, S, dtype=torch.float32, device=dev),
+            "freed_slots": torch.empty(B, Hkv, S, dtype=torch.int32, device=dev)}
+
+    def run_sequence():
+        cache.reset()
+        for q, k, v in inputs:
+            h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs)
+
+    for _ in range(args.warmup):
+        run_sequence()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    n_launch = args.steps * wl.n_chunks
+    timers = {k: h2o.KernelTimer(k, n_launch) for k in ("attn", "colsum", "update", "select",
+                                                       "insert")}
+    for t in timers.values():
+        t.__enter__()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_sequence()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for t in timers.values():
+        t.__exit__(None, None, None)
+    ms_per_step = elapsed / args.steps * 1e3
+
+    # sanity on the last chunk: every query row's weights sum to 1
+    total = bufs["colsum_cache"].sum().item() + bufs["colsum_new"].sum().item()
+    expect = B * Hkv * S * (Hq // Hkv)
+    if abs(total - expect) > 1e-3 * expect:
+        print(f"[bench] WARNING: summed weights {total} != {expect}", file=sys.stderr)
+
+    sched = chunk_schedule(wl)
+    pairs = sum(pairs_per_head(n, S) for n in sched)
+    f6 = 6.0 * D * Hq * B * pairs
+    f4 = 4.0 * D * Hq * B * pairs
+    tflops = f6 / (ms_per_step * 1e-3) / 1e12
+    tokens_per_s = B * wl.seq_len / (ms_per_step * 1e-3)
+
+    attn = timers["attn"]
+    attn_flops_per_launch = f4 / wl.n_chunks          # QK^T + PV, averaged over the chunks
+    attn_ms = attn.mean_ms
+    achieved = attn_flops_per_launch / (attn_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": "attn_bf16_kernel<128>",
+                "launches": attn.launches, "mean_launch_us": round(attn_ms * 1e3, 2)}
+    kernel_us = {k: round(t.mean_ms * 1e3, 2) for k, t in timers.items()}
+    steady_n = [i for i, n in enumerate(sched) if n == NC]
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_budget)
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "capacity": NC, "recent_window": wl.recent_window,
+                   "chunk": S, "seq_len": wl.seq_len, "chunks": wl.n_chunks,
+                   "parallelism": "single-gpu"},
+        "tokens_per_s": round(tokens_per_s, 1),
+        "tflops_f4": round(f4 / (ms_per_step * 1e-3) / 1e12, 3),
+        "frac_bf16_peak_f6": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "kernel_mean_us": kernel_us,
+        "steady_chunks": len(steady_n),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+"""H2O chunked sparse attention on MI355X: Python binding of libh2o.
+
+Argument marshalling only: every step runs in the HIP kernels of
+``csrc/`` behind the C ABI of ``include/h2o.h``.  PyTorch supplies device
+memory and streams.  Layouts and semantics are those of the C header.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from ._native import (  # noqa: F401
+    H2O_BF16, H2O_ERR_CAPACITY, H2O_ERR_HIP, H2O_ERR_INVALID_ARG, H2O_ERR_UNSUPPORTED,
+    H2O_ERR_WORKSPACE, H2O_F32, H2O_OK, H2O_SCORE_H2O, H2O_SCORE_H2O_NORM, KERNEL_IDS,
+    LIB_PATH, CacheStruct, Dims, H2OError, check, lib,
+)
+
+SCORE_MODES = {"h2o": H2O_SCORE_H2O, "h2o_norm": H2O_SCORE_H2O_NORM}
+_TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+_C_DTYPES = {"bf16": H2O_BF16, "f32": H2O_F32}
+
+
+@dataclass(frozen=True)
+class H2ODims:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    capacity: int
+    recent_window: int
+    dtype: str = "bf16"          # "bf16" | "f32"
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPES[self.dtype]
+
+    def c(self) -> Dims:
+        return Dims(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.capacity,
+                    self.recent_window, _C_DTYPES[self.dtype])
+
+
+class H2OCache:
+    """One layer's cache: device tensors k, v [B,Hkv,N_C,d], pos int32 and score fp32
+    [B,Hkv,N_C], plus the host-side count of filled slots and the next position."""
+
+    def __init__(self, dims: H2ODims, device="cuda"):
+        B, Hkv, NC, d = dims.batch, dims.n_kv_heads, dims.capacity, dims.head_dim
+        self.dims = dims
+        self.k = torch.zeros(B, Hkv, NC, d, dtype=dims.torch_dtype, device=device)
+        self.v = torch.zeros(B, Hkv, NC, d, dtype=dims.torch_dtype, device=device)
+        self.pos = torch.full((B, Hkv, NC), -1, dtype=torch.int32, device=device)
+        self.score = torch.zeros(B, Hkv, NC, dtype=torch.float32, device=device)
+        self.n_valid = 0
+        self.next_pos = 0
+
+    def reset(self):
+        self.n_valid = 0
+        self.next_pos = 0
+
+    def load(self, k, v, pos, score, n_valid, next_pos):
+        self.k.copy_(k)
+        self.v.copy_(v)
+        self.pos.copy_(pos)
+        self.score.copy_(score)
+        self.n_valid = int(n_valid)
+        self.next_pos = int(next_pos)
+
+    def c(self) -> CacheStruct:
+        return CacheStruct(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(),
+                           self.score.data_ptr(), self.n_valid)
+
+
+def _stream_ptr(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, shape, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype} != {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def workspace_bytes(dims: H2ODims, chunk_len: int) -> int:
+    return int(lib.h2o_workspace_bytes(ctypes.byref(dims.c()), chunk_len))
+
+
+def chunk_attn(cache: H2OCache, chunk_start: int, q, k_new, v_new, sm_scale: float,
+               out=None, lse=None, colsum_cache=None, colsum_new=None, workspace=None,
+               stream=None):
+    """h2o_chunk_attn: returns (out, lse, colsum_cache, colsum_new)."""
+    d = cache.dims
+    B, Hq, Hkv, D, NC = d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim, d.capacity
+    S = q.shape[2]
+    dev = cache.k.device
+    _need(q, (B, Hq, S, D), d.torch_dtype, "q")
+    _need(k_new, (B, Hkv, S, D), d.torch_dtype, "k_new")
+    _need(v_new, (B, Hkv, S, D), d.torch_dtype, "v_new")
+    if out is None:
+        out = torch.empty(B, Hq, S, D, dtype=d.torch_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(B, Hq, S, dtype=torch.float32, device=dev)
+    if colsum_cache is None:
+        colsum_cache = torch.empty(B, Hkv, NC, dtype=torch.float32, device=dev)
+    if colsum_new is None:
+        colsum_new = torch.empty(B, Hkv, S, dtype=torch.float32, device=dev)
+    _need(out, (B, Hq, S, D), d.torch_dtype, "out")
+    _need(lse, (B, Hq, S), torch.float32, "lse")
+    _need(colsum_cache, (B, Hkv, NC), torch.float32, "colsum_cache")
+    _need(colsum_new, (B, Hkv, S), torch.float32, "colsum_new")
+    ws_need = workspace_bytes(d, S)
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.h2o_chunk_attn(ctypes.byref(d.c()), ctypes.byref(cache.c()), int(chunk_start), S,
+                             float(sm_scale), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                             out.data_ptr(), lse.data_ptr(), colsum_cache.data_ptr(),
+                             colsum_new.data_ptr(), ws_ptr, ws_len, _stream_ptr(stream, dev)))
+    return out, lse, colsum_cache, colsum_new
+
+
+def update_scores(cache: H2OCache, colsum_cache, stream=None):
+    """h2o_update_scores: cache.score[..., :n_valid] += colsum_cache[..., :n_valid]."""
+    d = cache.dims
+    _need(colsum_cache, (d.batch, d.n_kv_heads, d.capacity), torch.float32, "colsum_cache")
+    check(lib.h2o_update_scores(ctypes.byref(d.c()), ctypes.byref(cache.c()),
+                                colsum_cache.data_ptr(), _stream_ptr(stream, cache.k.device)))
+
+
+def evict_and_insert(cache: H2OCache, chunk_start: int, k_new, v_new, colsum_new,
+                     freed_slots=None, score_mode="h2o", stream=None):
+    """h2o_evict_and_insert: returns freed_slots [B,Hkv,S] and advances cache.n_valid."""
+    d = cache.dims
+    B, Hkv, D = d.batch, d.n_kv_heads, d.head_dim
+    S = k_new.shape[2]
+    dev = cache.k.device
+    _need(k_new, (B, Hkv, S, D), d.torch_dtype, "k_new")
+    _need(v_new, (B, Hkv, S, D), d.torch_dtype, "v_new")
+    _need(colsum_new, (B, Hkv, S), torch.float32, "colsum_new")
+    if freed_slots is None:
+        freed_slots = torch.empty(B, Hkv, S, dtype=torch.int32, device=dev)
+    _need(freed_slots, (B, Hkv, S), torch.int32, "freed_slots")
+    cs = cache.c()
+    check(lib.h2o_evict_and_insert(ctypes.byref(d.c()), ctypes.byref(cs), int(chunk_start), S,
+                                   SCORE_MODES[score_mode], k_new.data_ptr(), v_new.data_ptr(),
+                                   colsum_new.data_ptr(), freed_slots.data_ptr(), None, 0,
+                                   _stream_ptr(stream, dev)))
+    cache.n_valid = cs.n_valid
+    cache.next_pos = int(chunk_start) + S
+    return freed_slots
+
+
+def step(cache: H2OCache, q, k_new, v_new, sm_scale: float, score_mode="h2o", bufs=None,
+         stream=None):
+    """One chunk through the three calls at position cache.next_pos.  ``bufs`` (a dict
+    holding out, lse, colsum_cache, colsum_new, freed_slots, workspace) is reused if given."""
+    b = bufs or {}
+    P = cache.next_pos
+    out, lse, cs_cache, cs_new = chunk_attn(cache, P, q, k_new, v_new, sm_scale,
+                                            b.get("out"), b.get("lse"), b.get("colsum_cache"),
+                                            b.get("colsum_new"), b.get("workspace"), stream)
+    update_scores(cache, cs_cache, stream)
+    freed = evict_and_insert(cache, P, k_new, v_new, cs_new, b.get("freed_slots"), score_mode,
+                             stream)
+    return {"out": out, "lse": lse, "colsum_cache": cs_cache, "colsum_new": cs_new,
+            "freed_slots": freed}
+
+
+class KernelTimer:
+    """Sum of per-launch durations of one library kernel, from HIP events the library
+    records on the launch stream (h2o_kernel_timer_start / _stop)."""
+
+    def __init__(self, kernel: str, max_launches: int = 65536):
+        self.kid = KERNEL_IDS[kernel]
+        self.max = max_launches
+        self.total_ms = 0.0
+        self.launches = 0
+
+    def __enter__(self):
+        check(lib.h2o_kernel_timer_start(self.kid, self.max))
+        return self
+
+    def __exit__(self, *exc):
+        ms = ctypes.c_double()
+        cnt = ctypes.c_int64()
+        check(lib.h2o_kernel_timer_stop(self.kid, ctypes.byref(ms), ctypes.byref(cnt)))
+        self.total_ms, self.launches = ms.value, cnt.value
+        return False
+
+    @property
+    def mean_ms(self) -> float:
+        return self.total_ms / max(1, self.launches)

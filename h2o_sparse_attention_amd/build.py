@@ -1,0 +1,72 @@
+"""Build libh2o.so (HIP, gfx950) in-tree: h2o_sparse_attention_amd/lib/libh2o.so.
+
+Usage: python h2o_sparse_attention_amd/build.py [--verbose]
+(run as a file: importing the package loads the library this script builds)
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OBJ_DIR = os.path.join(HERE, "_build")
+LIB_DIR = os.path.join(HERE, "lib")
+LIB_PATH = os.path.join(LIB_DIR, "libh2o.so")
+
+SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "evict.hip", "decode.hip"]
+ARCH = "gfx950"
+CXXFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+    "-Wall", "-Wno-unused-function",
+    # no packed fp32 instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # the host pass does not know the packed-fp32 target feature; that warning is expected
+    out = "\n".join(l for l in p.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{out}")
+    if verbose and out.strip():
+        print(out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libh2o.so; return its path."""
+    hipcc = _hipcc()
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([hipcc, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

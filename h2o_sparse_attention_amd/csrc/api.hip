@@ -1,0 +1,302 @@
+// C ABI of libh2o: argument validation, kernel dispatch, optional timers.
+// Entry points are declared and documented in include/h2o.h.
+#include "h2o_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+namespace h2o {
+namespace {
+
+thread_local std::string g_error;
+
+h2o_status_t fail(h2o_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+h2o_status_t ok() {
+    g_error.clear();
+    return H2O_OK;
+}
+
+h2o_status_t check_hip(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(H2O_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return H2O_OK;
+}
+
+h2o_status_t validate_dims(const h2o_dims_t* d) {
+    if (!d) return fail(H2O_ERR_INVALID_ARG, "dims is NULL");
+    if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+        return fail(H2O_ERR_INVALID_ARG, "batch, n_q_heads and n_kv_heads must be >= 1");
+    if (d->n_q_heads % d->n_kv_heads != 0)
+        return fail(H2O_ERR_INVALID_ARG, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                    d->n_q_heads, d->n_kv_heads);
+    if (d->dtype != H2O_F32 && d->dtype != H2O_BF16)
+        return fail(H2O_ERR_UNSUPPORTED, "dtype %d is not supported", d->dtype);
+    if (d->head_dim != 64 && d->head_dim != 128)
+        return fail(H2O_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", d->head_dim);
+    if (d->capacity < 1 || d->capacity > kMaxCapacity)
+        return fail(H2O_ERR_UNSUPPORTED, "capacity %d outside 1..%d", d->capacity, kMaxCapacity);
+    if (d->recent_window < 0) return fail(H2O_ERR_INVALID_ARG, "recent_window must be >= 0");
+    const long long groups = (long long)d->batch * d->n_kv_heads;
+    if (groups > 65535 || (long long)d->batch * d->n_q_heads > (1LL << 24))
+        return fail(H2O_ERR_UNSUPPORTED, "batch x heads too large");
+    return H2O_OK;
+}
+
+h2o_status_t validate_cache(const h2o_dims_t* d, const h2o_cache_t* c) {
+    if (!c) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+    if (!c->k || !c->v || !c->pos || !c->score)
+        return fail(H2O_ERR_INVALID_ARG, "cache k, v, pos and score must be non-NULL");
+    if (c->n_valid < 0 || c->n_valid > d->capacity)
+        return fail(H2O_ERR_INVALID_ARG, "n_valid %d outside 0..capacity (%d)", c->n_valid,
+                    d->capacity);
+    return H2O_OK;
+}
+
+h2o_status_t validate_chunk(int64_t chunk_start, int32_t chunk_len) {
+    if (chunk_len < 1) return fail(H2O_ERR_INVALID_ARG, "chunk_len must be >= 1");
+    if (chunk_len > (1 << 20)) return fail(H2O_ERR_UNSUPPORTED, "chunk_len too large");
+    if (chunk_start < 0) return fail(H2O_ERR_INVALID_ARG, "chunk_start must be >= 0");
+    if (chunk_start + (int64_t)chunk_len > 2147483647LL)
+        return fail(H2O_ERR_UNSUPPORTED, "chunk_start + chunk_len exceeds INT32_MAX");
+    return H2O_OK;
+}
+
+// Kernel timers --------------------------------------------------------------
+struct Timer {
+    bool on = false;
+    int max = 0;
+    int used = 0;
+    std::vector<hipEvent_t> ev;
+};
+Timer g_timer[H2O_KERNEL_COUNT];
+
+void destroy_events(Timer& t) {
+    for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+    t.ev.clear();
+    t.on = false;
+    t.used = 0;
+    t.max = 0;
+}
+
+}  // namespace
+
+void timer_begin(int kernel, hipStream_t s) {
+    Timer& t = g_timer[kernel];
+    if (t.on && t.used < t.max) (void)hipEventRecord(t.ev[2 * t.used], s);
+}
+
+void timer_end(int kernel, hipStream_t s) {
+    Timer& t = g_timer[kernel];
+    if (t.on && t.used < t.max) {
+        (void)hipEventRecord(t.ev[2 * t.used + 1], s);
+        ++t.used;
+    }
+}
+
+}  // namespace h2o
+
+using namespace h2o;
+
+extern "C" {
+
+int32_t h2o_abi_version(void) { return H2O_ABI_VERSION; }
+
+const char* h2o_last_error(void) { return g_error.c_str(); }
+
+size_t h2o_workspace_bytes(const h2o_dims_t* dims, int32_t chunk_len) {
+    if (validate_dims(dims) != H2O_OK || chunk_len < 1) return 0;
+    if (chunk_len == 1 && dims->dtype == H2O_BF16 && dims->head_dim == 128)
+        return decode_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads,
+                                      dims->capacity);
+    return 0;
+}
+
+h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
+                            int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                            const void* q, const void* k_new, const void* v_new, void* out,
+                            float* lse, float* colsum_cache, float* colsum_new,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    h2o_status_t st;
+    if ((st = validate_dims(dims)) != H2O_OK) return st;
+    if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
+    if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
+    if (!q || !k_new || !v_new || !out || !lse || !colsum_cache || !colsum_new)
+        return fail(H2O_ERR_INVALID_ARG, "q, k_new, v_new, out, lse and colsum buffers must be non-NULL");
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+        return fail(H2O_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+    const size_t ws_need = h2o_workspace_bytes(dims, chunk_len);
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
+        return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", ws_need,
+                    workspace ? workspace_bytes : (size_t)0);
+
+    ChunkArgs a;
+    a.q = q;
+    a.kc = cache->k;
+    a.vc = cache->v;
+    a.kn = k_new;
+    a.vn = v_new;
+    a.pos = cache->pos;
+    a.out = out;
+    a.lse = lse;
+    a.cs_cache = colsum_cache;
+    a.cs_new = colsum_new;
+    a.B = dims->batch;
+    a.Hq = dims->n_q_heads;
+    a.Hkv = dims->n_kv_heads;
+    a.G = dims->n_q_heads / dims->n_kv_heads;
+    a.D = dims->head_dim;
+    a.S = chunk_len;
+    a.NC = dims->capacity;
+    a.n = cache->n_valid;
+    a.P = (int)chunk_start;
+    a.sm_scale = sm_scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int rows = a.B * a.Hkv;
+
+    if (a.n < a.NC) {
+        if ((st = check_hip(launch_zero_f32(colsum_cache, a.NC - a.n, a.NC, rows, a.n, s),
+                            "zero colsum tail")) != H2O_OK)
+            return st;
+    }
+    if (ws_need > 0) {
+        timer_begin(H2O_KERNEL_DECODE, s);
+        hipError_t e = launch_decode(a, workspace, s);
+        timer_end(H2O_KERNEL_DECODE, s);
+        if ((st = check_hip(e, "decode attention launch")) != H2O_OK) return st;
+        return ok();
+    }
+    const bool bf16 = dims->dtype == H2O_BF16;
+    timer_begin(H2O_KERNEL_ATTN, s);
+    hipError_t e = bf16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
+    timer_end(H2O_KERNEL_ATTN, s);
+    if ((st = check_hip(e, "attention launch")) != H2O_OK) return st;
+    timer_begin(H2O_KERNEL_COLSUM, s);
+    e = bf16 ? launch_colsum_bf16(a, s) : launch_colsum_f32(a, s);
+    timer_end(H2O_KERNEL_COLSUM, s);
+    if ((st = check_hip(e, "colsum launch")) != H2O_OK) return st;
+    return ok();
+}
+
+h2o_status_t h2o_update_scores(const h2o_dims_t* dims, const h2o_cache_t* cache,
+                               const float* colsum_cache, void* stream) {
+    h2o_status_t st;
+    if ((st = validate_dims(dims)) != H2O_OK) return st;
+    if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
+    if (!colsum_cache) return fail(H2O_ERR_INVALID_ARG, "colsum_cache is NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    timer_begin(H2O_KERNEL_UPDATE, s);
+    hipError_t e = launch_update_scores(cache->score, colsum_cache,
+                                        dims->batch * dims->n_kv_heads, dims->capacity,
+                                        cache->n_valid, s);
+    timer_end(H2O_KERNEL_UPDATE, s);
+    if ((st = check_hip(e, "update launch")) != H2O_OK) return st;
+    return ok();
+}
+
+h2o_status_t h2o_evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache,
+                                  int64_t chunk_start, int32_t chunk_len, int32_t score_mode,
+                                  const void* k_new, const void* v_new,
+                                  const float* colsum_new, int32_t* freed_slots, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    h2o_status_t st;
+    if ((st = validate_dims(dims)) != H2O_OK) return st;
+    if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
+    if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
+    if (!k_new || !v_new || !colsum_new || !freed_slots)
+        return fail(H2O_ERR_INVALID_ARG, "k_new, v_new, colsum_new and freed_slots must be non-NULL");
+    if (score_mode != H2O_SCORE_H2O && score_mode != H2O_SCORE_H2O_NORM)
+        return fail(H2O_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
+    const int n = cache->n_valid, S = chunk_len, NC = dims->capacity, W = dims->recent_window;
+    const int k = n + S - NC;
+    if (k > 0 && (long long)S + W > NC)
+        return fail(H2O_ERR_CAPACITY,
+                    "cannot evict %d slots: capacity %d < chunk_len %d + recent_window %d", k, NC,
+                    S, W);
+    EvictArgs a;
+    a.kc = cache->k;
+    a.vc = cache->v;
+    a.pos = cache->pos;
+    a.score = cache->score;
+    a.kn = k_new;
+    a.vn = v_new;
+    a.cs_new = colsum_new;
+    a.freed = freed_slots;
+    a.B = dims->batch;
+    a.Hkv = dims->n_kv_heads;
+    a.D = dims->head_dim;
+    a.S = S;
+    a.NC = NC;
+    a.n = n;
+    a.W = W;
+    a.P = (int)chunk_start;
+    a.elem_bytes = dims->dtype == H2O_BF16 ? 2 : 4;
+    a.score_mode = score_mode;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    timer_begin(H2O_KERNEL_SELECT, s);
+    hipError_t e = launch_select(a, s);
+    timer_end(H2O_KERNEL_SELECT, s);
+    if ((st = check_hip(e, "select launch")) != H2O_OK) return st;
+    timer_begin(H2O_KERNEL_INSERT, s);
+    e = launch_insert(a, s);
+    timer_end(H2O_KERNEL_INSERT, s);
+    if ((st = check_hip(e, "insert launch")) != H2O_OK) return st;
+    cache->n_valid = n + S < NC ? n + S : NC;
+    return ok();
+}
+
+h2o_status_t h2o_kernel_timer_start(int32_t kernel, int32_t max_launches) {
+    if (kernel < 0 || kernel >= H2O_KERNEL_COUNT)
+        return fail(H2O_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+    if (max_launches < 1 || max_launches > (1 << 20))
+        return fail(H2O_ERR_INVALID_ARG, "max_launches outside 1..2^20");
+    Timer& t = g_timer[kernel];
+    destroy_events(t);
+    t.ev.resize(2 * (size_t)max_launches);
+    for (size_t i = 0; i < t.ev.size(); ++i) {
+        hipError_t e = hipEventCreate(&t.ev[i]);
+        if (e != hipSuccess) {
+            t.ev.resize(i);
+            destroy_events(t);
+            return check_hip(e, "hipEventCreate");
+        }
+    }
+    t.max = max_launches;
+    t.used = 0;
+    t.on = true;
+    return ok();
+}
+
+h2o_status_t h2o_kernel_timer_stop(int32_t kernel, double* total_ms, int64_t* launches) {
+    if (kernel < 0 || kernel >= H2O_KERNEL_COUNT)
+        return fail(H2O_ERR_INVALID_ARG, "unknown kernel id %d", kernel);
+    if (!total_ms || !launches) return fail(H2O_ERR_INVALID_ARG, "NULL output pointer");
+    Timer& t = g_timer[kernel];
+    double sum = 0.0;
+    h2o_status_t st = H2O_OK;
+    for (int i = 0; i < t.used && st == H2O_OK; ++i) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(t.ev[2 * i + 1]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]);
+        st = check_hip(e, "kernel timer");
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = t.used;
+    destroy_events(t);
+    return st == H2O_OK ? ok() : st;
+}
+
+}  // extern "C"

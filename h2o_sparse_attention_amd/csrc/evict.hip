@@ -1,0 +1,225 @@
+// Score accumulation, heavy-hitter selection and chunk insertion.
+//
+// "Learning how to Forget: Fine-tuning for Long-Context Sparse Attention",
+// montaan paper page, "Improvements to Heavy-Hitter Oracle (H2O)", item 2: the
+// H2O score is the running sum of the summed attention weights, optionally
+// normalised by age, and new content overwrites the slots of smallest score.
+#include "h2o_internal.h"
+
+#include <climits>
+
+namespace h2o {
+namespace {
+
+// ------------------------------------------------------------------ update
+__global__ __launch_bounds__(256) void update_scores_kernel(float* __restrict__ score,
+                                                            const float* __restrict__ cs,
+                                                            int rows, int NC, int n) {
+    const size_t total = (size_t)rows * n;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (size_t)gridDim.x * blockDim.x) {
+        const size_t r = e / n, j = e % n;
+        const size_t idx = r * NC + j;
+        score[idx] += cs[idx];
+    }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, size_t per_row,
+                                                   size_t stride, int rows, size_t offset) {
+    const size_t total = (size_t)rows * per_row;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (size_t)gridDim.x * blockDim.x)
+        p[(e / per_row) * stride + offset + e % per_row] = 0.f;
+}
+
+// ------------------------------------------------------------------ select
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr uint32_t kIneligible = 0xFFFFFFFEu;   // filled slot inside the recent window
+constexpr uint32_t kAbsent = 0xFFFFFFFFu;       // slot >= n: never a victim
+constexpr uint32_t kMaxEligible = 0xFF800001u;  // just above +inf: NaN scores rank here
+
+// Monotone map float -> uint32 (a < b  =>  key(a) < key(b); -0 == +0).
+__device__ __forceinline__ uint32_t order_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return u < kMaxEligible ? u : kMaxEligible;
+}
+
+__device__ __forceinline__ int wave_count(bool pred) {
+    return __popcll(__ballot(pred));
+}
+
+// Exclusive prefix sum over the block in thread order; also returns the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sWave, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) sWave[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        const int x = sWave[w];
+        before += w < wave ? x : 0;
+        total += x;
+    }
+    __syncthreads();
+    return before + incl - v;
+}
+
+// One workgroup per (b, kv head); KPT consecutive slots per thread, held in
+// registers.  The k-th smallest key T is found by a most-significant-bit-first
+// radix-2 select: 32 rounds, each counting keys below a candidate with wave
+// ballots.  Victims are every key below T plus the lowest-index slots equal
+// to T, which gives the (score, slot index) order exactly.
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
+    __shared__ int sCnt[2][kSelWaves];
+    __shared__ int sWave[kSelWaves];
+    const int bg = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = a.n, S = a.S, NC = a.NC;
+    const int n_new = min(NC, n + S);
+    const int k = max(0, n + S - NC);
+    int32_t* freed = a.freed + (size_t)bg * S;
+
+    if (k > 0) {
+        const float* sc = a.score + (size_t)bg * NC;
+        const int32_t* ps = a.pos + (size_t)bg * NC;
+        const int thr = a.P - a.W;            // eligible iff t(j) < P - W
+        const int t_now = a.P + S;
+        const int j0 = tid * KPT;
+        uint32_t key[KPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int j = j0 + e;
+            uint32_t kv = kAbsent;
+            if (j < n) {
+                const int pj = ps[j];
+                float v = sc[j];
+                if (a.score_mode == H2O_SCORE_H2O_NORM) v = v / (float)(t_now - pj);
+                kv = pj < thr ? order_key(v) : kIneligible;
+            }
+            key[e] = kv;
+        }
+
+        uint32_t T = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t X = T | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) cnt += wave_count(key[e] < X);
+            if (lane == 0) sCnt[bit & 1][wave] = cnt;
+            __syncthreads();
+            int tot = 0;
+#pragma unroll
+            for (int w = 0; w < kSelWaves; ++w) tot += sCnt[bit & 1][w];
+            if (tot < k) T = X;
+        }
+        // T is the k-th smallest key: count(< T) < k <= count(<= T).
+        int my_less = 0, my_eq = 0;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            my_less += key[e] < T;
+            my_eq += (key[e] == T) && (j0 + e < n);
+        }
+        int less_total, eq_total;
+        block_exclusive_scan(my_less, sWave, less_total);
+        int eq_before = block_exclusive_scan(my_eq, sWave, eq_total);
+        const int need_eq = k - less_total;
+        int my_v = 0;
+        bool vic[KPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const bool eq = (key[e] == T) && (j0 + e < n);
+            vic[e] = key[e] < T || (eq && eq_before < need_eq);
+            eq_before += eq;
+            my_v += vic[e];
+        }
+        int v_total;
+        int out_idx = block_exclusive_scan(my_v, sWave, v_total);
+#pragma unroll
+        for (int e = 0; e < KPT; ++e)
+            if (vic[e]) freed[out_idx++] = j0 + e;
+    }
+    for (int e = tid; e < n_new - n; e += kSelThreads) freed[k + e] = n + e;
+}
+
+// ------------------------------------------------------------------ insert
+constexpr int kInsTokens = 16;
+
+__global__ __launch_bounds__(256) void insert_kernel(EvictArgs a) {
+    const int bg = blockIdx.y;
+    const int tok0 = blockIdx.x * kInsTokens;
+    const int units = a.D * a.elem_bytes / 16;    // 16-byte units per row
+    const int32_t* freed = a.freed + (size_t)bg * a.S;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const size_t row_units_cache = (size_t)bg * a.NC * units;
+    const size_t row_units_chunk = (size_t)bg * a.S * units;
+    u32x4* kc = static_cast<u32x4*>(a.kc);
+    u32x4* vc = static_cast<u32x4*>(a.vc);
+    const u32x4* kn = static_cast<const u32x4*>(a.kn);
+    const u32x4* vn = static_cast<const u32x4*>(a.vn);
+    for (int u = threadIdx.x; u < kInsTokens * units; u += blockDim.x) {
+        const int tok = tok0 + u / units, part = u % units;
+        if (tok >= a.S) break;
+        const int slot = freed[tok];
+        kc[row_units_cache + (size_t)slot * units + part] = kn[row_units_chunk + (size_t)tok * units + part];
+        vc[row_units_cache + (size_t)slot * units + part] = vn[row_units_chunk + (size_t)tok * units + part];
+    }
+    if (threadIdx.x < kInsTokens) {
+        const int tok = tok0 + threadIdx.x;
+        if (tok < a.S) {
+            const int slot = freed[tok];
+            a.pos[(size_t)bg * a.NC + slot] = a.P + tok;
+            a.score[(size_t)bg * a.NC + slot] = a.cs_new[(size_t)bg * a.S + tok];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_update_scores(float* score, const float* cs, int rows, int NC, int n,
+                                hipStream_t s) {
+    const size_t total = (size_t)rows * n;
+    if (total == 0) return hipSuccess;
+    const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+    hipLaunchKernelGGL(update_scores_kernel, dim3(blocks), dim3(256), 0, s, score, cs, rows, NC, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* p, size_t per_row, size_t stride, int rows, size_t offset,
+                           hipStream_t s) {
+    const size_t total = (size_t)rows * per_row;
+    if (total == 0) return hipSuccess;
+    const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, p, per_row, stride, rows, offset);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const EvictArgs& a, hipStream_t s) {
+    const dim3 grid(a.B * a.Hkv), block(kSelThreads);
+    const int kpt = (a.NC + kSelThreads - 1) / kSelThreads;
+    if (kpt <= 1) hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, s, a);
+    else if (kpt <= 2) hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, s, a);
+    else if (kpt <= 4) hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, s, a);
+    else if (kpt <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, s, a);
+    else if (kpt <= 16) hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(select_kernel<32>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_insert(const EvictArgs& a, hipStream_t s) {
+    const dim3 grid((a.S + kInsTokens - 1) / kInsTokens, a.B * a.Hkv), block(256);
+    hipLaunchKernelGGL(insert_kernel, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace h2o

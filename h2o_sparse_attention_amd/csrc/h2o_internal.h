@@ -1,0 +1,62 @@
+// Internal declarations shared by the HIP translation units of libh2o.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/h2o.h"
+
+namespace h2o {
+
+// Problem description handed to every kernel (plain values, device pointers).
+struct ChunkArgs {
+    const void* q;          // [B][Hq][S][D]
+    const void* kc;         // [B][Hkv][NC][D]  cache keys
+    const void* vc;         // [B][Hkv][NC][D]  cache values
+    const void* kn;         // [B][Hkv][S][D]   chunk keys
+    const void* vn;         // [B][Hkv][S][D]   chunk values
+    const int32_t* pos;     // [B][Hkv][NC]     t(b,g,j)
+    void* out;              // [B][Hq][S][D]
+    float* lse;             // [B][Hq][S]
+    float* cs_cache;        // [B][Hkv][NC]
+    float* cs_new;          // [B][Hkv][S]
+    int B, Hq, Hkv, G, D, S, NC, n;
+    int P;                  // absolute position of the chunk's first query row
+    float sm_scale;
+};
+
+struct EvictArgs {
+    void* kc;
+    void* vc;
+    int32_t* pos;
+    float* score;
+    const void* kn;
+    const void* vn;
+    const float* cs_new;
+    int32_t* freed;
+    int B, Hkv, D, S, NC, n, W, P, elem_bytes, score_mode;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_attn_bf16(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_colsum_bf16(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_colsum_f32(const ChunkArgs& a, hipStream_t s);
+hipError_t launch_zero_f32(float* p, size_t count_per_row, size_t row_stride, int rows,
+                           size_t offset, hipStream_t s);
+hipError_t launch_update_scores(float* score, const float* cs, int rows, int NC, int n,
+                                hipStream_t s);
+hipError_t launch_select(const EvictArgs& a, hipStream_t s);
+hipError_t launch_insert(const EvictArgs& a, hipStream_t s);
+
+// Decode (S = 1) specialisation.
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int NC);
+hipError_t launch_decode(const ChunkArgs& a, void* ws, hipStream_t s);
+
+// Kernel timers (api.hip): bracket a launch with events when enabled.
+void timer_begin(int kernel, hipStream_t s);
+void timer_end(int kernel, hipStream_t s);
+
+constexpr int kMaxCapacity = 32768;
+
+}  // namespace h2o

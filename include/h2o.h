@@ -1,0 +1,179 @@
+/*
+ * h2o.h -- C ABI of the H2O chunked sparse-attention library for MI355X (gfx950).
+ *
+ * The method: "Learning how to Forget: Fine-tuning for Long-Context Sparse
+ * Attention" (montaan paper page).  A fixed-capacity KV cache per layer and KV
+ * head holds N_C slots; slot j carries the token position t(b,h,j) and the H2O
+ * score phi_h2o(b,h,j), the accumulated summed attention weights.  A chunk of S
+ * query tokens attends to the filled slots and to its own causal keys; the same
+ * computation returns the summed attention weights sum_i m_{b,h,i,j} ("Kernel
+ * Support Needs"); those are added to the scores, and the chunk is written
+ * into the slots of smallest score ("Improvements to Heavy-Hitter Oracle
+ * (H2O)", item 2).
+ *
+ * Memory.  Every pointer is a device pointer allocated and owned by the caller.
+ * The library never allocates or frees device memory, never synchronises the
+ * device, and enqueues all work on `stream` (a hipStream_t; NULL = the null
+ * stream).  Layouts are dense, row-major, no strides:
+ *   q, out          [B][Hq][S][d]         dtype (bf16 or f32)
+ *   k_new, v_new    [B][Hkv][S][d]        dtype
+ *   cache->k, ->v   [B][Hkv][N_C][d]      dtype
+ *   cache->pos      [B][Hkv][N_C]         int32, -1 marks an empty slot
+ *   cache->score    [B][Hkv][N_C]         float32
+ *   lse             [B][Hq][S]            float32, natural log
+ *   colsum_cache    [B][Hkv][N_C]         float32
+ *   colsum_new      [B][Hkv][S]           float32
+ *   freed_slots     [B][Hkv][S]           int32
+ * Query head h reads KV head h / (Hq/Hkv) (contiguous GQA groups).
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued; a
+ * non-OK status means nothing was launched, and h2o_last_error() (thread-local)
+ * describes it.  A failed launch returns H2O_ERR_HIP.  Faults inside kernels
+ * surface at the caller's next synchronisation, as with any HIP work.  No C++
+ * exception crosses this boundary.
+ *
+ * Threads.  The entry points keep no state between calls (apart from the
+ * thread-local error text and the optional kernel timers) and may be called
+ * from several threads; calls that write the same cache must be ordered by the
+ * caller (same stream, or events).
+ */
+#ifndef H2O_H
+#define H2O_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H2O_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define H2O_API __attribute__((visibility("default")))
+#else
+#define H2O_API
+#endif
+
+typedef enum {
+    H2O_OK = 0,
+    H2O_ERR_INVALID_ARG = -1,   /* null pointer, bad size, inconsistent shape   */
+    H2O_ERR_UNSUPPORTED = -2,   /* valid but not implemented (head_dim, dtype)  */
+    H2O_ERR_CAPACITY = -3,      /* the cache cannot take the chunk (see below)  */
+    H2O_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required   */
+    H2O_ERR_HIP = -5            /* a HIP runtime call or launch failed          */
+} h2o_status_t;
+
+typedef enum { H2O_F32 = 0, H2O_BF16 = 1 } h2o_dtype_t;
+
+/* Ranking used to choose the slots to overwrite. */
+typedef enum {
+    H2O_SCORE_H2O = 0,        /* phi_h2o(b,h,j)                                    */
+    H2O_SCORE_H2O_NORM = 1    /* phi_h2o(b,h,j) / (t - t(b,h,j)), t = P + S, formed
+                                 in float32 ("Improvements to H2O", item 2)       */
+} h2o_score_mode_t;
+
+typedef struct {
+    int32_t batch;            /* B >= 1                                  */
+    int32_t n_q_heads;        /* Hq >= 1, a multiple of n_kv_heads       */
+    int32_t n_kv_heads;       /* Hkv >= 1                                */
+    int32_t head_dim;         /* d: 64 or 128                            */
+    int32_t capacity;         /* N_C: 1 .. 32768 slots per (b, kv head)  */
+    int32_t recent_window;    /* W >= 0: protected most recent positions */
+    int32_t dtype;            /* h2o_dtype_t of q, k, v, out and the cache K/V */
+} h2o_dims_t;
+
+/* One layer's cache.  Slots [0, n_valid) are filled, for every (b, kv head).
+ * n_valid lives on the host; h2o_evict_and_insert advances it. */
+typedef struct {
+    void    *k;
+    void    *v;
+    int32_t *pos;
+    float   *score;
+    int32_t  n_valid;
+} h2o_cache_t;
+
+/* Bytes of workspace h2o_chunk_attn needs for this chunk length (0 = none). */
+H2O_API size_t h2o_workspace_bytes(const h2o_dims_t *dims, int32_t chunk_len);
+
+/*
+ * Chunk attention with summed weights ("Kernel Support Needs").
+ * Query row i (0 <= i < S) sits at position P + i, P = chunk_start.  Keys are
+ * the filled slots j < n_valid and the chunk's own keys (position P + i').  Key
+ * j is visible to row i iff 0 <= t(j) <= P + i.  For every query head h:
+ *   out[b,h,i]  = sum_j softmax_j(sm_scale * q.k_j) v_j     (over visible keys)
+ *   lse[b,h,i]  = log sum_j exp(sm_scale * q.k_j)
+ * and for every KV head g, summing over its query heads and the S rows:
+ *   colsum_cache[b,g,j] = sum_{h in g} sum_i m_{b,h,i,j}     j < n_valid (0 beyond)
+ *   colsum_new[b,g,i']  = sum_{h in g} sum_i m_{b,h,i,i'}    chunk keys
+ * bf16: MFMA inputs are bf16, accumulation and softmax fp32; the weights are
+ * rounded to bf16 only for the product with V; summed weights are fp32.
+ * Requires 1 <= S, 0 <= n_valid <= N_C, chunk_start >= 0,
+ * chunk_start + S <= INT32_MAX, sm_scale finite and > 0.  The cache is read only.
+ */
+H2O_API h2o_status_t h2o_chunk_attn(const h2o_dims_t *dims, const h2o_cache_t *cache,
+                            int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                            const void *q, const void *k_new, const void *v_new,
+                            void *out, float *lse, float *colsum_cache, float *colsum_new,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Score accumulation ("Improvements to H2O", item 2): the H2O score is the
+ * running sum of summed attention weights.
+ *   cache->score[b,g,j] += colsum_cache[b,g,j]   for j < cache->n_valid.
+ */
+H2O_API h2o_status_t h2o_update_scores(const h2o_dims_t *dims, const h2o_cache_t *cache,
+                               const float *colsum_cache, void *stream);
+
+/*
+ * Eviction and insertion ("Improvements to H2O", item 2: new content overwrites
+ * the slots with the smallest score).  With n = cache->n_valid, P = chunk_start:
+ *   k = max(0, n + S - N_C) slots are evicted among the eligible ones
+ *   E = { j < n : t(j) < P - W }, the k smallest by (score, slot index);
+ *   targets = those victims and the empty slots [n, min(N_C, n+S)), ascending;
+ *   chunk token i goes to targets[i]: K, V rows copied from k_new/v_new,
+ *   t = P + i, score = colsum_new[b,g,i];  freed_slots[b,g,i] = targets[i];
+ *   then cache->n_valid = min(N_C, n + S).
+ * Returns H2O_ERR_CAPACITY (nothing launched) when k > 0 and S + W > N_C: with
+ * distinct cached positions below P, |E| >= n - W, so S + W <= N_C guarantees
+ * |E| >= k.  If the caller breaks that invariant and |E| < k on the device,
+ * the shortfall is taken from the ineligible filled slots in slot order.
+ * workspace may be NULL (none is needed).
+ */
+H2O_API h2o_status_t h2o_evict_and_insert(const h2o_dims_t *dims, h2o_cache_t *cache,
+                                  int64_t chunk_start, int32_t chunk_len, int32_t score_mode,
+                                  const void *k_new, const void *v_new,
+                                  const float *colsum_new, int32_t *freed_slots,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+H2O_API const char *h2o_last_error(void);
+
+/* H2O_ABI_VERSION of the loaded library. */
+H2O_API int32_t h2o_abi_version(void);
+
+/*
+ * Optional per-kernel timing (a diagnostic, process-wide, not thread-safe).
+ * While a timer is running, each launch of that kernel is bracketed by two HIP
+ * events recorded on its launch stream (at most max_launches launches are
+ * recorded).  h2o_kernel_timer_stop waits for those events and returns the sum
+ * of their elapsed times and the number of launches recorded.
+ */
+typedef enum {
+    H2O_KERNEL_ATTN = 0,      /* chunk attention: output + log-sum-exp          */
+    H2O_KERNEL_COLSUM = 1,    /* summed attention weights (recompute pass)      */
+    H2O_KERNEL_UPDATE = 2,    /* score accumulation                             */
+    H2O_KERNEL_SELECT = 3,    /* eligibility + victim selection                 */
+    H2O_KERNEL_INSERT = 4,    /* chunk insertion                                */
+    H2O_KERNEL_DECODE = 5,    /* S = 1 attention (split over slots)             */
+    H2O_KERNEL_COUNT = 6
+} h2o_kernel_id_t;
+
+H2O_API h2o_status_t h2o_kernel_timer_start(int32_t kernel, int32_t max_launches);
+H2O_API h2o_status_t h2o_kernel_timer_stop(int32_t kernel, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H2O_H */

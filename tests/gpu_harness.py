@@ -1,0 +1,164 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and compare
+it with the fp64 oracle on identical seeded inputs.
+
+Tolerances (bf16): attention output |got - ref| <= 1e-2 + 2^-8 |ref| per element
+and relative L2 <= 5e-3, log-sum-exp abs <= 1e-3, summed weights and scores
+relative <= 1e-3.  The 2^-8 |ref| term is what bf16 itself costs: the output is
+stored in bf16 (half an ulp, 2^-9 |ref|) and the weights are rounded to bf16
+before the product with V (2^-9 relative); for |ref| >= 4 the storage rounding
+alone can exceed 1e-2.  (f32):
+output max-abs <= 1e-4, relative L2 <= 1e-5, lse abs <= 1e-5, summed weights
+and scores relative <= 1e-5.  Victim sets must match exactly, except that a
+swap of two slots straddling the cut is accepted when their oracle scores are
+within 1e-5 (relative) of the cut value; the GPU cache is then reloaded from
+the oracle's state so the next chunk starts from the same input.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import h2o_sparse_attention_amd as h2o
+import oracle
+
+DEV = torch.device("cuda:0")
+TOL = {
+    "bf16": dict(out_abs=1e-2, out_rel=2.0 ** -8, out_rel_l2=5e-3, lse_abs=1e-3, cs_rel=1e-3),
+    "f32": dict(out_abs=1e-4, out_rel=0.0, out_rel_l2=1e-5, lse_abs=1e-5, cs_rel=1e-5),
+}
+NEAR_TIE_REL = 1e-5
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV, dtype)
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.is_floating_point() \
+        else t.detach().cpu().numpy()
+
+
+def dims_of(wl) -> h2o.H2ODims:
+    return h2o.H2ODims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity,
+                       wl.recent_window, wl.dtype)
+
+
+def load_oracle_state(cache: h2o.H2OCache, st: oracle.H2OState, dtype: str):
+    dt = TORCH_DT[dtype]
+    cache.load(dev(st.K, dt), dev(st.V, dt), dev(st.pos.astype(np.int32), torch.int32),
+               dev(st.phi.astype(np.float32), torch.float32), st.n, st.P)
+
+
+def gpu_chunk(cache: h2o.H2OCache, x: dict, sm_scale: float, dtype: str,
+              score_mode: str = "h2o") -> dict:
+    """The three calls, with a snapshot of the scores between update and eviction."""
+    dt = TORCH_DT[dtype]
+    q, k, v = dev(x["q"], dt), dev(x["k"], dt), dev(x["v"], dt)
+    P = cache.next_pos
+    out, lse, cs_cache, cs_new = h2o.chunk_attn(cache, P, q, k, v, sm_scale)
+    h2o.update_scores(cache, cs_cache)
+    phi_upd = cache.score.clone()
+    freed = h2o.evict_and_insert(cache, P, k, v, cs_new, score_mode=score_mode)
+    torch.cuda.synchronize()
+    return {"out": host(out), "lse": host(lse), "colsum_cache": host(cs_cache),
+            "colsum_new": host(cs_new), "phi_updated": host(phi_upd),
+            "freed_slots": host(freed).astype(np.int64),
+            "K": cache.k.clone(), "V": cache.v.clone(), "pos": host(cache.pos).astype(np.int64),
+            "phi": host(cache.score), "n": cache.n_valid}
+
+
+def rel_err(got, want, floor=1e-30):
+    return np.abs(got - want) / np.maximum(np.abs(want), floor)
+
+
+def compare_attention(g: dict, r: dict, n: int, dtype: str, where: str = ""):
+    tol = TOL[dtype]
+    diff = np.abs(g["out"] - r["out"])
+    bound = tol["out_abs"] + tol["out_rel"] * np.abs(r["out"])
+    d_out = diff.max()
+    l2 = np.linalg.norm(g["out"] - r["out"]) / np.linalg.norm(r["out"])
+    at = np.unravel_index((diff / bound).argmax(), diff.shape)
+    info = (f"worst at {tuple(int(x) for x in at)} err={diff[at]:.3e} |ref|={abs(r['out'][at]):.4f} "
+            f"rel-L2={l2:.2e} |ref|max={np.abs(r['out']).max():.3f} "
+            f"n_over_1e-2={(diff > tol['out_abs']).sum()}")
+    print(f"{where} out max-abs {d_out:.3e} {info}")
+    assert (diff <= bound).all(), f"{where} out error over bound: {info}"
+    assert l2 <= tol["out_rel_l2"], f"{where} out rel-L2 {l2:.3e}"
+    d_lse = np.abs(g["lse"] - r["lse"]).max()
+    assert d_lse <= tol["lse_abs"], f"{where} lse abs {d_lse:.3e}"
+    e1 = rel_err(g["colsum_cache"][:, :, :n], r["colsum_cache"][:, :, :n]).max(initial=0.0)
+    e2 = rel_err(g["colsum_new"], r["colsum_new"]).max()
+    assert e1 <= tol["cs_rel"], f"{where} colsum_cache rel {e1:.3e}"
+    assert e2 <= tol["cs_rel"], f"{where} colsum_new rel {e2:.3e}"
+    assert (g["colsum_cache"][:, :, n:] == 0).all(), f"{where} colsum beyond n not zero"
+    return {"out_abs": d_out, "out_l2": l2, "lse_abs": d_lse, "cs_rel": max(e1, e2)}
+
+
+def compare_victims(g_freed, r_freed, r_phi_upd, pos_before, n, P, W, where=""):
+    """Returns the number of accepted near-tie swaps (0 = identical)."""
+    swaps = 0
+    B, Hkv, S = r_freed.shape
+    for b in range(B):
+        for h in range(Hkv):
+            gv = {int(x) for x in g_freed[b, h] if x < n}
+            ov = {int(x) for x in r_freed[b, h] if x < n}
+            assert sorted(g_freed[b, h].tolist()) == g_freed[b, h].tolist(), \
+                f"{where} freed not ascending"
+            assert len(set(g_freed[b, h].tolist())) == S, f"{where} freed not distinct"
+            if gv == ov:
+                continue
+            phi = r_phi_upd[b, h]
+            cut = max(phi[j] for j in ov)
+            for a in gv - ov:
+                assert pos_before[b, h, a] < P - W, f"{where} evicted a protected slot {a}"
+                assert phi[a] - cut <= NEAR_TIE_REL * cut, \
+                    f"{where} ({b},{h}) slot {a} phi {phi[a]!r} vs cut {cut!r}"
+            for o in ov - gv:
+                assert cut - phi[o] <= NEAR_TIE_REL * cut, \
+                    f"{where} ({b},{h}) kept slot {o} phi {phi[o]!r} vs cut {cut!r}"
+            swaps += len(gv - ov)
+    return swaps
+
+
+def compare_step(g: dict, r: dict, st_after: oracle.H2OState, n_before: int, pos_before,
+                 P: int, W: int, dtype: str, where: str = "") -> int:
+    compare_attention(g, r, n_before, dtype, where)
+    tol = TOL[dtype]
+    e = rel_err(g["phi_updated"][:, :, :n_before], r["phi_updated"][:, :, :n_before])
+    assert e.max(initial=0.0) <= tol["cs_rel"], f"{where} phi_updated rel {e.max():.3e}"
+    swaps = compare_victims(g["freed_slots"], r["freed_slots"], r["phi_updated"], pos_before,
+                            n_before, P, W, where)
+    if swaps == 0:
+        assert (g["freed_slots"] == r["freed_slots"]).all(), f"{where} freed slots"
+        assert (g["pos"] == st_after.pos).all(), f"{where} pos after insert"
+        dt = TORCH_DT[dtype]
+        assert torch.equal(g["K"], dev(st_after.K, dt)) and torch.equal(g["V"], dev(st_after.V, dt)), \
+            f"{where} cache rows after insert"
+        n = st_after.n
+        e = rel_err(g["phi"][:, :, :n], st_after.phi[:, :, :n]).max()
+        assert e <= tol["cs_rel"], f"{where} phi after insert rel {e:.3e}"
+        assert g["n"] == st_after.n
+    return swaps
+
+
+def run_chain(wl, chunks, get_inputs, cache=None, st=None, resync="on_divergence",
+              score_mode="h2o", layer=0):
+    """Drive GPU and oracle over the given chunks; return the number of near-tie swaps."""
+    dims = dims_of(wl)
+    cache = cache or h2o.H2OCache(dims, DEV)
+    st = st or oracle.H2OState.empty(wl.batch, wl.n_kv_heads, wl.capacity, wl.head_dim)
+    swaps = 0
+    for c in chunks:
+        x = get_inputs(c)
+        n_before, pos_before, P = st.n, st.pos.copy(), st.P
+        assert cache.n_valid == st.n and cache.next_pos == st.P
+        g = gpu_chunk(cache, x, wl.sm_scale, wl.dtype, score_mode)
+        r = oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window,
+                            score_mode)
+        s = compare_step(g, r, st, n_before, pos_before, P, wl.recent_window, wl.dtype,
+                         where=f"chunk {c}:")
+        swaps += s
+        if resync == "always" or s:
+            load_oracle_state(cache, st, wl.dtype)
+    return swaps

@@ -1,0 +1,163 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs (needs a GPU).
+
+Every call goes through the C ABI (libh2o.so) via the ctypes binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gpu_harness as H  # noqa: E402
+import h2o_sparse_attention_amd as h2o  # noqa: E402
+
+
+def _chunk_getter(wl, layer=0):
+    return lambda c: W.chunk_inputs(wl, layer, c)
+
+
+def test_plumbing_f32_full_sequence():
+    """Tiny plumbing workload (f32, d=64, GQA 2, N_C=256, W=32, S=64, 1024 tokens):
+    all 16 chunks free-running, 4 filling and 12 evicting."""
+    wl = W.WORKLOADS[1]
+    swaps = H.run_chain(wl, range(wl.n_chunks), _chunk_getter(wl))
+    print("near-tie swaps:", swaps)
+
+
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_bf16_chain_reduced(head_dim):
+    """Qwen3-4B-like structure at reduced size (B=2, 8q/2kv heads, N_C=512, W=64,
+    S=128, 2048 tokens): 4 filling and 12 evicting chunks, free-running."""
+    wl = W.workload(2, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=head_dim, capacity=512,
+                    recent_window=64, chunk=128, seq_len=2048, heavy_count=20)
+    swaps = H.run_chain(wl, range(wl.n_chunks), _chunk_getter(wl))
+    print("near-tie swaps:", swaps)
+
+
+def test_bf16_chain_h2o_norm():
+    wl = W.workload(2, batch=1, n_q_heads=8, n_kv_heads=2, capacity=512, recent_window=64,
+                    chunk=128, seq_len=1536, heavy_count=15)
+    H.run_chain(wl, range(wl.n_chunks), _chunk_getter(wl), score_mode="h2o_norm")
+
+
+def test_qwen3_shape_first_chunks():
+    """Full Qwen3-4B attention shape, chunk 1k: the first two chunks (n = 0, 1024)."""
+    wl = W.WORKLOADS[2]
+    H.run_chain(wl, range(2), _chunk_getter(wl))
+
+
+def _steady(wl, start, seed=0):
+    s = W.steady_state(wl, 0, start=start, seed=seed)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    return cache, st
+
+
+@pytest.mark.parametrize("key", [2, 3])
+def test_steady_chunk_full_size(key):
+    """One evicting chunk at the full configured size from a full cache
+    (chunk 1k / N_C 8192 / W 256, and chunk 2k / N_C 16384 / W 512)."""
+    wl = W.WORKLOADS[key]
+    c = 16
+    cache, st = _steady(wl, start=c * wl.chunk)
+    H.run_chain(wl, [c], _chunk_getter(wl), cache=cache, st=st)
+
+
+@pytest.mark.parametrize("case", [
+    dict(dtype="bf16", head_dim=64, n_q_heads=6, n_kv_heads=2, capacity=300, chunk=100,
+         recent_window=10, seq_len=700),
+    dict(dtype="bf16", head_dim=128, n_q_heads=3, n_kv_heads=3, capacity=97, chunk=33,
+         recent_window=5, seq_len=330),
+    dict(dtype="bf16", head_dim=128, n_q_heads=4, n_kv_heads=1, capacity=64, chunk=1,
+         recent_window=3, seq_len=80),
+    dict(dtype="f32", head_dim=128, n_q_heads=4, n_kv_heads=2, capacity=150, chunk=65,
+         recent_window=7, seq_len=520),
+    dict(dtype="f32", head_dim=64, n_q_heads=2, n_kv_heads=2, capacity=40, chunk=1,
+         recent_window=2, seq_len=60),
+], ids=["bf16_d64_g3_S100", "bf16_mha_S33", "bf16_S1", "f32_d128_S65", "f32_S1"])
+def test_ragged_shapes(case):
+    """Chunk lengths and capacities that are not tile multiples, MHA and GQA 3/4,
+    single-token chunks, and capacities that are not multiples of the chunk."""
+    wl = W.workload(2, batch=2, heavy_count=4, sm_scale=case["head_dim"] ** -0.5, **case)
+    H.run_chain(wl, range(wl.n_chunks), _chunk_getter(wl))
+
+
+def _isolated_evict(wl, score_mode, seed):
+    s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=seed, tie_fraction=0.2)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    x = W.chunk_inputs(wl, 0, 20)
+    cs_new = np.random.default_rng(seed).random((wl.batch, wl.n_kv_heads, wl.chunk)).astype(
+        np.float32)
+    k, v = H.dev(x["k"], torch.bfloat16), H.dev(x["v"], torch.bfloat16)
+    freed = h2o.evict_and_insert(cache, st.P, k, v, H.dev(cs_new, torch.float32),
+                                 score_mode=score_mode)
+    torch.cuda.synchronize()
+    victims = oracle.select_victims(st, wl.chunk, wl.recent_window, score_mode)
+    want = oracle.evict_and_insert(st, victims, x["k"], x["v"], cs_new)
+    return freed, cache, st, want
+
+
+@pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_evict_isolated_bit_exact(score_mode, seed):
+    """Same scores in, same victims out: selection and insertion are bit-exact at the
+    full chunk-1k size, with 20% of the scores set to three shared values (ties)."""
+    wl = W.WORKLOADS[2]
+    freed, cache, st, want = _isolated_evict(wl, score_mode, seed)
+    assert (H.host(freed) == want).all()
+    assert (H.host(cache.pos) == st.pos).all()
+    assert (H.host(cache.k) == st.K).all() and (H.host(cache.v) == st.V).all()
+    assert (H.host(cache.score) == st.phi).all()
+    assert cache.n_valid == st.n
+
+
+def test_evict_isolated_large_capacity():
+    wl = W.workload(3, capacity=32768, chunk=2048, recent_window=512)
+    freed, cache, st, want = _isolated_evict(wl, "h2o", 3)
+    assert (H.host(freed) == want).all()
+    assert (H.host(cache.pos) == st.pos).all()
+
+
+def test_update_scores_matches_oracle():
+    wl = W.WORKLOADS[2]
+    cache, st = _steady(wl, start=16 * wl.chunk)
+    cs = np.random.default_rng(0).random((1, 8, wl.capacity)).astype(np.float32)
+    h2o.update_scores(cache, H.dev(cs, torch.float32))
+    oracle.update_scores(st, cs)
+    torch.cuda.synchronize()
+    got = H.host(cache.score)
+    assert (H.rel_err(got, st.phi) <= 2 ** -23).all()     # one fp32 rounding
+
+
+def test_determinism_bitwise():
+    """Two runs of the same steady chunk give identical bits (no atomics in the reductions)."""
+    wl = W.WORKLOADS[2]
+    outs = []
+    for _ in range(2):
+        cache, st = _steady(wl, start=16 * wl.chunk)
+        x = W.chunk_inputs(wl, 0, 16)
+        g = H.gpu_chunk(cache, x, wl.sm_scale, wl.dtype)
+        outs.append(g)
+    for key in ("out", "lse", "colsum_cache", "colsum_new", "phi", "freed_slots"):
+        assert (outs[0][key] == outs[1][key]).all(), key
+
+
+def test_decode_steps_full_cache():
+    """Decode workload (16 sequences, N_C 16384 full, W 512): the first 3 single-token
+    steps, each with one eviction per (sequence, KV head)."""
+    wl = W.WORKLOADS[5]
+    s = W.decode_initial_state(wl)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    del s
+    H.run_chain(wl, range(3), lambda t: W.decode_step_inputs(wl, t), cache=cache, st=st)
