@@ -135,6 +135,12 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
         return fail(H2O_ERR_INVALID_ARG, "q, k_new, v_new, out, lse and colsum buffers must be non-NULL");
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
         return fail(H2O_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+    {
+        const long long G = dims->n_q_heads / dims->n_kv_heads;
+        if (G * G * (long long)chunk_len >= (1LL << 31))
+            return fail(H2O_ERR_UNSUPPORTED, "query heads per KV head (%lld) too large for chunk_len %d",
+                        G, chunk_len);
+    }
     const size_t ws_need = h2o_workspace_bytes(dims, chunk_len);
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
         return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", ws_need,

@@ -82,26 +82,68 @@ __device__ __forceinline__ int perm_key(int m) {
 }
 
 // ---------------------------------------------------------------------------
+// Key tiles.  The filled cache slots form ceil(n/64) tiles (the last one may be
+// partial) and the chunk's own keys follow in tiles of their own, so a tile
+// never mixes cache rows and chunk rows: one base pointer and one count of
+// valid keys describe it, and full tiles load with no per-key tests.
+// ---------------------------------------------------------------------------
+struct TileRef {
+    const u16* k;
+    const u16* v;
+    int first;      // index of the tile's first key in its source (cache or chunk)
+    int valid;      // keys of the tile that exist (1..64)
+    bool cache;
+};
+
+__device__ __forceinline__ TileRef tile_ref(int tile, int cache_tiles, int n, int S, int D,
+                                            const u16* Kc, const u16* Vc, const u16* Kn,
+                                            const u16* Vn) {
+    TileRef t;
+    t.cache = tile < cache_tiles;
+    t.first = (t.cache ? tile : tile - cache_tiles) * kKeysPerTile;
+    t.valid = min(kKeysPerTile, (t.cache ? n : S) - t.first);
+    t.k = (t.cache ? Kc : Kn) + (size_t)t.first * D;
+    t.v = (t.cache ? Vc : Vn) + (size_t)t.first * D;
+    return t;
+}
+
+template <int D>
+struct AttnSmem {
+    static constexpr int KROW = D + 8;                  // LDS K row, +16 B pad
+    static constexpr int VROW = kKeysPerTile + 8;       // LDS V^T row, +16 B pad
+    static constexpr int K_BYTES = kKeysPerTile * KROW * 2;
+    static constexpr int V_BYTES = D * VROW * 2;
+    static constexpr int BUF_BYTES = K_BYTES + V_BYTES + kKeysPerTile * 4;
+    static constexpr int MERGE_FLOATS = 2 + (D / 32) * 16;   // m, l, O^T accumulators
+    static constexpr int MERGE_BYTES = 4 * MERGE_FLOATS * 64 * 4;
+    static constexpr int BYTES = 4 * BUF_BYTES > MERGE_BYTES ? 4 * BUF_BYTES : MERGE_BYTES;
+};
+
+// ---------------------------------------------------------------------------
 // Attention pass: O and LSE for 128 query rows of one (b, kv head).
 // Rows of a KV head are ordered position-major: row r = i*G + hh is query
-// head g*G + hh at chunk position i.
+// head g*G + hh at chunk position i.  Eight waves: waves 0-3 and 4-7 own the
+// same four 32-row groups and split the key tiles between them (even / odd
+// tiles), each half with its own double-buffered LDS tiles; the two partial
+// softmax states are merged through LDS at the end.
 // ---------------------------------------------------------------------------
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kHalfThreads = kAttnThreads / 2;
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
+    using L = AttnSmem<D>;
     constexpr int KS = D / 16;                    // MFMA k-steps over head_dim
     constexpr int DT = D / 32;                    // 32-row tiles of O^T
-    constexpr int KROW = D + 8;                   // LDS K row, +16 B pad
-    constexpr int VROW = kKeysPerTile + 8;        // LDS V^T row, +16 B pad
+    constexpr int KROW = L::KROW, VROW = L::VROW;
     constexpr int KCH = D / 8;                    // 16-byte chunks per key row
-    constexpr int K_LD = kKeysPerTile * KCH / kThreads;
+    constexpr int K_LD = kKeysPerTile * KCH / kHalfThreads;
     constexpr int VP = D / 2;                     // d pairs
-    constexpr int VKG = kThreads / VP;            // key groups for V staging
+    constexpr int VKG = kHalfThreads / VP;        // key groups for V staging
     constexpr int VKPG = kKeysPerTile / VKG;      // keys per group (8 or 16)
     static_assert(K_LD >= 1 && VKPG % 8 == 0, "tile shape");
-
-    __shared__ __attribute__((aligned(16))) u16 sK[kKeysPerTile * KROW];
-    __shared__ __attribute__((aligned(16))) u16 sVt[D * VROW];
-    __shared__ __attribute__((aligned(16))) int sPos[kKeysPerTile];
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
     const int R = a.G * a.S;
     const int nrb = (R + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -113,8 +155,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int kh = wave >> 2, rw = wave & 3, htid = tid & (kHalfThreads - 1);
     const int lq = lane & 31, hh = lane >> 5;
-    const int row = rb * kRowsPerBlock + wave * 32 + lq;
+    const int row = rb * kRowsPerBlock + rw * 32 + lq;
     const bool row_ok = row < R;
     const int i = row_ok ? row / a.G : a.S - 1;
     const int h = g * a.G + (row_ok ? row % a.G : 0);
@@ -130,56 +173,71 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
         qf[ks] = as_bf16x8(v);
     }
 
+    const int n = a.n, S = a.S;
+    const int cache_tiles = (n + kKeysPerTile - 1) / kKeysPerTile;
     const int last_row = min(R - 1, rb * kRowsPerBlock + kRowsPerBlock - 1);
-    const int nkeys = a.n + last_row / a.G + 1;
-    const int ntiles = (nkeys + kKeysPerTile - 1) / kKeysPerTile;
-    const int wave_row0 = min(R - 1, rb * kRowsPerBlock + wave * 32);
+    const int ntiles = cache_tiles + (last_row / a.G) / kKeysPerTile + 1;
+    const int steps = (ntiles + 1) / 2;
+    const int wave_row0 = min(R - 1, rb * kRowsPerBlock + rw * 32);
     const int qpos_wave_min = a.P + wave_row0 / a.G;
 
     const u16* Kc = static_cast<const u16*>(a.kc) + (size_t)bg * a.NC * D;
     const u16* Vc = static_cast<const u16*>(a.vc) + (size_t)bg * a.NC * D;
-    const u16* Kn = static_cast<const u16*>(a.kn) + (size_t)bg * a.S * D;
-    const u16* Vn = static_cast<const u16*>(a.vn) + (size_t)bg * a.S * D;
+    const u16* Kn = static_cast<const u16*>(a.kn) + (size_t)bg * S * D;
+    const u16* Vn = static_cast<const u16*>(a.vn) + (size_t)bg * S * D;
     const int32_t* posg = a.pos + (size_t)bg * a.NC;
-    const int n = a.n, S = a.S;
 
     u32x4 kreg[K_LD];
     uint32_t vreg[VKPG];
     int preg = INT_MAX;
+    const int dp = htid % VP, kg = htid / VP;
 
     auto gload = [&](int tile) {
-        const int base = tile * kKeysPerTile;
+        const TileRef tr = tile_ref(tile, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
+        if (tr.valid == kKeysPerTile) {
 #pragma unroll
-        for (int it = 0; it < K_LD; ++it) {
-            const int c = tid + it * kThreads;
-            const int kk = base + c / KCH, col = (c % KCH) * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (kk < n) v = ld16(Kc + (size_t)kk * D + col);
-            else if (kk < n + S) v = ld16(Kn + (size_t)(kk - n) * D + col);
-            kreg[it] = v;
-        }
-        const int dp = tid % VP, kg = tid / VP;
+            for (int it = 0; it < K_LD; ++it) {
+                const int c = htid + it * kHalfThreads;
+                kreg[it] = ld16(tr.k + (c / KCH) * D + (c % KCH) * 8);
+            }
 #pragma unroll
-        for (int e = 0; e < VKPG; ++e) {
-            const int kk = base + kg * VKPG + e;
-            uint32_t v = 0u;
-            if (kk < n) v = *reinterpret_cast<const uint32_t*>(Vc + (size_t)kk * D + 2 * dp);
-            else if (kk < n + S)
-                v = *reinterpret_cast<const uint32_t*>(Vn + (size_t)(kk - n) * D + 2 * dp);
-            vreg[e] = v;
+            for (int e = 0; e < VKPG; ++e)
+                vreg[e] = *reinterpret_cast<const uint32_t*>(tr.v + (kg * VKPG + e) * D + 2 * dp);
+        } else {
+#pragma unroll
+            for (int it = 0; it < K_LD; ++it) {
+                const int c = htid + it * kHalfThreads;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (c / KCH < tr.valid) v = ld16(tr.k + (c / KCH) * D + (c % KCH) * 8);
+                kreg[it] = v;
+            }
+#pragma unroll
+            for (int e = 0; e < VKPG; ++e) {
+                const int key = kg * VKPG + e;
+                vreg[e] = key < tr.valid
+                              ? *reinterpret_cast<const uint32_t*>(tr.v + key * D + 2 * dp)
+                              : 0u;
+            }
         }
-        if (tid < kKeysPerTile) {
-            const int kk = base + tid;
-            preg = kk < n ? posg[kk] : (kk < n + S ? a.P + (kk - n) : INT_MAX);
-        }
+        if (htid < kKeysPerTile)
+            preg = htid < tr.valid ? (tr.cache ? posg[tr.first + htid] : a.P + tr.first + htid)
+                                   : INT_MAX;
     };
-    auto lstore = [&]() {
+    auto bufs = [&](int which, u16*& sK, u16*& sVt, int*& sPos) {
+        unsigned char* base = smem + (kh * 2 + which) * L::BUF_BYTES;
+        sK = reinterpret_cast<u16*>(base);
+        sVt = reinterpret_cast<u16*>(base + L::K_BYTES);
+        sPos = reinterpret_cast<int*>(base + L::K_BYTES + L::V_BYTES);
+    };
+    auto lstore = [&](int which) {
+        u16 *sK, *sVt;
+        int* sPos;
+        bufs(which, sK, sVt, sPos);
 #pragma unroll
         for (int it = 0; it < K_LD; ++it) {
-            const int c = tid + it * kThreads;
+            const int c = htid + it * kHalfThreads;
             *reinterpret_cast<u32x4*>(&sK[(c / KCH) * KROW + (c % KCH) * 8]) = kreg[it];
         }
-        const int dp = tid % VP, kg = tid / VP;
 #pragma unroll
         for (int e0 = 0; e0 < VKPG; e0 += 8) {
             u32x4 lo, hi;
@@ -192,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
             *reinterpret_cast<u32x4*>(&sVt[(2 * dp) * VROW + kg * VKPG + e0]) = lo;
             *reinterpret_cast<u32x4*>(&sVt[(2 * dp + 1) * VROW + kg * VKPG + e0]) = hi;
         }
-        if (tid < kKeysPerTile) sPos[tid] = preg;
+        if (htid < kKeysPerTile) sPos[htid] = preg;
     };
 
     const float c = a.sm_scale * kLog2e;          // logits -> log2 units
@@ -203,13 +261,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
     const int prow = perm_key(lq);
 
-    if (ntiles > 0) gload(0);
-    for (int tile = 0; tile < ntiles; ++tile) {
-        __syncthreads();
-        lstore();
-        __syncthreads();
-        if (tile + 1 < ntiles) gload(tile + 1);
-
+    auto compute = [&](int which) {
+        u16 *sK, *sVt;
+        int* sPos;
+        bufs(which, sK, sVt, sPos);
         f32x16 s[2];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
@@ -219,7 +274,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
             for (int ks = 0; ks < KS; ++ks)
                 s[sub] = mfma32(as_bf16x8(ld16(kp + 16 * ks)), qf[ks], s[sub]);
         }
-
         // Implicit positional mask; skipped when every key of the tile is
         // visible to every row of this wave.
         const int kp_lane = sPos[lane];
@@ -239,7 +293,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
                     }
                 }
         }
-
         float mt = s[0][0];
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(s[0][r], s[1][r]));
@@ -257,7 +310,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
             m_run = m_next;
         }
         const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-
         bf16x8 pb[2][2];
         float lsum = 0.f;
 #pragma unroll
@@ -275,7 +327,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
                 pb[sub][s2] = as_bf16x8(w);
             }
         l_run += lsum;
-
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const u16* vp = &sVt[(dt * 32 + lq) * VROW + 8 * hh];
@@ -285,6 +336,48 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
                 for (int s2 = 0; s2 < 2; ++s2)
                     o[dt] = mfma32(as_bf16x8(ld16(vp + sub * 32 + 16 * s2)), pb[sub][s2], o[dt]);
         }
+    };
+
+    // Half kh owns tiles kh, kh+2, kh+4, ...; both halves step together.
+    if (kh < ntiles) {
+        gload(kh);
+        lstore(0);
+    }
+    __syncthreads();
+    for (int st = 0; st < steps; ++st) {
+        const int cur = st & 1;
+        const int my_tile = 2 * st + kh, next_tile = my_tile + 2;
+        if (next_tile < ntiles) gload(next_tile);
+        if (my_tile < ntiles) compute(cur);
+        if (next_tile < ntiles) lstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Merge the two halves' (m, l, O) for each row (all LDS tile reads are done).
+    constexpr int MF = L::MERGE_FLOATS;
+    float* mb = reinterpret_cast<float*>(smem) + rw * MF * 64;
+    if (kh == 1) {
+        mb[lane] = m_run;
+        mb[64 + lane] = l_run;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mb[(2 + dt * 16 + r) * 64 + lane] = o[dt][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    {
+        const float m1 = mb[lane], l1 = mb[64 + lane];
+        const float m = fmaxf(m_run, m1);
+        const float a0 = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m) * c);
+        const float a1 = m1 == -INFINITY ? 0.f : fast_exp2((m1 - m) * c);
+        l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o[dt][r] = o[dt][r] * a0 + mb[(2 + dt * 16 + r) * 64 + lane] * a1;
+        m_run = m;
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -308,61 +401,62 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 // Colsum pass: for 128 keys of one (b, kv head), sum exp(s - lse) over every
 // query row of the group (G heads x S positions).  K stays in registers; Q
-// and LSE tiles stream through LDS.  Each lane accumulates its 16 keys over
-// its query column, and the 32 columns are added in a fixed order at the end,
-// so the result is deterministic (no atomics).
+// and LSE tiles stream through double-buffered LDS.  Each lane accumulates its
+// 16 keys over its query column, and the 32 columns are added in a fixed
+// order at the end, so the result is deterministic (no atomics).  Key blocks
+// follow the same cache / chunk split as the attention tiles.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void colsum_bf16_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
     constexpr int KS = D / 16;
     constexpr int QROW = D + 8;
     constexpr int QCH = D / 8;
     constexpr int Q_LD = kRowsPerTile * QCH / kThreads;
+    constexpr int QBUF = kRowsPerTile * QROW;      // u16 per Q buffer
     static_assert(Q_LD >= 1, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) u16 sQ[kRowsPerTile * QROW];
-    __shared__ float sL[kRowsPerTile];
+    __shared__ __attribute__((aligned(16))) u16 sQ[2][QBUF];
+    __shared__ float sL[2][kRowsPerTile];
     __shared__ float sRed[kWaves][32][33];
 
     const int n = a.n, S = a.S, G = a.G;
-    const int nkeys = n + S;
-    const int nkb = (nkeys + kKeysPerBlock - 1) / kKeysPerBlock;
+    const int cache_blocks = (n + kKeysPerBlock - 1) / kKeysPerBlock;
+    const int nkb = cache_blocks + (S + kKeysPerBlock - 1) / kKeysPerBlock;
     const int total = nkb * a.B * a.Hkv;
     const int t = xcd_tile(blockIdx.x, total);
     if (t >= total) return;
     const int bg = t / nkb, kb = t % nkb;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const bool is_cache = kb < cache_blocks;
+    const int block_first = (is_cache ? kb : kb - cache_blocks) * kKeysPerBlock;
+    const int limit = is_cache ? n : S;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lq = lane & 31, hh = lane >> 5;
-    const int key0 = kb * kKeysPerBlock + wave * 32;
+    const int first = block_first + wave * 32;    // this wave's first key in its source
 
-    const u16* Kc = static_cast<const u16*>(a.kc) + (size_t)bg * a.NC * D;
-    const u16* Kn = static_cast<const u16*>(a.kn) + (size_t)bg * S * D;
+    const u16* Ksrc = is_cache ? static_cast<const u16*>(a.kc) + (size_t)bg * a.NC * D
+                               : static_cast<const u16*>(a.kn) + (size_t)bg * S * D;
     const int32_t* posg = a.pos + (size_t)bg * a.NC;
-    auto key_pos = [&](int kk) -> int {
-        return kk < n ? posg[kk] : (kk < n + S ? a.P + (kk - n) : INT_MAX);
+    auto key_pos = [&](int idx) -> int {
+        return idx < limit ? (is_cache ? posg[idx] : a.P + idx) : INT_MAX;
     };
 
-    // A operand: this lane's key row.
     bf16x8 kf[KS];
     {
-        const int kk = key0 + lq;
-        const u16* src = kk < n ? Kc + (size_t)kk * D
-                                : (kk < n + S ? Kn + (size_t)(kk - n) * D : nullptr);
+        const int idx = first + lq;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (src) v = ld16(src + 16 * ks + 8 * hh);
+            if (idx < limit) v = ld16(Ksrc + (size_t)idx * D + 16 * ks + 8 * hh);
             kf[ks] = as_bf16x8(v);
         }
     }
-    // Positions of the 16 keys of this lane's C registers.
     int kpos[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) kpos[r] = key_pos(key0 + 8 * (r >> 2) + 4 * hh + (r & 3));
-    int kmin = key_pos(key0 + lq), kmax = kmin;
+    for (int r = 0; r < 16; ++r) kpos[r] = key_pos(first + 8 * (r >> 2) + 4 * hh + (r & 3));
+    int kmin = key_pos(first + lq), kmax = kmin;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         kmin = min(kmin, __shfl_xor(kmin, off));
@@ -371,13 +465,16 @@ __global__ __launch_bounds__(kThreads, 2) void colsum_bf16_kernel(ChunkArgs a) {
 
     const int R = G * S;
     const int ntile = (R + kRowsPerTile - 1) / kRowsPerTile;
-    // Blocks made only of chunk keys are invisible to rows before their first key.
-    const int first_key = kb * kKeysPerBlock;
-    const int tile0 = first_key >= n ? ((first_key - n) * G) / kRowsPerTile : 0;
+    // Chunk keys are invisible to the rows before their own position.
+    const int tile0 = is_cache ? 0 : (block_first * G) / kRowsPerTile;
 
     const u16* Q = static_cast<const u16*>(a.q);
     u32x4 qreg[Q_LD];
     float lreg = INFINITY;
+    auto row_split = [&](int r, int& hq, int& ipos) {
+        ipos = G == 1 ? r : (int)__umulhi((uint32_t)r, g_magic);
+        hq = g * G + (r - ipos * G);
+    };
     auto gload = [&](int rt) {
 #pragma unroll
         for (int it = 0; it < Q_LD; ++it) {
@@ -385,24 +482,30 @@ __global__ __launch_bounds__(kThreads, 2) void colsum_bf16_kernel(ChunkArgs a) {
             const int r = rt * kRowsPerTile + cidx / QCH, col = (cidx % QCH) * 8;
             u32x4 v = {0u, 0u, 0u, 0u};
             if (r < R) {
-                const int hq = g * G + r % G, ipos = r / G;
+                int hq, ipos;
+                row_split(r, hq, ipos);
                 v = ld16(Q + ((size_t)(b * a.Hq + hq) * S + ipos) * D + col);
             }
             qreg[it] = v;
         }
         if (tid < kRowsPerTile) {
             const int r = rt * kRowsPerTile + tid;
-            lreg = r < R ? a.lse[(size_t)(b * a.Hq + g * G + r % G) * S + r / G] * kLog2e
-                         : INFINITY;
+            lreg = INFINITY;
+            if (r < R) {
+                int hq, ipos;
+                row_split(r, hq, ipos);
+                lreg = a.lse[(size_t)(b * a.Hq + hq) * S + ipos] * kLog2e;
+            }
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int which) {
 #pragma unroll
         for (int it = 0; it < Q_LD; ++it) {
             const int cidx = tid + it * kThreads;
-            *reinterpret_cast<u32x4*>(&sQ[(cidx / QCH) * QROW + (cidx % QCH) * 8]) = qreg[it];
+            *reinterpret_cast<u32x4*>(&sQ[which][(cidx / QCH) * QROW + (cidx % QCH) * 8]) =
+                qreg[it];
         }
-        if (tid < kRowsPerTile) sL[tid] = lreg;
+        if (tid < kRowsPerTile) sL[which][tid] = lreg;
     };
 
     const float c = a.sm_scale * kLog2e;
@@ -410,28 +513,32 @@ __global__ __launch_bounds__(kThreads, 2) void colsum_bf16_kernel(ChunkArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-    if (tile0 < ntile) gload(tile0);
+    if (tile0 < ntile) {
+        gload(tile0);
+        lstore(0);
+    }
+    __syncthreads();
     for (int rt = tile0; rt < ntile; ++rt) {
-        __syncthreads();
-        lstore();
-        __syncthreads();
+        const int cur = (rt - tile0) & 1;
         if (rt + 1 < ntile) gload(rt + 1);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int rloc = sub * 32 + lq;
-            const float lse2 = sL[rloc];
+            const float lse2 = sL[cur][rloc];
             f32x16 sacc = f32x16{};
-            const u16* qp = &sQ[rloc * QROW + 8 * hh];
+            const u16* qp = &sQ[cur][rloc * QROW + 8 * hh];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 sacc = mfma32(kf[ks], as_bf16x8(ld16(qp + 16 * ks)), sacc);
             const int row_first = rt * kRowsPerTile + sub * 32;
-            const int qpos_min = a.P + min(row_first, R - 1) / G;
+            const int rf = min(row_first, R - 1);
+            const int qpos_min = a.P + (G == 1 ? rf : (int)__umulhi((uint32_t)rf, g_magic));
             if (kmin >= 0 && kmax <= qpos_min) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[r] += fast_exp2(fmaf(sacc[r], c, -lse2));
             } else {
-                const int qpos = a.P + min(row_first + lq, R - 1) / G;
+                const int rq = min(row_first + lq, R - 1);
+                const int qpos = a.P + (G == 1 ? rq : (int)__umulhi((uint32_t)rq, g_magic));
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float p = fast_exp2(fmaf(sacc[r], c, -lse2));
@@ -439,6 +546,8 @@ __global__ __launch_bounds__(kThreads, 2) void colsum_bf16_kernel(ChunkArgs a) {
                 }
             }
         }
+        if (rt + 1 < ntile) lstore(cur ^ 1);
+        __syncthreads();
     }
 
 #pragma unroll
@@ -448,28 +557,50 @@ __global__ __launch_bounds__(kThreads, 2) void colsum_bf16_kernel(ChunkArgs a) {
         float sum = 0.f;
 #pragma unroll 8
         for (int j = 0; j < 32; ++j) sum += sRed[wave][lane][j];
-        const int kk = key0 + lane;
-        if (kk < n) a.cs_cache[(size_t)bg * a.NC + kk] = sum;
-        else if (kk < n + S) a.cs_new[(size_t)bg * S + (kk - n)] = sum;
+        const int idx = first + lane;
+        if (idx < limit) {
+            if (is_cache) a.cs_cache[(size_t)bg * a.NC + idx] = sum;
+            else a.cs_new[(size_t)bg * S + idx] = sum;
+        }
     }
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const ChunkArgs& a, hipStream_t s) {
+template <int D>
+hipError_t launch_attn_d(const ChunkArgs& a, hipStream_t s) {
+    // More than 64 KB of LDS per workgroup must be requested explicitly, once per device.
+    static unsigned configured = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned bit = 1u << (dev & 31);
+    if (!(configured & bit)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, AttnSmem<D>::BYTES);
+        if (e != hipSuccess) return e;
+        configured |= bit;
+    }
     const int R = a.G * a.S;
     const int total = ((R + kRowsPerBlock - 1) / kRowsPerBlock) * a.B * a.Hkv;
-    const dim3 grid(xcd_grid(total)), block(kThreads);
-    if (a.D == 128) hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, block, 0, s, a);
+    hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(xcd_grid(total)), dim3(kAttnThreads),
+                       AttnSmem<D>::BYTES, s, a);
     return hipGetLastError();
 }
 
+hipError_t launch_attn_bf16(const ChunkArgs& a, hipStream_t s) {
+    return a.D == 128 ? launch_attn_d<128>(a, s) : launch_attn_d<64>(a, s);
+}
+
 hipError_t launch_colsum_bf16(const ChunkArgs& a, hipStream_t s) {
-    const int total = ((a.n + a.S + kKeysPerBlock - 1) / kKeysPerBlock) * a.B * a.Hkv;
+    const int blocks = (a.n + kKeysPerBlock - 1) / kKeysPerBlock +
+                       (a.S + kKeysPerBlock - 1) / kKeysPerBlock;
+    const int total = blocks * a.B * a.Hkv;
+    // floor(r / G) = umulhi(r, ceil(2^32 / G)) for r * G < 2^32 (checked by the caller)
+    const uint32_t magic = a.G > 1 ? (uint32_t)((0x100000000ull + a.G - 1) / a.G) : 0u;
     const dim3 grid(xcd_grid(total)), block(kThreads);
-    if (a.D == 128) hipLaunchKernelGGL(colsum_bf16_kernel<128>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(colsum_bf16_kernel<64>, grid, block, 0, s, a);
+    if (a.D == 128) hipLaunchKernelGGL(colsum_bf16_kernel<128>, grid, block, 0, s, a, magic);
+    else hipLaunchKernelGGL(colsum_bf16_kernel<64>, grid, block, 0, s, a, magic);
     return hipGetLastError();
 }
 
