@@ -137,7 +137,8 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
         return fail(H2O_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
     {
         const long long G = dims->n_q_heads / dims->n_kv_heads;
-        if (G * G * (long long)chunk_len >= (1LL << 31))
+        if (G * G * (long long)chunk_len >= (1LL << 31) ||
+            G * (long long)chunk_len * dims->head_dim * 4 >= (1LL << 31))
             return fail(H2O_ERR_UNSUPPORTED, "query heads per KV head (%lld) too large for chunk_len %d",
                         G, chunk_len);
     }

@@ -67,6 +67,22 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer descriptors: a wave-uniform base and byte count in scalar
+// registers, a loop-invariant per-lane byte offset in a vector register.
+// Loads past `bytes` return zero, which is how partial tiles are padded.
+constexpr int kBufferFlags = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
+}
+__device__ __forceinline__ u32x4 bload16(Rsrc r, int voff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload4(Rsrc r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
+
 // Workgroup ids are dispatched round-robin over the 8 XCDs; give each XCD a
 // contiguous range of logical tiles so tiles that share K/V (or Q) share an L2.
 __device__ __forceinline__ int xcd_tile(int lin, int total) {
@@ -154,7 +170,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     const int b = bg / a.Hkv, g = bg % a.Hkv;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    // wave-uniform by construction; readfirstlane lets the compiler keep it scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kh = wave >> 2, rw = wave & 3, htid = tid & (kHalfThreads - 1);
     const int lq = lane & 31, hh = lane >> 5;
     const int row = rb * kRowsPerBlock + rw * 32 + lq;
@@ -192,36 +210,30 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     int preg = INT_MAX;
     const int dp = htid % VP, kg = htid / VP;
 
+    // Loop-invariant lane offsets (bytes) into a tile.
+    int koff[K_LD];
+#pragma unroll
+    for (int it = 0; it < K_LD; ++it) {
+        const int c = htid + it * kHalfThreads;
+        koff[it] = ((c / KCH) * D + (c % KCH) * 8) * 2;
+    }
+    const int voff = (kg * VKPG * D + 2 * dp) * 2;
     auto gload = [&](int tile) {
         const TileRef tr = tile_ref(tile, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
-        if (tr.valid == kKeysPerTile) {
+        const Rsrc rk = make_rsrc(tr.k, tr.valid * D * 2);
+        const Rsrc rv = make_rsrc(tr.v, tr.valid * D * 2);
 #pragma unroll
-            for (int it = 0; it < K_LD; ++it) {
-                const int c = htid + it * kHalfThreads;
-                kreg[it] = ld16(tr.k + (c / KCH) * D + (c % KCH) * 8);
-            }
+        for (int it = 0; it < K_LD; ++it) kreg[it] = bload16(rk, koff[it]);
 #pragma unroll
-            for (int e = 0; e < VKPG; ++e)
-                vreg[e] = *reinterpret_cast<const uint32_t*>(tr.v + (kg * VKPG + e) * D + 2 * dp);
-        } else {
-#pragma unroll
-            for (int it = 0; it < K_LD; ++it) {
-                const int c = htid + it * kHalfThreads;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (c / KCH < tr.valid) v = ld16(tr.k + (c / KCH) * D + (c % KCH) * 8);
-                kreg[it] = v;
-            }
-#pragma unroll
-            for (int e = 0; e < VKPG; ++e) {
-                const int key = kg * VKPG + e;
-                vreg[e] = key < tr.valid
-                              ? *reinterpret_cast<const uint32_t*>(tr.v + key * D + 2 * dp)
-                              : 0u;
+        for (int e = 0; e < VKPG; ++e) vreg[e] = bload4(rv, voff + e * D * 2);
+        if (htid < kKeysPerTile) {
+            if (tr.cache) {
+                const Rsrc rp = make_rsrc(posg + tr.first, tr.valid * 4);
+                preg = htid < tr.valid ? (int)bload4(rp, htid * 4) : INT_MAX;
+            } else {
+                preg = htid < tr.valid ? a.P + tr.first + htid : INT_MAX;
             }
         }
-        if (htid < kKeysPerTile)
-            preg = htid < tr.valid ? (tr.cache ? posg[tr.first + htid] : a.P + tr.first + htid)
-                                   : INT_MAX;
     };
     auto bufs = [&](int which, u16*& sK, u16*& sVt, int*& sPos) {
         unsigned char* base = smem + (kh * 2 + which) * L::BUF_BYTES;
@@ -339,10 +351,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     };
 
     // Half kh owns tiles kh, kh+2, kh+4, ...; both halves step together.
-    if (kh < ntiles) {
-        gload(kh);
-        lstore(0);
-    }
+    // Unconditional prologue (a half with no tile stages tile 0 and never reads
+    // it), so every path has waited for the Q loads before the loop.
+    gload(min(kh, ntiles - 1));
+    lstore(0);
     __syncthreads();
     for (int st = 0; st < steps; ++st) {
         const int cur = st & 1;
@@ -468,33 +480,60 @@ __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint
     // Chunk keys are invisible to the rows before their own position.
     const int tile0 = is_cache ? 0 : (block_first * G) / kRowsPerTile;
 
-    const u16* Q = static_cast<const u16*>(a.q);
+    // The G query heads of KV head g are contiguous in Q and in LSE.
+    const u16* Qg = static_cast<const u16*>(a.q) + (size_t)(b * a.Hq + g * G) * S * D;
+    const float* Lg = a.lse + (size_t)(b * a.Hq + g * G) * S;
+    const int q_bytes = G * S * D * 2;
     u32x4 qreg[Q_LD];
     float lreg = INFINITY;
-    auto row_split = [&](int r, int& hq, int& ipos) {
+    // When G divides the tile height every tile holds 64/G positions of all G
+    // heads, so a lane's offset inside the tile is loop-invariant.
+    const bool even_rows = (kRowsPerTile % G) == 0;
+    const int pos_per_tile = even_rows ? kRowsPerTile / G : 0;
+    int qoff[Q_LD];
+    int l_il = 0, l_off = 0;
+#pragma unroll
+    for (int it = 0; it < Q_LD; ++it) {
+        const int cidx = tid + it * kThreads;
+        const int rloc = cidx / QCH, col = (cidx % QCH) * 8;
+        qoff[it] = even_rows ? (((rloc % G) * S + rloc / G) * D + col) * 2 : col * 2;
+    }
+    if (even_rows && tid < kRowsPerTile) {
+        l_il = tid / G;
+        l_off = ((tid % G) * S + l_il) * 4;
+    }
+    auto row_split = [&](int r, int& hh_, int& ipos) {
         ipos = G == 1 ? r : (int)__umulhi((uint32_t)r, g_magic);
-        hq = g * G + (r - ipos * G);
+        hh_ = r - ipos * G;
     };
     auto gload = [&](int rt) {
+        if (even_rows) {
+            const int p0 = rt * pos_per_tile;                 // first position of the tile
+            const Rsrc rq = make_rsrc(Qg + (size_t)p0 * D, q_bytes - p0 * D * 2);
 #pragma unroll
-        for (int it = 0; it < Q_LD; ++it) {
-            const int cidx = tid + it * kThreads;
-            const int r = rt * kRowsPerTile + cidx / QCH, col = (cidx % QCH) * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (r < R) {
-                int hq, ipos;
-                row_split(r, hq, ipos);
-                v = ld16(Q + ((size_t)(b * a.Hq + hq) * S + ipos) * D + col);
+            for (int it = 0; it < Q_LD; ++it) qreg[it] = bload16(rq, qoff[it]);
+            if (tid < kRowsPerTile) {
+                const Rsrc rl = make_rsrc(Lg + p0, (G * S - p0) * 4);
+                const float v = __uint_as_float(bload4(rl, l_off));
+                lreg = p0 + l_il < S ? v * kLog2e : INFINITY;
             }
-            qreg[it] = v;
-        }
-        if (tid < kRowsPerTile) {
-            const int r = rt * kRowsPerTile + tid;
-            lreg = INFINITY;
-            if (r < R) {
-                int hq, ipos;
-                row_split(r, hq, ipos);
-                lreg = a.lse[(size_t)(b * a.Hq + hq) * S + ipos] * kLog2e;
+        } else {
+            const Rsrc rq = make_rsrc(Qg, q_bytes);
+#pragma unroll
+            for (int it = 0; it < Q_LD; ++it) {
+                const int cidx = tid + it * kThreads;
+                const int r = rt * kRowsPerTile + cidx / QCH;
+                int hh_ = 0, ipos = 0;
+                row_split(min(r, R - 1), hh_, ipos);
+                const int off = r < R ? ((hh_ * S + ipos) * D) * 2 + qoff[it] : q_bytes;
+                qreg[it] = bload16(rq, off);
+            }
+            if (tid < kRowsPerTile) {
+                const int r = rt * kRowsPerTile + tid;
+                int hh_ = 0, ipos = 0;
+                row_split(min(r, R - 1), hh_, ipos);
+                const float v = Lg[hh_ * S + ipos];
+                lreg = r < R ? v * kLog2e : INFINITY;
             }
         }
     };
@@ -513,10 +552,8 @@ __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-    if (tile0 < ntile) {
-        gload(tile0);
-        lstore(0);
-    }
+    gload(tile0);          // tile0 < ntile: a chunk key block starts before the last row
+    lstore(0);
     __syncthreads();
     for (int rt = tile0; rt < ntile; ++rt) {
         const int cur = (rt - tile0) & 1;
