@@ -208,6 +208,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     u32x4 kreg[K_LD];
     uint32_t vreg[VKPG];
     int preg = INT_MAX;
+    bool pvalid = false;
     const int dp = htid % VP, kg = htid / VP;
 
     // Loop-invariant lane offsets (bytes) into a tile.
@@ -226,12 +227,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
         for (int it = 0; it < K_LD; ++it) kreg[it] = bload16(rk, koff[it]);
 #pragma unroll
         for (int e = 0; e < VKPG; ++e) vreg[e] = bload4(rv, voff + e * D * 2);
+        // The loaded position is only consumed in lstore (after compute), so the
+        // prefetch stays in flight; invalid keys are marked there.
         if (htid < kKeysPerTile) {
+            pvalid = htid < tr.valid;
             if (tr.cache) {
                 const Rsrc rp = make_rsrc(posg + tr.first, tr.valid * 4);
-                preg = htid < tr.valid ? (int)bload4(rp, htid * 4) : INT_MAX;
+                preg = (int)bload4(rp, htid * 4);
             } else {
-                preg = htid < tr.valid ? a.P + tr.first + htid : INT_MAX;
+                preg = a.P + tr.first + htid;
             }
         }
     };
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
             *reinterpret_cast<u32x4*>(&sVt[(2 * dp) * VROW + kg * VKPG + e0]) = lo;
             *reinterpret_cast<u32x4*>(&sVt[(2 * dp + 1) * VROW + kg * VKPG + e0]) = hi;
         }
-        if (htid < kKeysPerTile) sPos[htid] = preg;
+        if (htid < kKeysPerTile) sPos[htid] = pvalid ? preg : INT_MAX;
     };
 
     const float c = a.sm_scale * kLog2e;          // logits -> log2 units
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 // order at the end, so the result is deterministic (no atomics).  Key blocks
 // follow the same cache / chunk split as the attention tiles.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool EVEN_ROWS>
 __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
     constexpr int KS = D / 16;
     constexpr int QROW = D + 8;
@@ -485,10 +489,12 @@ __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint
     const float* Lg = a.lse + (size_t)(b * a.Hq + g * G) * S;
     const int q_bytes = G * S * D * 2;
     u32x4 qreg[Q_LD];
-    float lreg = INFINITY;
+    uint32_t lraw = 0u;          // LSE bits as loaded; scaled and masked in lstore
+    bool lvalid = false;
     // When G divides the tile height every tile holds 64/G positions of all G
     // heads, so a lane's offset inside the tile is loop-invariant.
-    const bool even_rows = (kRowsPerTile % G) == 0;
+    // EVEN_ROWS: G divides the tile height (checked by the launcher).
+    constexpr bool even_rows = EVEN_ROWS;
     const int pos_per_tile = even_rows ? kRowsPerTile / G : 0;
     int qoff[Q_LD];
     int l_il = 0, l_off = 0;
@@ -507,15 +513,15 @@ __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint
         hh_ = r - ipos * G;
     };
     auto gload = [&](int rt) {
-        if (even_rows) {
+        if constexpr (even_rows) {
             const int p0 = rt * pos_per_tile;                 // first position of the tile
             const Rsrc rq = make_rsrc(Qg + (size_t)p0 * D, q_bytes - p0 * D * 2);
 #pragma unroll
             for (int it = 0; it < Q_LD; ++it) qreg[it] = bload16(rq, qoff[it]);
             if (tid < kRowsPerTile) {
                 const Rsrc rl = make_rsrc(Lg + p0, (G * S - p0) * 4);
-                const float v = __uint_as_float(bload4(rl, l_off));
-                lreg = p0 + l_il < S ? v * kLog2e : INFINITY;
+                lraw = bload4(rl, l_off);
+                lvalid = p0 + l_il < S;
             }
         } else {
             const Rsrc rq = make_rsrc(Qg, q_bytes);
@@ -532,8 +538,8 @@ __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint
                 const int r = rt * kRowsPerTile + tid;
                 int hh_ = 0, ipos = 0;
                 row_split(min(r, R - 1), hh_, ipos);
-                const float v = Lg[hh_ * S + ipos];
-                lreg = r < R ? v * kLog2e : INFINITY;
+                lraw = __float_as_uint(Lg[hh_ * S + ipos]);
+                lvalid = r < R;
             }
         }
     };
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint
             *reinterpret_cast<u32x4*>(&sQ[which][(cidx / QCH) * QROW + (cidx % QCH) * 8]) =
                 qreg[it];
         }
-        if (tid < kRowsPerTile) sL[which][tid] = lreg;
+        if (tid < kRowsPerTile) sL[which][tid] = lvalid ? __uint_as_float(lraw) * kLog2e : INFINITY;
     };
 
     const float c = a.sm_scale * kLog2e;
@@ -636,8 +642,14 @@ hipError_t launch_colsum_bf16(const ChunkArgs& a, hipStream_t s) {
     // floor(r / G) = umulhi(r, ceil(2^32 / G)) for r * G < 2^32 (checked by the caller)
     const uint32_t magic = a.G > 1 ? (uint32_t)((0x100000000ull + a.G - 1) / a.G) : 0u;
     const dim3 grid(xcd_grid(total)), block(kThreads);
-    if (a.D == 128) hipLaunchKernelGGL(colsum_bf16_kernel<128>, grid, block, 0, s, a, magic);
-    else hipLaunchKernelGGL(colsum_bf16_kernel<64>, grid, block, 0, s, a, magic);
+    const bool even = kRowsPerTile % a.G == 0;
+    if (a.D == 128) {
+        if (even) hipLaunchKernelGGL((colsum_bf16_kernel<128, true>), grid, block, 0, s, a, magic);
+        else hipLaunchKernelGGL((colsum_bf16_kernel<128, false>), grid, block, 0, s, a, magic);
+    } else {
+        if (even) hipLaunchKernelGGL((colsum_bf16_kernel<64, true>), grid, block, 0, s, a, magic);
+        else hipLaunchKernelGGL((colsum_bf16_kernel<64, false>), grid, block, 0, s, a, magic);
+    }
     return hipGetLastError();
 }
 
