@@ -423,7 +423,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 // follow the same cache / chunk split as the attention tiles.
 // ---------------------------------------------------------------------------
 template <int D, bool EVEN_ROWS>
-__global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
     constexpr int KS = D / 16;
     constexpr int QROW = D + 8;
     constexpr int QCH = D / 8;
@@ -469,9 +470,6 @@ __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint
             kf[ks] = as_bf16x8(v);
         }
     }
-    int kpos[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) kpos[r] = key_pos(first + 8 * (r >> 2) + 4 * hh + (r & 3));
     int kmin = key_pos(first + lq), kmax = kmin;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -558,40 +556,87 @@ __global__ __launch_bounds__(kThreads) void colsum_bf16_kernel(ChunkArgs a, uint
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-    gload(tile0);          // tile0 < ntile: a chunk key block starts before the last row
+    // S^T (this wave's 32 keys x 32 query rows of sub-tile `sub`) from buffer `buf`.
+    auto mma = [&](int buf, int sub) {
+        f32x16 r = f32x16{};
+        const u16* qp = &sQ[buf][(sub * 32 + lq) * QROW + 8 * hh];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) r = mfma32(kf[ks], as_bf16x8(ld16(qp + 16 * ks)), r);
+        return r;
+    };
+    auto first_pos = [&](int rt, int sub) {
+        const int rf = min(rt * kRowsPerTile + sub * 32, R - 1);
+        return a.P + (G == 1 ? rf : (int)__umulhi((uint32_t)rf, g_magic));
+    };
+    auto lane_pos = [&](int rt, int sub) {
+        const int rq = min(rt * kRowsPerTile + sub * 32 + lq, R - 1);
+        return a.P + (G == 1 ? rq : (int)__umulhi((uint32_t)rq, g_magic));
+    };
+    auto exp_full = [&](const f32x16& sv, float lse2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += fast_exp2(fmaf(sv[r], c, -lse2));
+    };
+    // Masked tiles (chunk keys near the diagonal, or empty-slot markers) re-read
+    // the positions of this lane's 16 keys instead of keeping them live.
+    auto exp_masked = [&](const f32x16& sv, float lse2, int qpos) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kp = key_pos(first + 8 * (r >> 2) + 4 * hh + (r & 3));
+            const float p = fast_exp2(fmaf(sv[r], c, -lse2));
+            acc[r] += (kp >= 0 && kp <= qpos) ? p : 0.f;
+        }
+    };
+    // Interleave the 8 MFMAs of one sub-tile with the exp/accumulate VALU work
+    // of the other, so the matrix pipe and the vector ALU run together.
+#define H2O_INTERLEAVE(VALU_PER_MFMA)                                  \
+    do {                                                             \
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           \
+        _Pragma("unroll") for (int i_ = 0; i_ < KS; ++i_) {          \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       \
+            __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0); \
+            if (i_ + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
+        }                                                            \
+    } while (0)
+
+    // Two-stage pipeline over row tiles.  Buffer (rt - tile0) & 1 holds tile rt.
+    // Step rt: store tile rt+1 (loaded during the previous step), load tile
+    // rt+2; stage A = MFMAs of sub-tile 1 with the exps of sub-tile 0; barrier;
+    // stage B = MFMAs of sub-tile 0 of tile rt+1 with the exps of sub-tile 1.
+    // A buffer is refilled only after the barrier that follows its last read.
+    gload(tile0);
     lstore(0);
+    if (tile0 + 1 < ntile) gload(tile0 + 1);
     __syncthreads();
+    const bool keys_ok = kmin >= 0;
+    f32x16 s0 = mma(0, 0);
     for (int rt = tile0; rt < ntile; ++rt) {
         const int cur = (rt - tile0) & 1;
-        if (rt + 1 < ntile) gload(rt + 1);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int rloc = sub * 32 + lq;
-            const float lse2 = sL[cur][rloc];
-            f32x16 sacc = f32x16{};
-            const u16* qp = &sQ[cur][rloc * QROW + 8 * hh];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sacc = mfma32(kf[ks], as_bf16x8(ld16(qp + 16 * ks)), sacc);
-            const int row_first = rt * kRowsPerTile + sub * 32;
-            const int rf = min(row_first, R - 1);
-            const int qpos_min = a.P + (G == 1 ? rf : (int)__umulhi((uint32_t)rf, g_magic));
-            if (kmin >= 0 && kmax <= qpos_min) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] += fast_exp2(fmaf(sacc[r], c, -lse2));
-            } else {
-                const int rq = min(row_first + lq, R - 1);
-                const int qpos = a.P + (G == 1 ? rq : (int)__umulhi((uint32_t)rq, g_magic));
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(fmaf(sacc[r], c, -lse2));
-                    acc[r] += (kpos[r] >= 0 && kpos[r] <= qpos) ? p : 0.f;
-                }
-            }
+        const bool has_next = rt + 1 < ntile;
+        const float l0 = sL[cur][lq], l1 = sL[cur][32 + lq];
+        if (has_next) lstore(cur ^ 1);
+        if (rt + 2 < ntile) gload(rt + 2);
+        f32x16 s1;
+        if (keys_ok && kmax <= first_pos(rt, 0)) {
+            s1 = mma(cur, 1);
+            exp_full(s0, l0);
+            H2O_INTERLEAVE(6);
+        } else {
+            s1 = mma(cur, 1);
+            exp_masked(s0, l0, lane_pos(rt, 0));
         }
-        if (rt + 1 < ntile) lstore(cur ^ 1);
         __syncthreads();
+        const bool full1 = keys_ok && kmax <= first_pos(rt, 1);
+        if (has_next && full1) {
+            s0 = mma(cur ^ 1, 0);
+            exp_full(s1, l1);
+            H2O_INTERLEAVE(6);
+        } else {
+            if (has_next) s0 = mma(cur ^ 1, 0);
+            if (full1) exp_full(s1, l1);
+            else exp_masked(s1, l1, lane_pos(rt, 1));
+        }
     }
+#undef H2O_INTERLEAVE
 
 #pragma unroll
     for (int r = 0; r < 16; ++r) sRed[wave][8 * (r >> 2) + 4 * hh + (r & 3)][lq] = acc[r];
