@@ -95,6 +95,102 @@ def cpu_baseline(wl, budget_s: float):
             "tokens_per_s": chunks * wl.chunk / dt, "ms_per_chunk": dt / chunks * 1e3}
 
 
+DECODE_METRIC = "H2O decode step (attn+score+evict) tokens/s, % HBM roofline"
+
+
+def decode_slot_bytes(wl) -> int:
+    """Algorithmic HBM bytes per cache slot per decode step: K and V rows read,
+    the score read and written, the position read."""
+    return 2 * wl.head_dim * 2 + 8 + 4
+
+
+def run_decode(args):
+    import torch
+
+    import h2o_sparse_attention_amd as h2o
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dims = h2o.H2ODims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity,
+                       wl.recent_window, wl.dtype)
+    dt = dims.torch_dtype
+    t_gen = time.perf_counter()
+    st = W.decode_initial_state(wl)
+    snap = {k: torch.from_numpy(st[k]).to(dev, dt if k in ("k", "v") else None)
+            for k in ("k", "v", "pos", "phi")}
+    del st
+    steps_in = []
+    for t in range(wl.seq_len):
+        x = W.decode_step_inputs(wl, t)
+        steps_in.append(tuple(torch.from_numpy(x[k]).to(dev, dt) for k in ("q", "k", "v")))
+    print(f"[bench] decode state + {wl.seq_len} steps generated in "
+          f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    cache = h2o.H2OCache(dims, dev)
+    B, Hq, Hkv, D, NC = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity
+    bufs = {"out": torch.empty(B, Hq, 1, D, dtype=dt, device=dev),
+            "lse": torch.empty(B, Hq, 1, dtype=torch.float32, device=dev),
+            "colsum_cache": torch.empty(B, Hkv, NC, dtype=torch.float32, device=dev),
+            "colsum_new": torch.empty(B, Hkv, 1, dtype=torch.float32, device=dev),
+            "freed_slots": torch.empty(B, Hkv, 1, dtype=torch.int32, device=dev),
+            "workspace": torch.zeros(h2o.workspace_bytes(dims, 1), dtype=torch.uint8, device=dev)}
+
+    def reset():
+        cache.load(snap["k"], snap["v"], snap["pos"].to(torch.int32), snap["phi"].float(),
+                   NC, NC)
+
+    def run(nsteps):
+        for t in range(nsteps):
+            q, k, v = steps_in[t % len(steps_in)]
+            h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs)
+
+    for _ in range(args.warmup):
+        reset()
+        run(wl.seq_len)
+    reset()
+    torch.cuda.synchronize()
+    n_launch = args.steps * wl.seq_len
+    timers = {k: h2o.KernelTimer(k, n_launch) for k in ("decode", "update", "select", "insert")}
+    total_s = 0.0
+    for t_ in timers.values():
+        t_.__enter__()
+    for _ in range(args.steps):
+        reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(wl.seq_len)
+        torch.cuda.synchronize()
+        total_s += time.perf_counter() - t0
+    for t_ in timers.values():
+        t_.__exit__(None, None, None)
+    n_tok = args.steps * wl.seq_len * B
+    us_per_step = total_s / (args.steps * wl.seq_len) * 1e6
+    slot_bytes = decode_slot_bytes(wl)
+    step_bytes = B * Hkv * NC * slot_bytes
+    dec = timers["decode"]
+    kv_bytes = B * Hkv * NC * 2 * D * 2            # K and V rows read by the attention launch
+    achieved = kv_bytes / (dec.mean_ms * 1e-3) / 1e9
+    line = {
+        "metric": DECODE_METRIC, "value": round(n_tok / total_s, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_s / args.steps * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "capacity": NC, "recent_window": wl.recent_window,
+                   "decode_steps": wl.seq_len, "parallelism": "single-gpu"},
+        "us_per_decode_step": round(us_per_step, 2),
+        "step_hbm_gbs": round(step_bytes / (us_per_step * 1e-6) / 1e9, 1),
+        "frac_hbm_peak_step": round(step_bytes / (us_per_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "kernel_mean_us": {k: round(t_.mean_ms * 1e3, 2) for k, t_ in timers.items()},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode_attn_kernel<128>", "launches": dec.launches,
+                     "mean_launch_us": round(dec.mean_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,7 +211,9 @@ def main():
     import workloads as W
 
     wl = W.WORKLOADS[args.workload]
-    assert not wl.decode and wl.layers == 1, "bench runs a single-layer prefill workload"
+    if wl.decode:
+        return run_decode(args)
+    assert wl.layers == 1, "bench runs a single-layer prefill workload"
     dev = torch.device("cuda:0")
     dims = h2o.H2ODims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity,
                        wl.recent_window, wl.dtype)

@@ -116,7 +116,8 @@ const char* h2o_last_error(void) { return g_error.c_str(); }
 
 size_t h2o_workspace_bytes(const h2o_dims_t* dims, int32_t chunk_len) {
     if (validate_dims(dims) != H2O_OK || chunk_len < 1) return 0;
-    if (chunk_len == 1 && dims->dtype == H2O_BF16 && dims->head_dim == 128)
+    if (chunk_len == 1 && dims->dtype == H2O_BF16 && dims->head_dim == 128 &&
+        dims->n_q_heads / dims->n_kv_heads <= 32)
         return decode_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads,
                                       dims->capacity);
     return 0;

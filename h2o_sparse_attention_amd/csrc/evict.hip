@@ -110,6 +110,29 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
             key[e] = kv;
         }
 
+        if (k == 1) {
+            // Single victim (decode): argmin of (key, slot), one reduction.
+            uint64_t best = ~0ull;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const uint64_t v = ((uint64_t)key[e] << 32) | (uint32_t)(j0 + e);
+                best = v < best ? v : best;
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const uint64_t o = __shfl_xor(best, off);
+                best = o < best ? o : best;
+            }
+            __shared__ uint64_t sBest[kSelWaves];
+            if (lane == 0) sBest[wave] = best;
+            __syncthreads();
+            if (tid == 0) {
+                uint64_t m = sBest[0];
+                for (int w = 1; w < kSelWaves; ++w) m = sBest[w] < m ? sBest[w] : m;
+                freed[0] = (int)(uint32_t)m;
+            }
+            return;
+        }
         uint32_t T = 0u;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t X = T | (1u << bit);
