@@ -341,9 +341,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
             const float* rec0 = ws.partial + ((size_t)bg * ws.nsplit * G + hh) * (D + 2);
             const size_t stride = (size_t)G * (D + 2);
             float acc = bf(Vn[d]) * fast_exp2(sNew[hh] - m);
-            for (int sp = 0; sp < nsplit_rt; ++sp) {
-                const float ms = rec0[sp * stride];
-                if (ms != -INFINITY) acc += rec0[sp * stride + 2 + d] * fast_exp2(ms - m);
+            // Issue the split loads in batches of 8 so they are in flight together.
+            for (int sp0 = 0; sp0 < nsplit_rt; sp0 += 8) {
+                float ms[8], ov[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int sp = min(sp0 + u, nsplit_rt - 1);
+                    ms[u] = rec0[sp * stride];
+                    ov[u] = rec0[sp * stride + 2 + d];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (sp0 + u < nsplit_rt && ms[u] != -INFINITY)
+                        acc += ov[u] * fast_exp2(ms[u] - m);
             }
             const float inv = fast_exp2(m - sLse2[hh]);       // 1 / l
             const size_t oi = (size_t)(b * a.Hq + g * G + hh) * D + d;
@@ -358,10 +368,26 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
     }
     const int j0 = kc * kFinishKeys, j1 = min(n, j0 + kFinishKeys);
     const float* lrow = ws.logits + (size_t)bg * G * ws.ncp;
-    for (int j = j0 + tid; j < j1; j += kDecThreads) {
-        float cs = 0.f;
-        for (int hh = 0; hh < G; ++hh) cs += fast_exp2(lrow[(size_t)hh * ws.ncp + j] - sLse2[hh]);
-        a.cs_cache[(size_t)bg * a.NC + j] = cs;
+    constexpr int U = kFinishKeys / kDecThreads;           // slots per thread
+    static_assert(kFinishKeys % kDecThreads == 0, "finish tiling");
+    float cs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cs[u] = 0.f;
+    for (int hh = 0; hh < G; ++hh) {
+        const float l2 = sLse2[hh];
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + tid + u * kDecThreads;
+            v[u] = j < j1 ? lrow[(size_t)hh * ws.ncp + j] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) cs[u] += fast_exp2(v[u] - l2);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = j0 + tid + u * kDecThreads;
+        if (j < j1) a.cs_cache[(size_t)bg * a.NC + j] = cs[u];
     }
 }
 

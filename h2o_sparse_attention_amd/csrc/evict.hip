@@ -12,24 +12,35 @@ namespace h2o {
 namespace {
 
 // ------------------------------------------------------------------ update
+// One (b, kv head) row per blockIdx.y; float4 where the row allows it.
 __global__ __launch_bounds__(256) void update_scores_kernel(float* __restrict__ score,
                                                             const float* __restrict__ cs,
-                                                            int rows, int NC, int n) {
-    const size_t total = (size_t)rows * n;
-    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (size_t)gridDim.x * blockDim.x) {
-        const size_t r = e / n, j = e % n;
-        const size_t idx = r * NC + j;
-        score[idx] += cs[idx];
+                                                            int NC, int n, bool vec) {
+    const size_t base = (size_t)blockIdx.y * NC;
+    if (vec) {
+        const int n4 = n / 4;
+        float4* s4 = reinterpret_cast<float4*>(score + base);
+        const float4* c4 = reinterpret_cast<const float4*>(cs + base);
+        for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
+            float4 v = s4[i];
+            const float4 w = c4[i];
+            v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+            s4[i] = v;
+        }
+        for (int j = n4 * 4 + blockIdx.x * blockDim.x + threadIdx.x; j < n;
+             j += gridDim.x * blockDim.x)
+            score[base + j] += cs[base + j];
+    } else {
+        for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x)
+            score[base + j] += cs[base + j];
     }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, size_t per_row,
-                                                   size_t stride, int rows, size_t offset) {
-    const size_t total = (size_t)rows * per_row;
-    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (size_t)gridDim.x * blockDim.x)
-        p[(e / per_row) * stride + offset + e % per_row] = 0.f;
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int per_row,
+                                                   size_t stride, size_t offset) {
+    float* row = p + (size_t)blockIdx.y * stride + offset;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < per_row; j += gridDim.x * blockDim.x)
+        row[j] = 0.f;
 }
 
 // ------------------------------------------------------------------ select
@@ -97,9 +108,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
         const int t_now = a.P + S;
         const int j0 = tid * KPT;
         uint32_t key[KPT];
+        // Coalesced pass: slot j = e*1024 + tid forms its order key into LDS; then
+        // each thread takes KPT consecutive slots, so thread order is slot order.
+        extern __shared__ uint32_t sKeys[];
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const int j = j0 + e;
+            const int j = e * kSelThreads + tid;
             uint32_t kv = kAbsent;
             if (j < n) {
                 const int pj = ps[j];
@@ -107,8 +121,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
                 if (a.score_mode == H2O_SCORE_H2O_NORM) v = v / (float)(t_now - pj);
                 kv = pj < thr ? order_key(v) : kIneligible;
             }
-            key[e] = kv;
+            sKeys[j + j / 16] = kv;               // one pad word per 16: no bank conflicts
         }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) key[e] = sKeys[j0 + e + (j0 + e) / 16];
 
         if (k == 1) {
             // Single victim (decode): argmin of (key, slot), one reduction.
@@ -211,32 +228,51 @@ __global__ __launch_bounds__(256) void insert_kernel(EvictArgs a) {
 
 hipError_t launch_update_scores(float* score, const float* cs, int rows, int NC, int n,
                                 hipStream_t s) {
-    const size_t total = (size_t)rows * n;
-    if (total == 0) return hipSuccess;
-    const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-    hipLaunchKernelGGL(update_scores_kernel, dim3(blocks), dim3(256), 0, s, score, cs, rows, NC, n);
+    if (rows == 0 || n == 0) return hipSuccess;
+    const int per_block = 256 * 4;
+    int bx = (n + per_block - 1) / per_block;
+    if (bx > 64) bx = 64;
+    // float4 rows need 16-byte aligned row starts in both arrays.
+    const bool vec = NC % 4 == 0 && ((reinterpret_cast<uintptr_t>(score) |
+                                      reinterpret_cast<uintptr_t>(cs)) & 15) == 0;
+    hipLaunchKernelGGL(update_scores_kernel, dim3(bx, rows), dim3(256), 0, s, score, cs, NC, n,
+                       vec);
     return hipGetLastError();
 }
 
 hipError_t launch_zero_f32(float* p, size_t per_row, size_t stride, int rows, size_t offset,
                            hipStream_t s) {
-    const size_t total = (size_t)rows * per_row;
-    if (total == 0) return hipSuccess;
-    const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-    hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, s, p, per_row, stride, rows, offset);
+    if (rows == 0 || per_row == 0) return hipSuccess;
+    int bx = (int)((per_row + 1023) / 1024);
+    if (bx > 64) bx = 64;
+    hipLaunchKernelGGL(zero_kernel, dim3(bx, rows), dim3(256), 0, s, p, (int)per_row, stride,
+                       offset);
     return hipGetLastError();
 }
 
 hipError_t launch_select(const EvictArgs& a, hipStream_t s) {
     const dim3 grid(a.B * a.Hkv), block(kSelThreads);
     const int kpt = (a.NC + kSelThreads - 1) / kSelThreads;
-    if (kpt <= 1) hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, s, a);
-    else if (kpt <= 2) hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, s, a);
-    else if (kpt <= 4) hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, s, a);
-    else if (kpt <= 8) hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, s, a);
-    else if (kpt <= 16) hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(select_kernel<32>, grid, block, 0, s, a);
-    return hipGetLastError();
+    int p2 = 1;
+    while (p2 < kpt) p2 <<= 1;
+    const size_t lds = (size_t)p2 * kSelThreads * 4 * 17 / 16;   // order keys, padded
+    auto go = [&](auto kernel) -> hipError_t {
+        // Above 64 KB of LDS the attribute must be raised first (once per device).
+        if (lds > 65536) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, a);
+        return hipGetLastError();
+    };
+    if (p2 <= 1) return go(select_kernel<1>);
+    if (p2 <= 2) return go(select_kernel<2>);
+    if (p2 <= 4) return go(select_kernel<4>);
+    if (p2 <= 8) return go(select_kernel<8>);
+    if (p2 <= 16) return go(select_kernel<16>);
+    return go(select_kernel<32>);
 }
 
 hipError_t launch_insert(const EvictArgs& a, hipStream_t s) {
