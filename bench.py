@@ -27,7 +27,7 @@ METRIC = "H2O chunk-attn+score+evict TFLOP/s & tokens/s (chunk 1k, 64k ctx), % r
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_chunk1k_ctx64k_traffic.txt")
-ATTN_SOURCE = os.path.join(ROOT, "h2o_sparse_attention_amd", "csrc", "attn_bf16.hip")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_b16_cache16k_traffic.txt")
 
 
 def pairs_per_head(n_before: int, S: int) -> int:
@@ -44,20 +44,18 @@ def chunk_schedule(wl):
     return out
 
 
-def source_digest() -> str:
-    return hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
-
-
-def read_traffic(launch_flops_unused=None):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source."""
+def read_traffic(path: str):
+    """HBM bytes per launch of the dominant kernel from a committed rocprofv3
+    counter summary, or None unless it was taken on the current kernel source."""
     try:
         fields = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(path):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 fields[k.strip()] = v.strip()
-        if fields.get("kernel_source_sha256_16") != source_digest():
+        src = os.path.join(ROOT, fields["kernel_source"])
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if fields.get("kernel_source_sha256_16") != digest:
             return None
         return float(fields["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -93,6 +91,23 @@ def cpu_baseline(wl, budget_s: float):
             "sample": f"{chunks} steady chunk(s) of {wl.name} (full cache, "
                       f"{wl.capacity}+{wl.chunk} keys, fp64 NumPy), {dt:.1f} s",
             "tokens_per_s": chunks * wl.chunk / dt, "ms_per_chunk": dt / chunks * 1e3}
+
+
+def copy_probe(mib: int) -> None:
+    """Plain device copies of a known size (mib MiB read, mib MiB written), run
+    before the workload so that HBM byte counters read for the path's kernels
+    can be scaled by what the same counters read for a copy."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    print(f"[bench] copy probe: 3 x copy_ and 3 x neg of {mib} MiB", file=sys.stderr,
+          flush=True)
 
 
 DECODE_METRIC = "H2O decode step (attn+score+evict) tokens/s, % HBM roofline"
@@ -183,7 +198,8 @@ def run_decode(args):
         "frac_hbm_peak_step": round(step_bytes / (us_per_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "kernel_mean_us": {k: round(t_.mean_ms * 1e3, 2) for k, t_ in timers.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic(DECODE_TRAFFIC_FILE),
                      "kernel": "decode_attn_kernel<128>", "launches": dec.launches,
                      "mean_launch_us": round(dec.mean_ms * 1e3, 2)},
         "cpu_baseline": None,
@@ -199,6 +215,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run plain copies of this size first (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -211,6 +229,8 @@ def main():
     import workloads as W
 
     wl = W.WORKLOADS[args.workload]
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
     if wl.decode:
         return run_decode(args)
     assert wl.layers == 1, "bench runs a single-layer prefill workload"
@@ -275,7 +295,7 @@ def main():
     attn_flops_per_launch = f4 / wl.n_chunks          # QK^T + PV, averaged over the chunks
     attn_ms = attn.mean_ms
     achieved = attn_flops_per_launch / (attn_ms * 1e-3) / 1e12
-    traffic = read_traffic()
+    traffic = read_traffic(TRAFFIC_FILE)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": "attn_bf16_kernel<128>",

@@ -274,11 +274,11 @@ h2o_status_t h2o_kernel_timer_start(int32_t kernel, int32_t max_launches) {
     destroy_events(t);
     t.ev.resize(2 * (size_t)max_launches);
     for (size_t i = 0; i < t.ev.size(); ++i) {
-        hipError_t e = hipEventCreate(&t.ev[i]);
+        hipError_t e = hipEventCreateWithFlags(&t.ev[i], hipEventDisableSystemFence);
         if (e != hipSuccess) {
             t.ev.resize(i);
             destroy_events(t);
-            return check_hip(e, "hipEventCreate");
+            return check_hip(e, "hipEventCreateWithFlags");
         }
     }
     t.max = max_launches;
