@@ -18,14 +18,15 @@
 // physical key 16*(r/8) + 8*hh + r%8: eight consecutive keys per lane and
 // per 16-key step, which is exactly the k-slot order of the B operand of the
 // P V product.  O^T = V^T P^T then takes P^T straight from registers (no
-// shuffle) and V^T from LDS (V is transposed while it is staged), and the
-// O^T accumulator keeps the lane's own query row, so the softmax rescale
-// needs no cross-lane traffic.
+// shuffle) and V^T from LDS through transposing reads, and the O^T
+// accumulator keeps the lane's own query row, so the softmax rescale needs no
+// cross-lane traffic.
 #include "h2o_internal.h"
 #include "device_common.h"
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 namespace h2o {
 namespace {
@@ -66,43 +67,88 @@ __device__ __forceinline__ TileRef tile_ref(int tile, int cache_tiles, int n, in
     return t;
 }
 
-template <int D>
-struct AttnSmem {
-    static constexpr int KROW = D + 8;                  // LDS K row, +16 B pad
-    static constexpr int VROW = kKeysPerTile + 8;       // LDS V^T row, +16 B pad
-    static constexpr int K_BYTES = kKeysPerTile * KROW * 2;
-    static constexpr int V_BYTES = D * VROW * 2;
-    static constexpr int BUF_BYTES = K_BYTES + V_BYTES + kKeysPerTile * 4;
-    static constexpr int MERGE_FLOATS = 2 + (D / 32) * 16;   // m, l, O^T accumulators
-    static constexpr int MERGE_BYTES = 4 * MERGE_FLOATS * 64 * 4;
-    static constexpr int BYTES = 4 * BUF_BYTES > MERGE_BYTES ? 4 * BUF_BYTES : MERGE_BYTES;
-};
-
 // ---------------------------------------------------------------------------
 // Attention pass: O and LSE for 128 query rows of one (b, kv head).
-// Rows of a KV head are ordered position-major: row r = i*G + hh is query
-// head g*G + hh at chunk position i.  Eight waves: waves 0-3 and 4-7 own the
-// same four 32-row groups and split the key tiles between them (even / odd
-// tiles), each half with its own double-buffered LDS tiles; the two partial
-// softmax states are merged through LDS at the end.
+// Rows of a KV head are ordered position-major: row r = i*G + hl is query
+// head g*G + hl at chunk position i.  Eight waves: waves 0-3 and 4-7 (the two
+// halves) own the same four 32-row groups and split the key tiles between
+// them (tiles 0, 2, 4, ... and 1, 3, 5, ...); the two partial softmax states
+// are merged through LDS at the end.
+//
+// Staging.  K and V tiles go from global memory straight into LDS (buffer
+// loads with the LDS destination, 16 bytes per lane, lane-linear in LDS), so
+// no registers hold tiles in flight.  Rows are stored unpadded with their
+// 16-byte chunks XOR-swizzled by row: the lane that fills LDS chunk c of row r
+// fetches global chunk c ^ swz(r).  The swizzles keep the MFMA operand reads
+// free of bank conflicts.  V stays row-major and is read transposed by
+// ds_read_b64_tr_b16: a 16-lane group addresses four rows of four consecutive
+// bf16 and lane j receives column j%4 of rows j/4, j/4+4, j/4+8, j/4+12, i.e.
+// four keys of one d, which are the k-slots of the V^T operand.
+//
+// Pipeline.  Each half has two K buffers and two V buffers.  Iteration j of a
+// half starts the loads of K(j+2) and V(j+1), then computes S(j+1) = K Q^T by
+// MFMA while the exponentials of tile j run on the VALU, then O += V(j)^T P(j)^T,
+// then waits for its loads and meets the other waves at one barrier.
 // ---------------------------------------------------------------------------
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kHalfThreads = kAttnThreads / 2;
+
+template <int D>
+struct AttnTile {
+    static constexpr int RB = 2 * D;                    // bytes per K / V row
+    static constexpr int U16 = kKeysPerTile * D;        // u16 per tile
+    static constexpr int LOADS = kKeysPerTile * RB / 1024 / 4;   // 1 KB loads per wave per tile
+};
+
+// LDS chunk c of row r holds logical chunk c ^ swz(r) (16-byte chunks).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Loads that write LDS are counted by vmcnt; the compiler only tracks them as
+// this wave's own writes, so before a barrier that publishes them to the other
+// waves each wave waits for all of its own (s_waitcnt vmcnt(0); expcnt and
+// lgkmcnt left at their maximum in the gfx9 encoding).
+constexpr int kWaitVmcnt0 = 0x0F70;
+__device__ __forceinline__ void publish_lds_loads() {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+}
+
+__device__ __forceinline__ void load_lds16(Rsrc r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(Rsrc r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+// Eight bf16 of the V^T operand: two transposing reads, four rows apart.
+__device__ __forceinline__ bf16x8 ld_vt(const unsigned char* p, int row_bytes4) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + row_bytes4));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
-    using L = AttnSmem<D>;
+    using T = AttnTile<D>;
     constexpr int KS = D / 16;                    // MFMA k-steps over head_dim
     constexpr int DT = D / 32;                    // 32-row tiles of O^T
-    constexpr int KROW = L::KROW, VROW = L::VROW;
-    constexpr int KCH = D / 8;                    // 16-byte chunks per key row
-    constexpr int K_LD = kKeysPerTile * KCH / kHalfThreads;
-    constexpr int VP = D / 2;                     // d pairs
-    constexpr int VKG = kHalfThreads / VP;        // key groups for V staging
-    constexpr int VKPG = kKeysPerTile / VKG;      // keys per group (8 or 16)
-    static_assert(K_LD >= 1 && VKPG % 8 == 0, "tile shape");
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    constexpr int RB = T::RB;
+    // Stage s of half h: sK<s>[h], sV<s>[h], sP<s>[h] (positions of cache keys).
+    // Separate objects per stage let the compiler see that loads into one stage
+    // never alias reads of the other.
+    __shared__ __attribute__((aligned(1024))) u16 sK0[2][T::U16];
+    __shared__ __attribute__((aligned(1024))) u16 sK1[2][T::U16];
+    __shared__ __attribute__((aligned(1024))) u16 sV0[2][T::U16];
+    __shared__ __attribute__((aligned(1024))) u16 sV1[2][T::U16];
+    __shared__ __attribute__((aligned(16))) int sP0[2][kKeysPerTile];
+    __shared__ __attribute__((aligned(16))) int sP1[2][kKeysPerTile];
 
     const int R = a.G * a.S;
     const int nrb = (R + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -116,8 +162,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     const int lane = tid & 63;
     // wave-uniform by construction; readfirstlane lets the compiler keep it scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kh = wave >> 2, rw = wave & 3, htid = tid & (kHalfThreads - 1);
+    const int kh = wave >> 2, rw = wave & 3;
     const int lq = lane & 31, hh = lane >> 5;
+    const int g16 = lane >> 4, j16 = lane & 15;
     const int row = rb * kRowsPerBlock + rw * 32 + lq;
     const bool row_ok = row < R;
     const int i = row_ok ? row / a.G : a.S - 1;
@@ -139,6 +186,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     const int last_row = min(R - 1, rb * kRowsPerBlock + kRowsPerBlock - 1);
     const int ntiles = cache_tiles + (last_row / a.G) / kKeysPerTile + 1;
     const int steps = (ntiles + 1) / 2;
+    const int mine = (ntiles - kh + 1) / 2;       // tiles of this half: kh, kh+2, ...
     const int wave_row0 = min(R - 1, rb * kRowsPerBlock + rw * 32);
     const int qpos_wave_min = a.P + wave_row0 / a.G;
 
@@ -148,69 +196,41 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     const u16* Vn = static_cast<const u16*>(a.vn) + (size_t)bg * S * D;
     const int32_t* posg = a.pos + (size_t)bg * a.NC;
 
-    u32x4 kreg[K_LD];
-    uint32_t vreg[VKPG];
-    int preg = INT_MAX;
-    bool pvalid = false;
-    const int dp = htid % VP, kg = htid / VP;
+    // Global byte offset (within a tile) of this lane's 16-byte load `it`:
+    // LDS chunk cp of row r is filled from global chunk cp ^ swz(r).
+    auto goff = [&](int it, bool is_v) {
+        const int off = (it * 4 + rw) * 1024 + 16 * lane;
+        const int r = off / RB, cp = (off % RB) / 16;
+        return r * RB + 16 * (cp ^ (is_v ? swz_v<D>(r) : swz_k<D>(r)));
+    };
+    // K and the key positions of tile jt (positions only for cache tiles).
+    auto issue_kp = [&](u16* dst, int* pdst, int jt) {
+        const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
+        const Rsrc rk = make_rsrc(tr.k, tr.valid * RB);
+        unsigned char* d = reinterpret_cast<unsigned char*>(dst) + rw * 1024;
+#pragma unroll
+        for (int it = 0; it < T::LOADS; ++it) load_lds16(rk, d + it * 4096, goff(it, false));
+        if (tr.cache && rw == 0) {
+            const Rsrc rp = make_rsrc(posg + tr.first, tr.valid * 4);
+            load_lds4(rp, pdst, lane * 4);
+        }
+    };
+    auto issue_v = [&](u16* dst, int jt) {
+        const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
+        const Rsrc rv = make_rsrc(tr.v, tr.valid * RB);
+        unsigned char* d = reinterpret_cast<unsigned char*>(dst) + rw * 1024;
+#pragma unroll
+        for (int it = 0; it < T::LOADS; ++it) load_lds16(rv, d + it * 4096, goff(it, true));
+    };
 
-    // Loop-invariant lane offsets (bytes) into a tile.
-    int koff[K_LD];
-#pragma unroll
-    for (int it = 0; it < K_LD; ++it) {
-        const int c = htid + it * kHalfThreads;
-        koff[it] = ((c / KCH) * D + (c % KCH) * 8) * 2;
-    }
-    const int voff = (kg * VKPG * D + 2 * dp) * 2;
-    auto gload = [&](int tile) {
-        const TileRef tr = tile_ref(tile, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
-        const Rsrc rk = make_rsrc(tr.k, tr.valid * D * 2);
-        const Rsrc rv = make_rsrc(tr.v, tr.valid * D * 2);
-#pragma unroll
-        for (int it = 0; it < K_LD; ++it) kreg[it] = bload16(rk, koff[it]);
-#pragma unroll
-        for (int e = 0; e < VKPG; ++e) vreg[e] = bload4(rv, voff + e * D * 2);
-        // The loaded position is only consumed in lstore (after compute), so the
-        // prefetch stays in flight; invalid keys are marked there.
-        if (htid < kKeysPerTile) {
-            pvalid = htid < tr.valid;
-            if (tr.cache) {
-                const Rsrc rp = make_rsrc(posg + tr.first, tr.valid * 4);
-                preg = (int)bload4(rp, htid * 4);
-            } else {
-                preg = a.P + tr.first + htid;
-            }
-        }
-    };
-    auto bufs = [&](int which, u16*& sK, u16*& sVt, int*& sPos) {
-        unsigned char* base = smem + (kh * 2 + which) * L::BUF_BYTES;
-        sK = reinterpret_cast<u16*>(base);
-        sVt = reinterpret_cast<u16*>(base + L::K_BYTES);
-        sPos = reinterpret_cast<int*>(base + L::K_BYTES + L::V_BYTES);
-    };
-    auto lstore = [&](int which) {
-        u16 *sK, *sVt;
-        int* sPos;
-        bufs(which, sK, sVt, sPos);
-#pragma unroll
-        for (int it = 0; it < K_LD; ++it) {
-            const int c = htid + it * kHalfThreads;
-            *reinterpret_cast<u32x4*>(&sK[(c / KCH) * KROW + (c % KCH) * 8]) = kreg[it];
-        }
-#pragma unroll
-        for (int e0 = 0; e0 < VKPG; e0 += 8) {
-            u32x4 lo, hi;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t w0 = vreg[e0 + 2 * j], w1 = vreg[e0 + 2 * j + 1];
-                lo[j] = (w0 & 0xffffu) | (w1 << 16);
-                hi[j] = (w0 >> 16) | (w1 & 0xffff0000u);
-            }
-            *reinterpret_cast<u32x4*>(&sVt[(2 * dp) * VROW + kg * VKPG + e0]) = lo;
-            *reinterpret_cast<u32x4*>(&sVt[(2 * dp + 1) * VROW + kg * VKPG + e0]) = hi;
-        }
-        if (htid < kKeysPerTile) sPos[htid] = pvalid ? preg : INT_MAX;
-    };
+    // Operand offsets: K row perm_key(lq) (+32 per sub-tile), k-step ks at
+    // kb ^ 32*ks; V^T rows 8*hh + j16/4 (+16*s2, +32*sub, +4 for the second
+    // read), d block dt at vb ^ 64*dt.
+    const int prow = perm_key(lq);
+    const int kb = prow * RB + 16 * (hh ^ swz_k<D>(prow));
+    const int vrow = 8 * hh + (j16 >> 2);
+    const int vb = vrow * RB + 16 * ((2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ swz_v<D>(vrow)) +
+                   8 * (j16 & 1);
 
     const float c = a.sm_scale * kLog2e;          // logits -> log2 units
     const float tau_raw = kRescaleLog2 / c;
@@ -218,44 +238,58 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
-    const int prow = perm_key(lq);
 
-    auto compute = [&](int which) {
-        u16 *sK, *sVt;
-        int* sPos;
-        bufs(which, sK, sVt, sPos);
-        f32x16 s[2];
+    // S^T = K Q^T of the tile in sKt.
+    auto qk = [&](const u16* sKt, f32x16 (&sd)[2]) {
+        const unsigned char* base = reinterpret_cast<const unsigned char*>(sKt);
+        sd[0] = f32x16{};
+        sd[1] = f32x16{};
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            s[sub] = f32x16{};
-            const u16* kp = &sK[(sub * 32 + prow) * KROW + 8 * hh];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s[sub] = mfma32(as_bf16x8(ld16(kp + 16 * ks)), qf[ks], s[sub]);
-        }
-        // Implicit positional mask; skipped when every key of the tile is
-        // visible to every row of this wave.
-        const int kp_lane = sPos[lane];
-        const bool vis_all = kp_lane >= 0 && kp_lane <= qpos_wave_min;
-        if (!__all(vis_all)) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int sub = 0; sub < 2; ++sub)
+                sd[sub] = mfma32(as_bf16x8(ld16(base + ((kb ^ (32 * ks)) + sub * 32 * RB))),
+                                 qf[ks], sd[sub]);
+    };
+    // This lane's key position in tile jt for the visibility test (cache
+    // tiles read it from LDS; INT_MAX past the valid keys).
+    auto lane_key_pos = [&](int jt, const int* sPt) {
+        const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
+        if (!tr.cache) return lane < tr.valid ? a.P + tr.first + lane : INT_MAX;
+        return lane < tr.valid ? sPt[lane] : INT_MAX;
+    };
+    // Positional mask of tile jt (tiles not visible to every row of the wave).
+    auto apply_mask = [&](f32x16 (&sv)[2], const int* sPt, int jt) {
+        const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
+        const int base_pos = a.P + tr.first;
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int k0 = sub * 32 + 16 * s2 + 8 * hh;
-                    const i32x4 p0 = *reinterpret_cast<const i32x4*>(&sPos[k0]);
-                    const i32x4 p1 = *reinterpret_cast<const i32x4*>(&sPos[k0 + 4]);
+        for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int kpv = e < 4 ? p0[e] : p1[e - 4];
-                        if (!(kpv >= 0 && kpv <= qpos)) s[sub][8 * s2 + e] = -INFINITY;
-                    }
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int k0 = sub * 32 + 16 * s2 + 8 * hh;
+                i32x4 p0, p1;
+                if (tr.cache) {
+                    p0 = *reinterpret_cast<const i32x4*>(&sPt[k0]);
+                    p1 = *reinterpret_cast<const i32x4*>(&sPt[k0 + 4]);
+                } else {
+                    p0 = i32x4{base_pos + k0, base_pos + k0 + 1, base_pos + k0 + 2,
+                               base_pos + k0 + 3};
+                    p1 = p0 + 4;
                 }
-        }
-        float mt = s[0][0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(s[0][r], s[1][r]));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+                for (int e = 0; e < 8; ++e) {
+                    const int kpv = e < 4 ? p0[e] : p1[e - 4];
+                    if (!(k0 + e < tr.valid && kpv >= 0 && kpv <= qpos))
+                        sv[sub][8 * s2 + e] = -INFINITY;
+                }
+            }
+    };
+    // Row max over both lane halves, running-max update and (rarely) the
+    // rescale of O and l; returns m_run * c for the exponentials.
+    auto rescale_for = [&](float mt) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt),
+                                                         __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         const float m_new = fmaxf(m_run, mt);
         const bool need = m_new > m_run + tau_raw;
         if (__any(need)) {
@@ -268,65 +302,154 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
             m_run = m_next;
         }
-        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        bf16x8 pb[2][2];
-        float lsum = 0.f;
+        return (m_run == -INFINITY) ? 0.f : m_run * c;
+    };
+    auto rowmax = [&](const f32x16 (&sv)[2]) {
+        float m4[4] = {sv[0][0], sv[0][1], sv[0][2], sv[0][3]};
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                float p[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    p[e] = fast_exp2(fmaf(s[sub][8 * s2 + e], c, -mc));
-                    lsum += p[e];
-                }
-                u32x4 w = {pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]),
-                           pack2(p[6], p[7])};
-                pb[sub][s2] = as_bf16x8(w);
-            }
-        l_run += lsum;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const u16* vp = &sVt[(dt * 32 + lq) * VROW + 8 * hh];
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    o[dt] = mfma32(as_bf16x8(ld16(vp + sub * 32 + 16 * s2)), pb[sub][s2], o[dt]);
-        }
+        for (int idx = 4; idx < 32; ++idx) m4[idx & 3] = fmaxf(m4[idx & 3], sv[idx >> 4][idx & 15]);
+        return fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     };
 
-    // Half kh owns tiles kh, kh+2, kh+4, ...; both halves step together.
-    // Unconditional prologue (a half with no tile stages tile 0 and never reads
-    // it), so every path has waited for the Q loads before the loop.
-    gload(min(kh, ntiles - 1));
-    lstore(0);
-    __syncthreads();
-    for (int st = 0; st < steps; ++st) {
-        const int cur = st & 1;
-        const int my_tile = 2 * st + kh, next_tile = my_tile + 2;
-        if (next_tile < ntiles) gload(next_tile);
-        if (my_tile < ntiles) compute(cur);
-        if (next_tile < ntiles) lstore(cur ^ 1);
-        __syncthreads();
+    // O^T += V^T P^T for the tile in sVt, operands read two MFMAs ahead,
+    // interleaved with the running max of the next tile's scores (sn).
+    auto pv_max = [&](const u16* sVt, const bf16x8 (&pb)[2][2], const f32x16 (&sn)[2]) {
+        const unsigned char* base = reinterpret_cast<const unsigned char*>(sVt);
+        auto vread = [&](int x) {
+            const int dt = x % DT, s2 = (x / DT) & 1, sub = x / (2 * DT);
+            return ld_vt(base + (vb ^ (64 * dt)) + (sub * 32 + 16 * s2) * RB, 4 * RB);
+        };
+        constexpr int NX = 4 * DT;
+        constexpr int AHEAD = 2;
+        constexpr int MPER = 32 / NX;             // maxima per MFMA
+        float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        bf16x8 va[AHEAD + 1];
+#pragma unroll
+        for (int x = 0; x < AHEAD; ++x) va[x] = vread(x);
+#pragma unroll
+        for (int x = 0; x < NX; ++x) {
+            if (x + AHEAD < NX) va[(x + AHEAD) % (AHEAD + 1)] = vread(x + AHEAD);
+            const int dt = x % DT, s2 = (x / DT) & 1, sub = x / (2 * DT);
+            o[dt] = mfma32(va[x % (AHEAD + 1)], pb[sub][s2], o[dt]);
+#pragma unroll
+            for (int e = 0; e < MPER; ++e) {
+                const int idx = x * MPER + e;
+                m4[idx & 3] = fmaxf(m4[idx & 3], sn[idx >> 4][idx & 15]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    };
+
+    // Prologue: K(0) (+ positions), V(0), K(1) of this half; S(0), its mask,
+    // max and exponent offset.  Positions travel with K: stage s holds K and
+    // positions of tiles s, s+2, ...; V has its own two stages.
+    f32x16 sA[2], sB[2];
+    float mc = 0.f;
+    if (mine > 0) {
+        issue_kp(sK0[kh], sP0[kh], 0);
+        issue_v(sV0[kh], 0);
+    }
+    if (mine > 1) issue_kp(sK1[kh], sP1[kh], 1);
+    publish_lds_loads();
+    if (mine > 0) {
+        qk(sK0[kh], sA);
+        if (!__all(lane_key_pos(0, sP0[kh]) <= qpos_wave_min &&
+                   lane_key_pos(0, sP0[kh]) >= 0))
+            apply_mask(sA, sP0[kh], 0);
+        mc = rescale_for(rowmax(sA));
     }
 
-    // Merge the two halves' (m, l, O) for each row (all LDS tile reads are done).
-    constexpr int MF = L::MERGE_FLOATS;
-    float* mb = reinterpret_cast<float*>(smem) + rw * MF * 64;
+    // Iteration jt: S(jt) is masked and mc is its exponent offset; K stage
+    // jt&1 is free (K(jt) was consumed), K stage (jt+1)&1 holds K(jt+1), V
+    // stage jt&1 holds V(jt).
+    auto iter = [&](auto odd_c, int jt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+        constexpr bool odd = decltype(odd_c)::value;
+        u16* kfree = odd ? sK1[kh] : sK0[kh];
+        int* pfree = odd ? sP1[kh] : sP0[kh];
+        const u16* knext = odd ? sK0[kh] : sK1[kh];
+        const int* pnext = odd ? sP0[kh] : sP1[kh];
+        const u16* vcur = odd ? sV1[kh] : sV0[kh];
+        u16* vnext = odd ? sV0[kh] : sV1[kh];
+        if (jt + 2 < mine) issue_kp(kfree, pfree, jt + 2);
+        if (jt + 1 < mine) issue_v(vnext, jt + 1);
+        if (jt < mine) {
+            const bool has_next = jt + 1 < mine;
+            const int kp_next = has_next ? lane_key_pos(jt + 1, pnext) : 0;
+            bf16x8 pb[2][2];
+            float lsum = 0.f;
+            // Phase A: QK^T of the next tile interleaved with this tile's
+            // exponentials, in source order (each k-step: read the next K
+            // fragments, two MFMAs, a slice of the exponentials).  On the
+            // half's last tile the next buffer holds stale data (in bounds)
+            // and the result is unused.
+            const unsigned char* kbase = reinterpret_cast<const unsigned char*>(knext);
+            auto kread = [&](int ks, int sub) {
+                return as_bf16x8(ld16(kbase + ((kb ^ (32 * ks)) + sub * 32 * RB)));
+            };
+            constexpr int PER = 32 / KS;          // exponentials per k-step
+            bf16x8 kr[2][2];
+            kr[0][0] = kread(0, 0);
+            kr[0][1] = kread(0, 1);
+            snext[0] = f32x16{};
+            snext[1] = f32x16{};
+            float p[8];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS) {
+                    kr[(ks + 1) & 1][0] = kread(ks + 1, 0);
+                    kr[(ks + 1) & 1][1] = kread(ks + 1, 1);
+                }
+                snext[0] = mfma32(kr[ks & 1][0], qf[ks], snext[0]);
+                snext[1] = mfma32(kr[ks & 1][1], qf[ks], snext[1]);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) {
+                    const int idx = ks * PER + e, q4 = idx >> 3, ee = idx & 7;
+                    p[ee] = fast_exp2(fmaf(scur[q4 >> 1][8 * (q4 & 1) + ee], c, -mc));
+                    lsum += p[ee];
+                }
+                if (((ks + 1) * PER) % 8 == 0) {
+                    const int q4 = (ks * PER) >> 3;
+                    pb[q4 >> 1][q4 & 1] =
+                        as_bf16x8(u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]),
+                                        pack2(p[4], p[5]), pack2(p[6], p[7])});
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            l_run += lsum;
+            // The next tile's mask (rare: partial or diagonal tiles).
+            if (has_next && !__all(kp_next >= 0 && kp_next <= qpos_wave_min))
+                apply_mask(snext, pnext, jt + 1);
+            // Phase B: P V of this tile with the next tile's row max.
+            const float mt = pv_max(vcur, pb, snext);
+            if (has_next) mc = rescale_for(mt);
+        }
+        publish_lds_loads();
+    };
+    for (int jt = 0; jt < steps; jt += 2) {
+        iter(std::false_type{}, jt, sA, sB);
+        if (jt + 1 < steps) iter(std::true_type{}, jt + 1, sB, sA);
+    }
+
+    // Merge the two halves' (m, l, O) for each row; the tile buffers are free
+    // (the loop ended on a barrier with no loads in flight).
+    auto mo = [&](int dt, int r) -> float& {
+        float* reg = reinterpret_cast<float*>(dt < DT / 2 ? &sK0[0][0] : &sK1[0][0]);
+        return reg[((rw * (DT / 2) + dt % (DT / 2)) * 16 + r) * 64 + lane];
+    };
+    float* ml = reinterpret_cast<float*>(&sV0[0][0]) + rw * 128;
     if (kh == 1) {
-        mb[lane] = m_run;
-        mb[64 + lane] = l_run;
+        ml[lane] = m_run;
+        ml[64 + lane] = l_run;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mb[(2 + dt * 16 + r) * 64 + lane] = o[dt][r];
+            for (int r = 0; r < 16; ++r) mo(dt, r) = o[dt][r];
     }
     __syncthreads();
     if (kh == 1) return;
     {
-        const float m1 = mb[lane], l1 = mb[64 + lane];
+        const float m1 = ml[lane], l1 = ml[64 + lane];
         const float m = fmaxf(m_run, m1);
         const float a0 = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m) * c);
         const float a1 = m1 == -INFINITY ? 0.f : fast_exp2((m1 - m) * c);
@@ -334,8 +457,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                o[dt][r] = o[dt][r] * a0 + mb[(2 + dt * 16 + r) * 64 + lane] * a1;
+            for (int r = 0; r < 16; ++r) o[dt][r] = o[dt][r] * a0 + mo(dt, r) * a1;
         m_run = m;
     }
 
@@ -600,22 +722,9 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
 
 template <int D>
 hipError_t launch_attn_d(const ChunkArgs& a, hipStream_t s) {
-    // More than 64 KB of LDS per workgroup must be requested explicitly, once per device.
-    static unsigned configured = 0;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    const unsigned bit = 1u << (dev & 31);
-    if (!(configured & bit)) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel<D>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, AttnSmem<D>::BYTES);
-        if (e != hipSuccess) return e;
-        configured |= bit;
-    }
     const int R = a.G * a.S;
     const int total = ((R + kRowsPerBlock - 1) / kRowsPerBlock) * a.B * a.Hkv;
-    hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(xcd_grid(total)), dim3(kAttnThreads),
-                       AttnSmem<D>::BYTES, s, a);
+    hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(xcd_grid(total)), dim3(kAttnThreads), 0, s, a);
     return hipGetLastError();
 }
 
