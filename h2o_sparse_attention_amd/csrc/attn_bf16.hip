@@ -123,9 +123,6 @@ __device__ __forceinline__ void publish_lds_loads() {
 __device__ __forceinline__ void load_lds16(Rsrc r, void* lds, int voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
-__device__ __forceinline__ void load_lds4(Rsrc r, void* lds, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
-}
 // Eight bf16 of the V^T operand: two transposing reads, four rows apart.
 __device__ __forceinline__ bf16x8 ld_vt(const unsigned char* p, int row_bytes4) {
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
@@ -140,15 +137,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     constexpr int KS = D / 16;                    // MFMA k-steps over head_dim
     constexpr int DT = D / 32;                    // 32-row tiles of O^T
     constexpr int RB = T::RB;
-    // Stage s of half h: sK<s>[h], sV<s>[h], sP<s>[h] (positions of cache keys).
+    // Stage s of half h: sK<s>[h], sV<s>[h].
     // Separate objects per stage let the compiler see that loads into one stage
     // never alias reads of the other.
     __shared__ __attribute__((aligned(1024))) u16 sK0[2][T::U16];
     __shared__ __attribute__((aligned(1024))) u16 sK1[2][T::U16];
     __shared__ __attribute__((aligned(1024))) u16 sV0[2][T::U16];
     __shared__ __attribute__((aligned(1024))) u16 sV1[2][T::U16];
-    __shared__ __attribute__((aligned(16))) int sP0[2][kKeysPerTile];
-    __shared__ __attribute__((aligned(16))) int sP1[2][kKeysPerTile];
 
     const int R = a.G * a.S;
     const int nrb = (R + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -169,7 +164,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     const bool row_ok = row < R;
     const int i = row_ok ? row / a.G : a.S - 1;
     const int h = g * a.G + (row_ok ? row % a.G : 0);
-    const int qpos = a.P + i;
 
     const u16* Q = static_cast<const u16*>(a.q);
     const size_t qoff = ((size_t)(b * a.Hq + h) * a.S + i) * D;
@@ -194,7 +188,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     const u16* Vc = static_cast<const u16*>(a.vc) + (size_t)bg * a.NC * D;
     const u16* Kn = static_cast<const u16*>(a.kn) + (size_t)bg * S * D;
     const u16* Vn = static_cast<const u16*>(a.vn) + (size_t)bg * S * D;
-    const int32_t* posg = a.pos + (size_t)bg * a.NC;
 
     // Global byte offset (within a tile) of this lane's 16-byte load `it`:
     // LDS chunk cp of row r is filled from global chunk cp ^ swz(r).
@@ -203,17 +196,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
         const int r = off / RB, cp = (off % RB) / 16;
         return r * RB + 16 * (cp ^ (is_v ? swz_v<D>(r) : swz_k<D>(r)));
     };
-    // K and the key positions of tile jt (positions only for cache tiles).
-    auto issue_kp = [&](u16* dst, int* pdst, int jt) {
+    auto issue_k = [&](u16* dst, int jt) {
         const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
         const Rsrc rk = make_rsrc(tr.k, tr.valid * RB);
         unsigned char* d = reinterpret_cast<unsigned char*>(dst) + rw * 1024;
 #pragma unroll
         for (int it = 0; it < T::LOADS; ++it) load_lds16(rk, d + it * 4096, goff(it, false));
-        if (tr.cache && rw == 0) {
-            const Rsrc rp = make_rsrc(posg + tr.first, tr.valid * 4);
-            load_lds4(rp, pdst, lane * 4);
-        }
     };
     auto issue_v = [&](u16* dst, int jt) {
         const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
@@ -251,38 +239,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
                 sd[sub] = mfma32(as_bf16x8(ld16(base + ((kb ^ (32 * ks)) + sub * 32 * RB))),
                                  qf[ks], sd[sub]);
     };
-    // This lane's key position in tile jt for the visibility test (cache
-    // tiles read it from LDS; INT_MAX past the valid keys).
-    auto lane_key_pos = [&](int jt, const int* sPt) {
+    // Visibility.  Filled cache slots hold positions below P (the cache only
+    // ever receives earlier tokens), so a cache key is visible to every row of
+    // the chunk and chunk key i' to row i iff i' <= i: within tile jt, key k is
+    // visible to this lane's row iff k <= lim(jt).  Tiles whose keys are all
+    // visible to every row of the wave skip the mask.
+    auto tile_lim = [&](int jt) {
         const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
-        if (!tr.cache) return lane < tr.valid ? a.P + tr.first + lane : INT_MAX;
-        return lane < tr.valid ? sPt[lane] : INT_MAX;
+        return tr.cache ? tr.valid - 1 : min(tr.valid - 1, i - tr.first);
     };
-    // Positional mask of tile jt (tiles not visible to every row of the wave).
-    auto apply_mask = [&](f32x16 (&sv)[2], const int* sPt, int jt) {
+    auto tile_all_visible = [&](int jt) {
         const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
-        const int base_pos = a.P + tr.first;
+        return tr.valid == kKeysPerTile &&
+               (tr.cache || tr.first + kKeysPerTile - 1 <= qpos_wave_min - a.P);
+    };
+    // -inf for this lane's keys k > lim (the lane holds keys
+    // 32*sub + 16*(r/8) + 8*hh + r%8 of the tile).
+    auto apply_mask = [&](f32x16 (&sv)[2], int lim) {
+        const int d = lim - 8 * hh;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int k0 = sub * 32 + 16 * s2 + 8 * hh;
-                i32x4 p0, p1;
-                if (tr.cache) {
-                    p0 = *reinterpret_cast<const i32x4*>(&sPt[k0]);
-                    p1 = *reinterpret_cast<const i32x4*>(&sPt[k0 + 4]);
-                } else {
-                    p0 = i32x4{base_pos + k0, base_pos + k0 + 1, base_pos + k0 + 2,
-                               base_pos + k0 + 3};
-                    p1 = p0 + 4;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int kpv = e < 4 ? p0[e] : p1[e - 4];
-                    if (!(k0 + e < tr.valid && kpv >= 0 && kpv <= qpos))
-                        sv[sub][8 * s2 + e] = -INFINITY;
-                }
-            }
+            for (int r = 0; r < 16; ++r)
+                if (sub * 32 + 16 * (r >> 3) + (r & 7) > d) sv[sub][r] = -INFINITY;
     };
     // Row max over both lane halves, running-max update and (rarely) the
     // rescale of O and l; returns m_run * c for the exponentials.
@@ -341,22 +320,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
         return fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
     };
 
-    // Prologue: K(0) (+ positions), V(0), K(1) of this half; S(0), its mask,
-    // max and exponent offset.  Positions travel with K: stage s holds K and
-    // positions of tiles s, s+2, ...; V has its own two stages.
+    // Prologue: K(0), V(0), K(1) of this half; S(0), its mask, max and
+    // exponent offset.
     f32x16 sA[2], sB[2];
     float mc = 0.f;
     if (mine > 0) {
-        issue_kp(sK0[kh], sP0[kh], 0);
+        issue_k(sK0[kh], 0);
         issue_v(sV0[kh], 0);
     }
-    if (mine > 1) issue_kp(sK1[kh], sP1[kh], 1);
+    if (mine > 1) issue_k(sK1[kh], 1);
     publish_lds_loads();
     if (mine > 0) {
         qk(sK0[kh], sA);
-        if (!__all(lane_key_pos(0, sP0[kh]) <= qpos_wave_min &&
-                   lane_key_pos(0, sP0[kh]) >= 0))
-            apply_mask(sA, sP0[kh], 0);
+        if (!tile_all_visible(0)) apply_mask(sA, tile_lim(0));
         mc = rescale_for(rowmax(sA));
     }
 
@@ -366,16 +342,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     auto iter = [&](auto odd_c, int jt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
         constexpr bool odd = decltype(odd_c)::value;
         u16* kfree = odd ? sK1[kh] : sK0[kh];
-        int* pfree = odd ? sP1[kh] : sP0[kh];
         const u16* knext = odd ? sK0[kh] : sK1[kh];
-        const int* pnext = odd ? sP0[kh] : sP1[kh];
         const u16* vcur = odd ? sV1[kh] : sV0[kh];
         u16* vnext = odd ? sV0[kh] : sV1[kh];
-        if (jt + 2 < mine) issue_kp(kfree, pfree, jt + 2);
+        if (jt + 2 < mine) issue_k(kfree, jt + 2);
         if (jt + 1 < mine) issue_v(vnext, jt + 1);
         if (jt < mine) {
             const bool has_next = jt + 1 < mine;
-            const int kp_next = has_next ? lane_key_pos(jt + 1, pnext) : 0;
             bf16x8 pb[2][2];
             float lsum = 0.f;
             // Phase A: QK^T of the next tile interleaved with this tile's
@@ -416,12 +389,18 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // Keep the exponentials here: their only uses come after a branch
+            // and would otherwise be sunk past it, out of the MFMA stream.
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                asm volatile("" : : "v"(__builtin_bit_cast(u32x4, pb[q4 >> 1][q4 & 1])));
+            asm volatile("" : : "v"(lsum));
             l_run += lsum;
             // The next tile's mask (rare: partial or diagonal tiles).
-            if (has_next && !__all(kp_next >= 0 && kp_next <= qpos_wave_min))
-                apply_mask(snext, pnext, jt + 1);
+            if (has_next && !tile_all_visible(jt + 1)) apply_mask(snext, tile_lim(jt + 1));
             // Phase B: P V of this tile with the next tile's row max.
             const float mt = pv_max(vcur, pb, snext);
+            asm volatile("" : : "v"(mt));         // keep the maxima under the MFMAs
             if (has_next) mc = rescale_for(mt);
         }
         publish_lds_loads();

@@ -100,7 +100,11 @@ H2O_API size_t h2o_workspace_bytes(const h2o_dims_t *dims, int32_t chunk_len);
  * Chunk attention with summed weights ("Kernel Support Needs").
  * Query row i (0 <= i < S) sits at position P + i, P = chunk_start.  Keys are
  * the filled slots j < n_valid and the chunk's own keys (position P + i').  Key
- * j is visible to row i iff 0 <= t(j) <= P + i.  For every query head h:
+ * j is visible to row i iff 0 <= t(j) <= P + i.  Precondition: every filled
+ * slot holds a position in [0, P) (the cache only ever receives earlier
+ * tokens, which h2o_evict_and_insert maintains), so every filled slot is
+ * visible to every row and chunk key i' to rows i >= i'.  For every query
+ * head h:
  *   out[b,h,i]  = sum_j softmax_j(sm_scale * q.k_j) v_j     (over visible keys)
  *   lse[b,h,i]  = log sum_j exp(sm_scale * q.k_j)
  * and for every KV head g, summing over its query heads and the S rows:
