@@ -120,8 +120,11 @@ __device__ __forceinline__ void publish_lds_loads() {
     __syncthreads();
 }
 
-__device__ __forceinline__ void load_lds16(Rsrc r, void* lds, int voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+__device__ __forceinline__ void load_lds16(Rsrc r, void* lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(Rsrc r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
 }
 // Eight bf16 of the V^T operand: two transposing reads, four rows apart.
 __device__ __forceinline__ bf16x8 ld_vt(const unsigned char* p, int row_bytes4) {
@@ -201,14 +204,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
         const Rsrc rk = make_rsrc(tr.k, tr.valid * RB);
         unsigned char* d = reinterpret_cast<unsigned char*>(dst) + rw * 1024;
 #pragma unroll
-        for (int it = 0; it < T::LOADS; ++it) load_lds16(rk, d + it * 4096, goff(it, false));
+        for (int it = 0; it < T::LOADS; ++it) load_lds16(rk, d + it * 4096, goff(it, false), 0);
     };
     auto issue_v = [&](u16* dst, int jt) {
         const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
         const Rsrc rv = make_rsrc(tr.v, tr.valid * RB);
         unsigned char* d = reinterpret_cast<unsigned char*>(dst) + rw * 1024;
 #pragma unroll
-        for (int it = 0; it < T::LOADS; ++it) load_lds16(rv, d + it * 4096, goff(it, true));
+        for (int it = 0; it < T::LOADS; ++it) load_lds16(rv, d + it * 4096, goff(it, true), 0);
     };
 
     // Operand offsets: K row perm_key(lq) (+32 per sub-tile), k-step ks at
@@ -460,24 +463,34 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Colsum pass: for 128 keys of one (b, kv head), sum exp(s - lse) over every
-// query row of the group (G heads x S positions).  K stays in registers; Q
-// and LSE tiles stream through double-buffered LDS.  Each lane accumulates its
-// 16 keys over its query column, and the 32 columns are added in a fixed
-// order at the end, so the result is deterministic (no atomics).  Key blocks
-// follow the same cache / chunk split as the attention tiles.
+// query row of the group (G heads x S positions).  K stays in registers; Q and
+// LSE tiles of 64 packed rows (row r = i*G + head) go from global memory
+// straight into double-buffered LDS, Q rows XOR-swizzled like the attention
+// pass's K.  Each lane accumulates its 16 keys over its query column, and the
+// 32 columns are added in a fixed order at the end, so the result is
+// deterministic (no atomics).  Key blocks follow the same cache / chunk split
+// as the attention tiles.  Filled cache slots precede the chunk, so cache keys
+// are visible to every row; a chunk key is visible to the rows at or after its
+// own position, which only blocks near the diagonal have to test.
+//
+// Pipeline, per row tile rt (stage buffer (rt - tile0) & 1):
+//   A: MFMAs of sub-tile 1 of tile rt, exponentials of sub-tile 0 of tile rt;
+//   barrier (tile rt+1 has landed; tile rt's buffer is free);
+//   B: start the loads of tile rt+2; MFMAs of sub-tile 0 of tile rt+1,
+//      exponentials of sub-tile 1 of tile rt.
 // ---------------------------------------------------------------------------
 template <int D, bool EVEN_ROWS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
     constexpr int KS = D / 16;
-    constexpr int QROW = D + 8;
-    constexpr int QCH = D / 8;
-    constexpr int Q_LD = kRowsPerTile * QCH / kThreads;
-    constexpr int QBUF = kRowsPerTile * QROW;      // u16 per Q buffer
-    static_assert(Q_LD >= 1, "tile shape");
-
-    __shared__ __attribute__((aligned(16))) u16 sQ[2][QBUF];
-    __shared__ float sL[2][kRowsPerTile];
+    constexpr int RB = 2 * D;                          // bytes per Q row
+    constexpr int QT = kRowsPerTile * RB;              // bytes per Q tile
+    constexpr int QLOADS = QT / 1024 / kWaves;         // 1 KB loads per wave per tile
+    static_assert(QLOADS >= 1, "tile shape");
+    __shared__ __attribute__((aligned(1024))) unsigned char sQ0[QT];
+    __shared__ __attribute__((aligned(1024))) unsigned char sQ1[QT];
+    __shared__ __attribute__((aligned(16))) float sL0[kRowsPerTile];
+    __shared__ __attribute__((aligned(16))) float sL1[kRowsPerTile];
     __shared__ float sRed[kWaves][32][33];
 
     const int n = a.n, S = a.S, G = a.G;
@@ -493,17 +506,13 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
     const int limit = is_cache ? n : S;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lq = lane & 31, hh = lane >> 5;
-    const int first = block_first + wave * 32;    // this wave's first key in its source
+    const int first = block_first + wave * 32;         // this wave's first key in its source
 
     const u16* Ksrc = is_cache ? static_cast<const u16*>(a.kc) + (size_t)bg * a.NC * D
                                : static_cast<const u16*>(a.kn) + (size_t)bg * S * D;
-    const int32_t* posg = a.pos + (size_t)bg * a.NC;
-    auto key_pos = [&](int idx) -> int {
-        return idx < limit ? (is_cache ? posg[idx] : a.P + idx) : INT_MAX;
-    };
-
     bf16x8 kf[KS];
     {
         const int idx = first + lq;
@@ -513,12 +522,6 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
             if (idx < limit) v = ld16(Ksrc + (size_t)idx * D + 16 * ks + 8 * hh);
             kf[ks] = as_bf16x8(v);
         }
-    }
-    int kmin = key_pos(first + lq), kmax = kmin;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        kmin = min(kmin, __shfl_xor(kmin, off));
-        kmax = max(kmax, __shfl_xor(kmax, off));
     }
 
     const int R = G * S;
@@ -530,69 +533,59 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
     const u16* Qg = static_cast<const u16*>(a.q) + (size_t)(b * a.Hq + g * G) * S * D;
     const float* Lg = a.lse + (size_t)(b * a.Hq + g * G) * S;
     const int q_bytes = G * S * D * 2;
-    u32x4 qreg[Q_LD];
-    uint32_t lraw = 0u;          // LSE bits as loaded; scaled and masked in lstore
-    bool lvalid = false;
-    // When G divides the tile height every tile holds 64/G positions of all G
-    // heads, so a lane's offset inside the tile is loop-invariant.
-    // EVEN_ROWS: G divides the tile height (checked by the launcher).
-    constexpr bool even_rows = EVEN_ROWS;
-    const int pos_per_tile = even_rows ? kRowsPerTile / G : 0;
-    int qoff[Q_LD];
-    int l_il = 0, l_off = 0;
-#pragma unroll
-    for (int it = 0; it < Q_LD; ++it) {
-        const int cidx = tid + it * kThreads;
-        const int rloc = cidx / QCH, col = (cidx % QCH) * 8;
-        qoff[it] = even_rows ? (((rloc % G) * S + rloc / G) * D + col) * 2 : col * 2;
-    }
-    if (even_rows && tid < kRowsPerTile) {
-        l_il = tid / G;
-        l_off = ((tid % G) * S + l_il) * 4;
-    }
-    auto row_split = [&](int r, int& hh_, int& ipos) {
+    // Packed row r of the group -> byte offset of its Q row / LSE entry, or
+    // past the end for r >= R (the loads then return zeros).
+    auto row_split = [&](int r, int& hl, int& ipos) {
         ipos = G == 1 ? r : (int)__umulhi((uint32_t)r, g_magic);
-        hh_ = r - ipos * G;
+        hl = r - ipos * G;
     };
-    auto gload = [&](int rt) {
-        if constexpr (even_rows) {
-            const int p0 = rt * pos_per_tile;                 // first position of the tile
-            const Rsrc rq = make_rsrc(Qg + (size_t)p0 * D, q_bytes - p0 * D * 2);
+    // This lane's 16-byte Q loads: load `it` fills LDS bytes
+    // (it*4 + wave)*1024 + 16*lane = row rl, chunk cp, from global chunk
+    // cp ^ swz(rl) of that row.
+    const int rl_base = (wave * 1024 + 16 * lane) / RB;
+    const int cp = (16 * lane % RB) / 16;
+    constexpr int ROWS_PER_LOAD = 4096 / RB;           // rows between loads it and it+1
+    int qoff[QLOADS];
 #pragma unroll
-            for (int it = 0; it < Q_LD; ++it) qreg[it] = bload16(rq, qoff[it]);
-            if (tid < kRowsPerTile) {
-                const Rsrc rl = make_rsrc(Lg + p0, (G * S - p0) * 4);
-                lraw = bload4(rl, l_off);
-                lvalid = p0 + l_il < S;
-            }
+    for (int it = 0; it < QLOADS; ++it) {
+        const int rl = rl_base + it * ROWS_PER_LOAD;
+        const int sw = D == 128 ? (rl & 15) : ((rl >> 1) & 7);
+        int hl = 0, il = 0;
+        if (EVEN_ROWS) {
+            hl = rl % G;
+            il = rl / G;
+        }
+        qoff[it] = ((hl * S + il) * D) * 2 + 16 * (cp ^ sw);
+    }
+    const int ppt = EVEN_ROWS ? kRowsPerTile / G : 0;  // positions per tile (EVEN_ROWS)
+    auto issue = [&](unsigned char* dq, float* dl, int rt) {
+        if (EVEN_ROWS) {
+            const int p0 = rt * ppt;
+            const Rsrc rq = make_rsrc(Qg + (size_t)p0 * D, max(0, q_bytes - p0 * D * 2));
+            unsigned char* d = dq + wave * 1024;
+#pragma unroll
+            for (int it = 0; it < QLOADS; ++it) load_lds16(rq, d + it * 4096, qoff[it], 0);
         } else {
             const Rsrc rq = make_rsrc(Qg, q_bytes);
+            unsigned char* d = dq + wave * 1024;
 #pragma unroll
-            for (int it = 0; it < Q_LD; ++it) {
-                const int cidx = tid + it * kThreads;
-                const int r = rt * kRowsPerTile + cidx / QCH;
-                int hh_ = 0, ipos = 0;
-                row_split(min(r, R - 1), hh_, ipos);
-                const int off = r < R ? ((hh_ * S + ipos) * D) * 2 + qoff[it] : q_bytes;
-                qreg[it] = bload16(rq, off);
-            }
-            if (tid < kRowsPerTile) {
-                const int r = rt * kRowsPerTile + tid;
-                int hh_ = 0, ipos = 0;
-                row_split(min(r, R - 1), hh_, ipos);
-                lraw = __float_as_uint(Lg[hh_ * S + ipos]);
-                lvalid = r < R;
+            for (int it = 0; it < QLOADS; ++it) {
+                const int r = rt * kRowsPerTile + rl_base + it * ROWS_PER_LOAD;
+                const int rl = rl_base + it * ROWS_PER_LOAD;
+                const int sw = D == 128 ? (rl & 15) : ((rl >> 1) & 7);
+                int hl = 0, ipos = 0;
+                row_split(min(r, R - 1), hl, ipos);
+                const int off = r < R ? ((hl * S + ipos) * D) * 2 + 16 * (cp ^ sw) : q_bytes;
+                load_lds16(rq, d + it * 4096, off, 0);
             }
         }
-    };
-    auto lstore = [&](int which) {
-#pragma unroll
-        for (int it = 0; it < Q_LD; ++it) {
-            const int cidx = tid + it * kThreads;
-            *reinterpret_cast<u32x4*>(&sQ[which][(cidx / QCH) * QROW + (cidx % QCH) * 8]) =
-                qreg[it];
+        if (wave == 0) {
+            const int r = rt * kRowsPerTile + lane;
+            int hl = 0, ipos = 0;
+            row_split(min(r, R - 1), hl, ipos);
+            const Rsrc rl = make_rsrc(Lg, G * S * 4);
+            load_lds4(rl, dl, r < R ? (hl * S + ipos) * 4 : G * S * 4);
         }
-        if (tid < kRowsPerTile) sL[which][tid] = lvalid ? __uint_as_float(lraw) * kLog2e : INFINITY;
     };
 
     const float c = a.sm_scale * kLog2e;
@@ -600,87 +593,101 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-    // S^T (this wave's 32 keys x 32 query rows of sub-tile `sub`) from buffer `buf`.
-    auto mma = [&](int buf, int sub) {
-        f32x16 r = f32x16{};
-        const u16* qp = &sQ[buf][(sub * 32 + lq) * QROW + 8 * hh];
+    // Q operand of query row lq of sub-tile `sub`, k-step ks: chunk 2*ks + hh
+    // of that row, swizzled.
+    const int qb = lq * RB + 16 * (hh ^ (D == 128 ? (lq & 15) : ((lq >> 1) & 7)));
+    auto qread = [&](const unsigned char* sQt, int sub, int ks) {
+        return as_bf16x8(ld16(sQt + ((qb ^ (32 * ks)) + sub * 32 * RB)));
+    };
+    // log2-scaled LSE of this lane's query row (+inf past the last row, which
+    // makes its weights zero).
+    auto lse2_of = [&](const float* sLt, int rt, int sub) {
+        const int r = rt * kRowsPerTile + sub * 32 + lq;
+        return r < R ? sLt[sub * 32 + lq] * kLog2e : INFINITY;
+    };
+    // Chunk key blocks near the diagonal: is every key of this wave visible
+    // to every row of sub-tile (rt, sub)?
+    const int kmax = min(first + 31, limit - 1);       // largest key index of the wave
+    auto full_tile = [&](int rt, int sub) {
+        if (is_cache) return true;
+        const int r0 = min(rt * kRowsPerTile + sub * 32, R - 1);
+        const int i0 = G == 1 ? r0 : (int)__umulhi((uint32_t)r0, g_magic);
+        return kmax <= i0;
+    };
+    // Exponentials of sub-tile values sv (lse2 of this lane's row) into acc,
+    // with the causal test when the tile is not fully visible.
+    auto exp_masked = [&](const f32x16& sv, float lse2, int rt, int sub) {
+        const int r = min(rt * kRowsPerTile + sub * 32 + lq, R - 1);
+        const int ipos = G == 1 ? r : (int)__umulhi((uint32_t)r, g_magic);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) r = mfma32(kf[ks], as_bf16x8(ld16(qp + 16 * ks)), r);
+        for (int e = 0; e < 16; ++e) {
+            const int key = first + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const float p = fast_exp2(fmaf(sv[e], c, -lse2));
+            acc[e] += key <= ipos ? p : 0.f;
+        }
+    };
+
+    // One stage: 8 MFMAs of (sQm, subm) into the result, interleaved with the
+    // exponentials of sv (fully visible) or followed by the masked form.
+    auto stage = [&](const unsigned char* sQm, int subm, const f32x16& sv, float lse2,
+                     bool full, int rt_e, int sub_e, bool do_mfma) {
+        f32x16 r = f32x16{};
+        if (full) {
+            bf16x8 qr[2];
+            if (do_mfma) qr[0] = qread(sQm, subm, 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (do_mfma) {
+                    if (ks + 1 < KS) qr[(ks + 1) & 1] = qread(sQm, subm, ks + 1);
+                    r = mfma32(kf[ks], qr[ks & 1], r);
+                }
+#pragma unroll
+                for (int e = 0; e < 16 / KS; ++e) {
+                    const int x = ks * (16 / KS) + e;
+                    acc[x] += fast_exp2(fmaf(sv[x], c, -lse2));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            if (do_mfma) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) r = mfma32(kf[ks], qread(sQm, subm, ks), r);
+            }
+            exp_masked(sv, lse2, rt_e, sub_e);
+        }
         return r;
     };
-    auto first_pos = [&](int rt, int sub) {
-        const int rf = min(rt * kRowsPerTile + sub * 32, R - 1);
-        return a.P + (G == 1 ? rf : (int)__umulhi((uint32_t)rf, g_magic));
-    };
-    auto lane_pos = [&](int rt, int sub) {
-        const int rq = min(rt * kRowsPerTile + sub * 32 + lq, R - 1);
-        return a.P + (G == 1 ? rq : (int)__umulhi((uint32_t)rq, g_magic));
-    };
-    auto exp_full = [&](const f32x16& sv, float lse2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += fast_exp2(fmaf(sv[r], c, -lse2));
-    };
-    // Masked tiles (chunk keys near the diagonal, or empty-slot markers) re-read
-    // the positions of this lane's 16 keys instead of keeping them live.
-    auto exp_masked = [&](const f32x16& sv, float lse2, int qpos) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kp = key_pos(first + 8 * (r >> 2) + 4 * hh + (r & 3));
-            const float p = fast_exp2(fmaf(sv[r], c, -lse2));
-            acc[r] += (kp >= 0 && kp <= qpos) ? p : 0.f;
-        }
-    };
-    // Interleave the 8 MFMAs of one sub-tile with the exp/accumulate VALU work
-    // of the other, so the matrix pipe and the vector ALU run together.
-#define H2O_INTERLEAVE(VALU_PER_MFMA)                                  \
-    do {                                                             \
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           \
-        _Pragma("unroll") for (int i_ = 0; i_ < KS; ++i_) {          \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       \
-            __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER_MFMA, 0); \
-            if (i_ + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); \
-        }                                                            \
-    } while (0)
 
-    // Two-stage pipeline over row tiles.  Buffer (rt - tile0) & 1 holds tile rt.
-    // Step rt: store tile rt+1 (loaded during the previous step), load tile
-    // rt+2; stage A = MFMAs of sub-tile 1 with the exps of sub-tile 0; barrier;
-    // stage B = MFMAs of sub-tile 0 of tile rt+1 with the exps of sub-tile 1.
-    // A buffer is refilled only after the barrier that follows its last read.
-    gload(tile0);
-    lstore(0);
-    if (tile0 + 1 < ntile) gload(tile0 + 1);
-    __syncthreads();
-    const bool keys_ok = kmin >= 0;
-    f32x16 s0 = mma(0, 0);
-    for (int rt = tile0; rt < ntile; ++rt) {
-        const int cur = (rt - tile0) & 1;
+    // Prologue: tiles tile0 and tile0+1; S of (tile0, sub 0).
+    issue(sQ0, sL0, tile0);
+    if (tile0 + 1 < ntile) issue(sQ1, sL1, tile0 + 1);
+    publish_lds_loads();
+    f32x16 s0 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) s0 = mfma32(kf[ks], qread(sQ0, 0, ks), s0);
+
+    auto step = [&](auto odd_c, int rt) {
+        constexpr bool odd = decltype(odd_c)::value;      // (rt - tile0) & 1
+        unsigned char* qc = odd ? sQ1 : sQ0;              // tile rt
+        unsigned char* qn = odd ? sQ0 : sQ1;              // tile rt+1
+        float* lc = odd ? sL1 : sL0;
+        float* ln = odd ? sL0 : sL1;
         const bool has_next = rt + 1 < ntile;
-        const float l0 = sL[cur][lq], l1 = sL[cur][32 + lq];
-        if (has_next) lstore(cur ^ 1);
-        if (rt + 2 < ntile) gload(rt + 2);
-        f32x16 s1;
-        if (keys_ok && kmax <= first_pos(rt, 0)) {
-            s1 = mma(cur, 1);
-            exp_full(s0, l0);
-            H2O_INTERLEAVE(6);
-        } else {
-            s1 = mma(cur, 1);
-            exp_masked(s0, l0, lane_pos(rt, 0));
-        }
-        __syncthreads();
-        const bool full1 = keys_ok && kmax <= first_pos(rt, 1);
-        if (has_next && full1) {
-            s0 = mma(cur ^ 1, 0);
-            exp_full(s1, l1);
-            H2O_INTERLEAVE(6);
-        } else {
-            if (has_next) s0 = mma(cur ^ 1, 0);
-            if (full1) exp_full(s1, l1);
-            else exp_masked(s1, l1, lane_pos(rt, 1));
-        }
+        const float l0 = lse2_of(lc, rt, 0), l1 = lse2_of(lc, rt, 1);
+        // A: MFMAs of (rt, 1) with the exponentials of (rt, 0).
+        const f32x16 s1 = stage(qc, 1, s0, l0, full_tile(rt, 0), rt, 0, true);
+        publish_lds_loads();
+        // B: loads of tile rt+2 into tile rt's buffer; MFMAs of (rt+1, 0) with
+        // the exponentials of (rt, 1).
+        if (rt + 2 < ntile) issue(qc, lc, rt + 2);
+        s0 = stage(qn, 0, s1, l1, full_tile(rt, 1), rt, 1, has_next);
+        (void)ln;
+    };
+    for (int rt = tile0; rt < ntile; rt += 2) {
+        step(std::false_type{}, rt);
+        if (rt + 1 < ntile) step(std::true_type{}, rt + 1);
     }
-#undef H2O_INTERLEAVE
+    publish_lds_loads();
 
 #pragma unroll
     for (int r = 0; r < 16; ++r) sRed[wave][8 * (r >> 2) + 4 * hh + (r & 3)][lq] = acc[r];
