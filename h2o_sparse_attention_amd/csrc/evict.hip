@@ -5,6 +5,7 @@
 // H2O score is the running sum of the summed attention weights, optionally
 // normalised by age, and new content overwrites the slots of smallest score.
 #include "h2o_internal.h"
+#include "device_common.h"
 
 #include <climits>
 
@@ -86,13 +87,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sWave, int& tota
 }
 
 // One workgroup per (b, kv head); KPT consecutive slots per thread, held in
-// registers.  The k-th smallest key T is found by a most-significant-bit-first
-// radix-2 select: 32 rounds, each counting keys below a candidate with wave
-// ballots.  Victims are every key below T plus the lowest-index slots equal
-// to T, which gives the (score, slot index) order exactly.
+// registers.  The k-th smallest key T is found by a most-significant-digit-
+// first radix select over four 8-bit digits: each pass builds an LDS
+// histogram of the digit among the keys that match the digits fixed so far,
+// and one wave scans it for the bin that holds the k-th key.  Victims are
+// every key below T plus the lowest-index slots equal to T, which gives the
+// (score, slot index) order exactly.
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
-    __shared__ int sCnt[2][kSelWaves];
+    __shared__ int sHist[256];
+    __shared__ int sSel[2];
     __shared__ int sWave[kSelWaves];
     const int bg = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -111,16 +115,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
         // Coalesced pass: slot j = e*1024 + tid forms its order key into LDS; then
         // each thread takes KPT consecutive slots, so thread order is slot order.
         extern __shared__ uint32_t sKeys[];
+        // All loads first (buffer loads past slot n return zero), then the keys.
+        const dev::Rsrc rs = dev::make_rsrc(sc, n * 4), rp = dev::make_rsrc(ps, n * 4);
+        uint32_t sraw[KPT], praw[KPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            sraw[e] = dev::bload4(rs, (e * kSelThreads + tid) * 4);
+            praw[e] = dev::bload4(rp, (e * kSelThreads + tid) * 4);
+        }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int j = e * kSelThreads + tid;
-            uint32_t kv = kAbsent;
-            if (j < n) {
-                const int pj = ps[j];
-                float v = sc[j];
-                if (a.score_mode == H2O_SCORE_H2O_NORM) v = v / (float)(t_now - pj);
-                kv = pj < thr ? order_key(v) : kIneligible;
-            }
+            const int pj = (int)praw[e];
+            float v = __uint_as_float(sraw[e]);
+            if (a.score_mode == H2O_SCORE_H2O_NORM) v = v / (float)(t_now - pj);
+            const uint32_t kv = j >= n ? kAbsent : (pj < thr ? order_key(v) : kIneligible);
             sKeys[j + j / 16] = kv;               // one pad word per 16: no bank conflicts
         }
         __syncthreads();
@@ -150,19 +159,44 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
             }
             return;
         }
-        uint32_t T = 0u;
-        for (int bit = 31; bit >= 0; --bit) {
-            const uint32_t X = T | (1u << bit);
-            int cnt = 0;
-#pragma unroll
-            for (int e = 0; e < KPT; ++e) cnt += wave_count(key[e] < X);
-            if (lane == 0) sCnt[bit & 1][wave] = cnt;
+        uint32_t prefix = 0u, mask = 0u;
+        int k_rem = k;                        // rank of T among the keys matching prefix
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            if (tid < 256) sHist[tid] = 0;
             __syncthreads();
-            int tot = 0;
 #pragma unroll
-            for (int w = 0; w < kSelWaves; ++w) tot += sCnt[bit & 1][w];
-            if (tot < k) T = X;
+            for (int e = 0; e < KPT; ++e)
+                if ((key[e] & mask) == prefix) atomicAdd(&sHist[(key[e] >> shift) & 255u], 1);
+            __syncthreads();
+            if (wave == 0) {
+                int c4[4], sum = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    c4[q] = sHist[4 * lane + q];
+                    sum += c4[q];
+                }
+                int incl = sum;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(incl, off);
+                    if (lane >= off) incl += y;
+                }
+                int before = incl - sum;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (before < k_rem && before + c4[q] >= k_rem) {
+                        sSel[0] = 4 * lane + q;
+                        sSel[1] = before;
+                    }
+                    before += c4[q];
+                }
+            }
+            __syncthreads();
+            prefix |= (uint32_t)sSel[0] << shift;
+            mask |= 255u << shift;
+            k_rem -= sSel[1];
         }
+        const uint32_t T = prefix;
         // T is the k-th smallest key: count(< T) < k <= count(<= T).
         int my_less = 0, my_eq = 0;
 #pragma unroll
