@@ -100,11 +100,6 @@ struct AttnTile {
     static constexpr int LOADS = kKeysPerTile * RB / 1024 / 4;   // 1 KB loads per wave per tile
 };
 
-// LDS chunk c of row r holds logical chunk c ^ swz(r) (16-byte chunks).
-template <int D>
-__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short s16x4 __attribute__((ext_vector_type(4)));

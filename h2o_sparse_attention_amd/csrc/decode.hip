@@ -38,15 +38,16 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecSub = 32;                 // slots per wave step
-constexpr int kDecSplit = 1024;             // slots per workgroup
+constexpr int kDecSplit = 4096;             // slots per workgroup
 constexpr int kFinishKeys = 2048;           // slots per finishing workgroup
 
 template <int D>
 struct DecSmem {
-    static constexpr int KROW = D + 8;      // +16 B: conflict-free A-operand rows
-    static constexpr int VROW = D + 32;     // +64 B: conflict-free transposing reads
-    static constexpr int K_BYTES = kDecSub * KROW * 2;
-    static constexpr int V_BYTES = kDecSub * VROW * 2;
+    // K and V tiles are unpadded with XOR-swizzled 16-byte chunks (swz_k,
+    // swz_v), which keeps two workgroups per CU.
+    static constexpr int RB = 2 * D;        // bytes per K / V row
+    static constexpr int K_BYTES = kDecSub * RB;
+    static constexpr int V_BYTES = kDecSub * RB;
     static constexpr int WAVE_BYTES = K_BYTES + V_BYTES + kDecSub * 4;
     static constexpr int QROW = D + 8;      // Q^T operand rows (32 columns)
     static constexpr int Q_BYTES = 32 * QROW * 2;
@@ -69,7 +70,7 @@ template <int D>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
     using L = DecSmem<D>;
-    constexpr int KS = D / 16, DT = D / 32, KROW = L::KROW, VROW = L::VROW;
+    constexpr int KS = D / 16, DT = D / 32, RB = L::RB;
     constexpr int CH = D / 8;                              // 16-byte chunks per row
     constexpr int LD = kDecSub * CH / 64;                  // 16-byte loads per lane
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -98,8 +99,8 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
     __syncthreads();
 
     unsigned char* wbase = smem + wave * L::WAVE_BYTES;
-    u16* sK = reinterpret_cast<u16*>(wbase);
-    u16* sV = reinterpret_cast<u16*>(wbase + L::K_BYTES);
+    unsigned char* sK = wbase;
+    unsigned char* sV = wbase + L::K_BYTES;
     int* sPos = reinterpret_cast<int*>(wbase + L::K_BYTES + L::V_BYTES);
 
     const u16* Kc = static_cast<const u16*>(a.kc) + (size_t)bg * NC * D;
@@ -123,8 +124,8 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
         const Rsrc rv = make_rsrc(Vc + (size_t)k0 * D, valid * D * 2);
 #pragma unroll
         for (int it = 0; it < LD; ++it) {
-            kreg[it] = bload16(rk, goff0 + it * RPL * D * 2);
-            vreg[it] = bload16(rv, goff0 + it * RPL * D * 2);
+            kreg[it] = bload16_stream(rk, goff0 + it * RPL * D * 2);
+            vreg[it] = bload16_stream(rv, goff0 + it * RPL * D * 2);
         }
         if (lane < kDecSub) {
             const Rsrc rp = make_rsrc(posg + k0, valid * 4);
@@ -132,11 +133,15 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
             pvalid = lane < valid;
         }
     };
+    // LDS byte offsets of this lane's chunks (row row0 + it*RPL, chunk lane%CH);
+    // RPL is a multiple of 4, so swz_v is the same for every `it`.
+    const int cg = lane % CH;
     auto lstore = [&]() {
 #pragma unroll
         for (int it = 0; it < LD; ++it) {
-            *reinterpret_cast<u32x4*>(&sK[(row0 + it * RPL) * KROW + col0]) = kreg[it];
-            *reinterpret_cast<u32x4*>(&sV[(row0 + it * RPL) * VROW + col0]) = vreg[it];
+            const int r = row0 + it * RPL;
+            *reinterpret_cast<u32x4*>(sK + r * RB + 16 * (cg ^ swz_k<D>(r))) = kreg[it];
+            *reinterpret_cast<u32x4*>(sV + r * RB + 16 * (cg ^ swz_v<D>(r))) = vreg[it];
         }
         if (lane < kDecSub) sPos[lane] = pvalid ? preg : INT_MAX;
     };
@@ -148,6 +153,12 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
     const int prow = perm_key(lq);
+    // K operand: row prow, chunk 2*ks + hh at kb ^ 32*ks; V^T operand rows
+    // 8*hh + j16/4 (+16*s2, +4 for the second read), d block dt at vb ^ 64*dt.
+    const int kb = prow * RB + 16 * (hh ^ swz_k<D>(prow));
+    const int vrow = 8 * hh + (j16 >> 2);
+    const int vb = vrow * RB + 16 * ((2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ swz_v<D>(vrow)) +
+                   8 * (j16 & 1);
     const int qpos = a.P;
     float* logit_row = ws.logits + ((size_t)bg * G + min(lq, G - 1)) * ws.ncp;
 
@@ -162,10 +173,9 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
         const int next = sub + kDecWaves;
         if (next < nsub) gload(next);
         f32x16 s = f32x16{};
-        const u16* kp = &sK[prow * KROW + 8 * hh];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            s = mfma32(as_bf16x8(ld16(kp + 16 * ks)),
+            s = mfma32(as_bf16x8(ld16(sK + (kb ^ (32 * ks)))),
                        as_bf16x8(ld16(&sQ[lq * L::QROW + 16 * ks + 8 * hh])), s);
         // key of C register r: 16*(r/8) + 8*hh + r%8 within the sub-tile
         const int kp_lane = sPos[lane & 31];
@@ -223,13 +233,12 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const u16* vp = &sV[(16 * s2 + 8 * hh + (j16 >> 2)) * VROW + dt * 32 +
-                                    16 * (g16 & 1) + 4 * (j16 & 3)];
+                const unsigned char* vp = sV + (vb ^ (64 * dt)) + 16 * s2 * RB;
                 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4*)(vp));
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4*)(vp + 4 * VROW));
+                    (lds_s16x4*)(vp + 4 * RB));
                 const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
                 const u32x4 av = {l2[0], l2[1], h2[0], h2[1]};
                 o[dt] = mfma32(as_bf16x8(av), pb[s2], o[dt]);
@@ -305,6 +314,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
     const u16* Vn = static_cast<const u16*>(a.vn) + (size_t)bg * D;
     auto bf = [](u16 x) { return __uint_as_float((uint32_t)x << 16); };
 
+    // The logits of this workgroup's slots for the first kPre heads do not
+    // depend on the merged LSE: start their loads before computing it.
+    // Slots past n read zeros and are never stored.
+    const int j0 = kc * kFinishKeys, j1 = min(n, j0 + kFinishKeys);
+    constexpr int U = kFinishKeys / kDecThreads;           // slots per thread
+    static_assert(kFinishKeys % kDecThreads == 0, "finish tiling");
+    constexpr int kPre = 4;
+    const Rsrc rlog = make_rsrc(ws.logits + (size_t)bg * G * ws.ncp, G * ws.ncp * 4);
+    auto lload = [&](int hh, int u) {
+        return __uint_as_float(bload4_stream(rlog, (hh * ws.ncp + j0 + tid + u * kDecThreads) * 4));
+    };
+    float vpre[kPre][U];
+#pragma unroll
+    for (int hh = 0; hh < kPre; ++hh)
+#pragma unroll
+        for (int u = 0; u < U; ++u) vpre[hh][u] = hh < G ? lload(hh, u) : 0.f;
+
     // Per head: the new token's logit and the merged log-sum-exp (log2 units).
     for (int hh = wave; hh < G; hh += kDecWaves) {
         const u16* q = Q + (size_t)(b * a.Hq + g * G + hh) * D;
@@ -366,21 +392,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
             a.cs_new[bg] = cs;
         }
     }
-    const int j0 = kc * kFinishKeys, j1 = min(n, j0 + kFinishKeys);
-    const float* lrow = ws.logits + (size_t)bg * G * ws.ncp;
-    constexpr int U = kFinishKeys / kDecThreads;           // slots per thread
-    static_assert(kFinishKeys % kDecThreads == 0, "finish tiling");
     float cs[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) cs[u] = 0.f;
-    for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+    for (int hh = 0; hh < kPre; ++hh) {
+        if (hh < G) {
+            const float l2 = sLse2[hh];
+#pragma unroll
+            for (int u = 0; u < U; ++u) cs[u] += fast_exp2(vpre[hh][u] - l2);
+        }
+    }
+    for (int hh = kPre; hh < G; ++hh) {
         const float l2 = sLse2[hh];
         float v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = j0 + tid + u * kDecThreads;
-            v[u] = j < j1 ? lrow[(size_t)hh * ws.ncp + j] : -INFINITY;
-        }
+        for (int u = 0; u < U; ++u) v[u] = lload(hh, u);
 #pragma unroll
         for (int u = 0; u < U; ++u) cs[u] += fast_exp2(v[u] - l2);
     }

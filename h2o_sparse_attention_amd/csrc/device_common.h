@@ -54,6 +54,16 @@ __device__ __forceinline__ u32x4 bload16(Rsrc r, int voff) {
 __device__ __forceinline__ uint32_t bload4(Rsrc r, int voff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
 }
+// Streaming loads of data read exactly once: cache policy SC1 (device scope),
+// which skips the CU's vector L1 and sustains more bandwidth for long streams.
+constexpr int kStreamPolicy = 2;
+__device__ __forceinline__ uint32_t bload4_stream(Rsrc r, int voff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kStreamPolicy);
+}
+__device__ __forceinline__ u32x4 bload16_stream(Rsrc r, int voff) {
+    return __builtin_bit_cast(u32x4,
+                              __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kStreamPolicy));
+}
 
 // Workgroup ids are dispatched round-robin over the 8 XCDs; give each XCD a
 // contiguous range of logical tiles so tiles that share K/V (or Q) share an L2.
@@ -63,6 +73,16 @@ __device__ __forceinline__ int xcd_tile(int lin, int total) {
 }
 
 __host__ __device__ inline int xcd_grid(int total) { return ((total + 7) >> 3) << 3; }
+
+// Unpadded LDS tiles of D-element bf16 rows hold their 16-byte chunks
+// XOR-swizzled: LDS chunk c of row r holds logical chunk c ^ swz(r).  swz_k
+// keeps the MFMA operand reads (row r of 16 or 32 consecutive rows, one chunk)
+// free of bank conflicts; swz_v does the same for ds_read_b64_tr_b16 reads
+// (four consecutive rows, two 8-byte halves of neighbouring chunks).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // A-operand row m of the QK^T product reads physical key perm_key(m).
 __device__ __forceinline__ int perm_key(int m) {
