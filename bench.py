@@ -165,7 +165,8 @@ def run_decode(args):
     reset()
     torch.cuda.synchronize()
     n_launch = args.steps * wl.seq_len
-    timers = {k: h2o.KernelTimer(k, n_launch) for k in ("decode", "update", "select", "insert")}
+    timers = {k: h2o.KernelTimer(k, n_launch)
+              for k in ("decode", "decode_finish", "update", "select", "insert")}
     total_s = 0.0
     for t_ in timers.values():
         t_.__enter__()

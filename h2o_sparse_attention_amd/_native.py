@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "H2O_OK", -1: "H2O_ERR_INVALID_ARG", -2: "H2O_ERR_UNSUPPORTED
 
 H2O_F32, H2O_BF16 = 0, 1
 H2O_SCORE_H2O, H2O_SCORE_H2O_NORM = 0, 1
-KERNEL_IDS = {"attn": 0, "colsum": 1, "update": 2, "select": 3, "insert": 4, "decode": 5}
+KERNEL_IDS = {"attn": 0, "colsum": 1, "update": 2, "select": 3, "insert": 4, "decode": 5,
+              "decode_finish": 6}
 
 # Every function include/h2o.h declares, with its ctypes signature.
 EXPORTS = {}

@@ -178,9 +178,7 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
             return st;
     }
     if (ws_need > 0) {
-        timer_begin(H2O_KERNEL_DECODE, s);
-        hipError_t e = launch_decode(a, workspace, s);
-        timer_end(H2O_KERNEL_DECODE, s);
+        hipError_t e = launch_decode(a, workspace, s);     // times its two kernels
         if ((st = check_hip(e, "decode attention launch")) != H2O_OK) return st;
         return ok();
     }

@@ -458,14 +458,18 @@ hipError_t launch_decode(const ChunkArgs& a, void* workspace, hipStream_t s) {
             configured |= bit;
         }
         const int total = nsplit_rt * a.B * a.Hkv;
+        timer_begin(H2O_KERNEL_DECODE, s);
         hipLaunchKernelGGL(decode_attn_kernel<128>, dim3(xcd_grid(total)), dim3(kDecThreads),
                            DecSmem<128>::BYTES, s, a, ws, nsplit_rt);
+        timer_end(H2O_KERNEL_DECODE, s);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int kchunks = a.n > 0 ? (a.n + kFinishKeys - 1) / kFinishKeys : 1;
+    timer_begin(H2O_KERNEL_DECODE_FINISH, s);
     hipLaunchKernelGGL(decode_finish_kernel<128>, dim3(kchunks, a.B * a.Hkv), dim3(kDecThreads), 0,
                        s, a, ws, nsplit_rt, kchunks);
+    timer_end(H2O_KERNEL_DECODE_FINISH, s);
     return hipGetLastError();
 }
 

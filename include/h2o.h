@@ -170,7 +170,8 @@ typedef enum {
     H2O_KERNEL_SELECT = 3,    /* eligibility + victim selection                 */
     H2O_KERNEL_INSERT = 4,    /* chunk insertion                                */
     H2O_KERNEL_DECODE = 5,    /* S = 1 attention (split over slots)             */
-    H2O_KERNEL_COUNT = 6
+    H2O_KERNEL_DECODE_FINISH = 6, /* S = 1: merge of the splits, summed weights */
+    H2O_KERNEL_COUNT = 7
 } h2o_kernel_id_t;
 
 H2O_API h2o_status_t h2o_kernel_timer_start(int32_t kernel, int32_t max_launches);
