@@ -19,6 +19,8 @@ from .h2o_oracle import (  # noqa: F401
     attend_chunk,
     evict_and_insert,
     h2o_step,
+    lastrec_step,
     select_victims,
+    select_victims_lastrec,
     update_scores,
 )

@@ -27,7 +27,10 @@ Readings taken where the pages are silent or garbled:
   whose position is older than P - W; victims are the k smallest by
   (score, slot index); chunk token i goes to the i-th smallest freed slot;
 * a newly inserted token starts with its own in-chunk summed weight as score;
-* h2o-norm divides the score by the age t - t(j) with t = P + S, in float32.
+* h2o-norm divides the score by the age t - t(j) with t = P + S, in float32;
+* lastrec ("Experimental Validation", the lr policy: the first beta and the
+  last N_C - beta tokens stay) evicts the k oldest filled slots whose position
+  is at least beta, and refuses a chunk when fewer are eligible.
 """
 from __future__ import annotations
 
@@ -203,3 +206,41 @@ def h2o_step(state: H2OState, q, k_new, v_new, sm_scale: float, W: int,
     return {"out": out, "lse": lse, "colsum_cache": cs_cache, "colsum_new": cs_new,
             "phi_updated": phi_after_update, "victims": victims,
             "evicted_phi": evicted_phi, "freed_slots": freed}
+
+
+# --------------------------------------------------------------------- lastrec
+def select_victims_lastrec(state: H2OState, S: int, beta: int):
+    """Victim slots of the lastrec policy, ascending slot index: shape (B, Hkv, k).
+
+    lastrec keeps the first beta tokens and the last N_C - beta tokens of the
+    sequence (montaan paper page, "Experimental Validation", the lr policy).
+    When the chunk does not fit, the k = n + S - N_C oldest filled slots among
+    those at position >= beta are evicted (positions are unique: no ties).
+    """
+    B, Hkv, NC = state.pos.shape
+    n = state.n
+    k = eviction_count(n, S, NC)
+    victims = np.zeros((B, Hkv, k), np.int64)
+    if k == 0:
+        return victims
+    for b in range(B):
+        for g in range(Hkv):
+            slots = np.arange(n)
+            eligible = slots[state.pos[b, g, :n] >= beta]
+            if eligible.size < k:
+                raise ValueError(f"cannot evict {k} slots: only {eligible.size} eligible")
+            oldest = np.argsort(state.pos[b, g, eligible], kind="stable")
+            victims[b, g] = np.sort(eligible[oldest[:k]])
+    return victims
+
+
+def lastrec_step(state: H2OState, q, k_new, v_new, sm_scale: float, beta: int):
+    """One chunk under lastrec: attend (the summed weights are not needed by the
+    policy), evict by position, insert with score 0.  Mutates ``state``."""
+    S = np.shape(q)[2]
+    out, lse, _, cs_new = attend_chunk(state, q, k_new, v_new, sm_scale)
+    victims = select_victims_lastrec(state, S, beta)
+    freed = evict_and_insert(state, victims, np.asarray(k_new, np.float64),
+                             np.asarray(v_new, np.float64), np.zeros(np.shape(cs_new)))
+    return {"out": out, "lse": lse, "victims": victims, "freed_slots": freed}
+

@@ -344,7 +344,60 @@ def check_slot_permutation_invariance(orc, seed=9):
         assert va == vb
 
 
+def lastrec_resident(c0, NC, beta):
+    """Closed form of the lastrec cache before the chunk starting at token c0: every
+    earlier token while they fit, else the first beta and the last NC - beta."""
+    if c0 <= NC:
+        return list(range(c0))
+    return list(range(beta)) + list(range(c0 - (NC - beta), c0))
+
+
+def check_lastrec_closed_form(orc, seed=10):
+    """lastrec keeps the first beta and the last N_C - beta tokens: the cache holds that
+    set after every chunk, K and V rows follow their tokens, and every chunk's output is
+    torch's SDPA over exactly those keys plus the chunk's causal keys."""
+    B, Hq, Hkv, d, N = 2, 4, 2, 8, 53
+    G = Hq // Hkv
+    sm = 0.7
+    q, k, v = random_problem(seed, B=B, Hq=Hq, Hkv=Hkv, d=d, N=N)
+    for S, NC, beta in [(4, 16, 3), (5, 12, 0), (3, 10, 7), (1, 9, 2)]:
+        st = orc.H2OState.empty(B, Hkv, NC, d)
+        for c0 in range(0, N, S):
+            c1 = min(N, c0 + S)
+            keys = lastrec_resident(c0, NC, beta) + list(range(c0, c1))
+            res = orc.lastrec_step(st, q[:, :, c0:c1], k[:, :, c0:c1], v[:, :, c0:c1], sm, beta)
+            kk = torch.from_numpy(np.repeat(k[:, :, keys], G, axis=1))
+            vv = torch.from_numpy(np.repeat(v[:, :, keys], G, axis=1))
+            mask = torch.from_numpy(np.array(keys)[None, :] <= np.arange(c0, c1)[:, None])
+            want = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[:, :, c0:c1]), kk, vv, attn_mask=mask, scale=sm).numpy()
+            np.testing.assert_allclose(res["out"], want, rtol=0, atol=1e-12)
+            held = sorted(lastrec_resident(c1, NC, beta))
+            for b in range(B):
+                for g in range(Hkv):
+                    assert sorted(st.pos[b, g, :st.n].tolist()) == held
+                    np.testing.assert_array_equal(st.K[b, g, :st.n], k[b, g, st.pos[b, g, :st.n]])
+                    np.testing.assert_array_equal(st.V[b, g, :st.n], v[b, g, st.pos[b, g, :st.n]])
+                    assert res["freed_slots"][b, g].tolist() == sorted(res["freed_slots"][b, g])
+
+
+def check_lastrec_capacity_error(orc):
+    """lastrec cannot evict the first beta tokens: a chunk longer than N_C - beta into a
+    full cache has too few eligible slots and must be refused."""
+    NC, beta, d = 8, 5, 4
+    st = orc.H2OState.empty(1, 1, NC, d)
+    z = np.zeros((1, 1, NC, d))
+    orc.lastrec_step(st, z, z, z, 1.0, beta)               # fills the cache
+    z4 = np.zeros((1, 1, 4, d))
+    try:
+        orc.lastrec_step(st, z4, z4, z4, 1.0, beta)        # needs 4 of 3 eligible
+    except ValueError:
+        return
+    raise AssertionError("lastrec accepted more victims than eligible slots")
+
+
 ALL_CHECKS = [check_golden, check_rows_normalised, check_exact_when_no_eviction,
               check_chunk_size_invariance, check_uniform_closed_form,
               check_bruteforce_selection, check_decode_is_argmin, check_dense_masked_replay,
-              check_conservation_and_monotonicity, check_slot_permutation_invariance]
+              check_conservation_and_monotonicity, check_slot_permutation_invariance,
+              check_lastrec_closed_form, check_lastrec_capacity_error]

@@ -41,6 +41,8 @@ MUTANTS = [
     ("state.pos[b, g, j] = state.P + i", "state.pos[b, g, j] = state.P + i + 1",
      "inserted position off by one"),
     ("t_now = state.P + S", "t_now = state.P", "h2o-norm age off by S"),
+    ("state.pos[b, g, :n] >= beta", "state.pos[b, g, :n] > beta", "lastrec sink off by one"),
+    ("np.sort(eligible[oldest[:k]])", "np.sort(eligible[oldest[-k:]])", "lastrec evicts newest"),
 ]
 
 
