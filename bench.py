@@ -8,6 +8,10 @@ tokens = 64 chunks).  Inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is F6 TFLOP/s: 6*d*Hq*(visible query/key pairs),
 i.e. QK^T and PV for the output plus the QK^T recompute for the summed weights.
+
+`--policy lastrec` runs the same sequence under the lastrec policy (attention
+without summed weights, eviction by position keeping the first `--sink`
+tokens); its `value` is F4 TFLOP/s, the work that policy does.
 """
 from __future__ import annotations
 
@@ -111,12 +115,14 @@ def copy_probe(mib: int) -> None:
 
 
 DECODE_METRIC = "H2O decode step (attn+score+evict) tokens/s, % HBM roofline"
+LASTREC_METRIC = "lastrec chunk-attn+evict TFLOP/s & tokens/s (chunk 1k, 64k ctx), % roofline"
+LASTREC_DECODE_METRIC = "lastrec decode step (attn+evict) tokens/s, % HBM roofline"
 
 
-def decode_slot_bytes(wl) -> int:
+def decode_slot_bytes(wl, policy="h2o") -> int:
     """Algorithmic HBM bytes per cache slot per decode step: K and V rows read,
-    the score read and written, the position read."""
-    return 2 * wl.head_dim * 2 + 8 + 4
+    the position read, and under h2o the score read and written."""
+    return 2 * wl.head_dim * 2 + 4 + (8 if policy == "h2o" else 0)
 
 
 def capture(fn, reset):
@@ -180,6 +186,8 @@ def run_decode(args):
             "freed_slots": torch.empty(B, Hkv, 1, dtype=torch.int32, device=dev),
             "workspace": torch.zeros(h2o.workspace_bytes(dims, 1), dtype=torch.uint8, device=dev)}
 
+    step_kw = dict(policy=args.policy, sink_tokens=args.sink)
+
     def reset():
         cache.load(snap["k"], snap["v"], snap["pos"].to(torch.int32), snap["phi"].float(),
                    NC, NC)
@@ -187,7 +195,7 @@ def run_decode(args):
     def run(nsteps):
         for t in range(nsteps):
             q, k, v = steps_in[t % len(steps_in)]
-            h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs)
+            h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs, **step_kw)
 
     for _ in range(args.warmup):
         reset()
@@ -196,8 +204,10 @@ def run_decode(args):
     torch.cuda.synchronize()
     # Per-kernel means: one eager pass with the library's kernel timers.
     n_launch = args.steps * wl.seq_len
-    timers = {k: h2o.KernelTimer(k, n_launch)
-              for k in ("decode", "decode_finish", "update", "select", "insert")}
+    kernels = ("decode", "decode_finish", "update", "select", "insert")
+    if args.policy == "lastrec":
+        kernels = ("decode", "decode_finish", "select", "insert")
+    timers = {k: h2o.KernelTimer(k, n_launch) for k in kernels}
     for t_ in timers.values():
         t_.__enter__()
     eager_s = 0.0
@@ -212,6 +222,7 @@ def run_decode(args):
         t_.__exit__(None, None, None)
     ref_out = bufs["out"].clone()
     ref_score = cache.score.clone()
+    ref_pos = cache.pos.clone()
     # Timed region: the 512 steps replayed from one captured HIP graph (the
     # snapshot reload between replays is outside the timed region).
     total_s = eager_s
@@ -225,22 +236,26 @@ def run_decode(args):
             graph.replay()
             torch.cuda.synchronize()
             total_s += time.perf_counter() - t0
-        check_replay("decode", [(bufs["out"], ref_out), (cache.score, ref_score)])
+        check_replay("decode", [(bufs["out"], ref_out), (cache.score, ref_score),
+                                (cache.pos, ref_pos)])
     n_tok = args.steps * wl.seq_len * B
     us_per_step = total_s / (args.steps * wl.seq_len) * 1e6
-    slot_bytes = decode_slot_bytes(wl)
+    slot_bytes = decode_slot_bytes(wl, args.policy)
     step_bytes = B * Hkv * NC * slot_bytes
     dec = timers["decode"]
     kv_bytes = B * Hkv * NC * 2 * D * 2            # K and V rows read by the attention launch
     achieved = kv_bytes / (dec.mean_ms * 1e-3) / 1e9
     line = {
-        "metric": DECODE_METRIC, "value": round(n_tok / total_s, 1), "unit": "tokens/s",
+        "metric": DECODE_METRIC if args.policy == "h2o" else LASTREC_DECODE_METRIC,
+        "value": round(n_tok / total_s, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(total_s / args.steps * 1e3, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "capacity": NC, "recent_window": wl.recent_window,
-                   "decode_steps": wl.seq_len, "parallelism": "single-gpu"},
+                   "decode_steps": wl.seq_len, "policy": args.policy,
+                   **({"sink_tokens": args.sink} if args.policy == "lastrec" else {}),
+                   "parallelism": "single-gpu"},
         "timing": "hip_graph" if not args.no_graph else "eager",
         "us_per_decode_step": round(us_per_step, 2),
         "us_per_decode_step_eager": round(eager_s / (args.steps * wl.seq_len) * 1e6, 2),
@@ -269,6 +284,9 @@ def main():
                     help="time eager launches instead of replaying a captured HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run plain copies of this size first (HBM counter calibration)")
+    ap.add_argument("--policy", choices=("h2o", "lastrec"), default="h2o")
+    ap.add_argument("--sink", type=int, default=64,
+                    help="lastrec: leading tokens kept (beta); the pages give no value")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -305,10 +323,13 @@ def main():
             "colsum_new": torch.empty(B, Hkv, S, dtype=torch.float32, device=dev),
             "freed_slots": torch.empty(B, Hkv, S, dtype=torch.int32, device=dev)}
 
+    step_kw = dict(policy=args.policy, sink_tokens=args.sink)
+    lastrec = args.policy == "lastrec"
+
     def run_sequence():
         cache.reset()
         for q, k, v in inputs:
-            h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs)
+            h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs, **step_kw)
 
     for _ in range(args.warmup):
         run_sequence()
@@ -317,8 +338,9 @@ def main():
 
     # Per-kernel means: one eager pass with the library's kernel timers.
     n_launch = args.steps * wl.n_chunks
-    timers = {k: h2o.KernelTimer(k, n_launch) for k in ("attn", "colsum", "update", "select",
-                                                       "insert")}
+    kernels = ("attn", "select", "insert") if lastrec else ("attn", "colsum", "update",
+                                                             "select", "insert")
+    timers = {k: h2o.KernelTimer(k, n_launch) for k in kernels}
     for t in timers.values():
         t.__enter__()
     torch.cuda.synchronize()
@@ -329,38 +351,37 @@ def main():
     eager_s = time.perf_counter() - t0
     for t in timers.values():
         t.__exit__(None, None, None)
-    ref = [bufs["out"].clone(), bufs["colsum_cache"].clone(), cache.score.clone(),
-           cache.pos.clone()]
+    checked = [bufs["out"], cache.score, cache.pos] + ([] if lastrec else [bufs["colsum_cache"]])
+    ref = [t.clone() for t in checked]
     # Timed region: whole sequences replayed from one captured HIP graph.
     elapsed = eager_s
     if not args.no_graph:
-        graph = capture(lambda: [h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs)
+        graph = capture(lambda: [h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs, **step_kw)
                                  for q, k, v in inputs], cache.reset)
         graph.replay()
         torch.cuda.synchronize()
-        check_replay("prefill", zip([bufs["out"], bufs["colsum_cache"], cache.score,
-                                     cache.pos], ref))
+        check_replay("prefill", zip(checked, ref))
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
             graph.replay()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        check_replay("prefill", zip([bufs["out"], bufs["colsum_cache"], cache.score,
-                                     cache.pos], ref))
+        check_replay("prefill", zip(checked, ref))
     ms_per_step = elapsed / args.steps * 1e3
 
     # sanity on the last chunk: every query row's weights sum to 1
-    total = bufs["colsum_cache"].sum().item() + bufs["colsum_new"].sum().item()
-    expect = B * Hkv * S * (Hq // Hkv)
-    if abs(total - expect) > 1e-3 * expect:
-        print(f"[bench] WARNING: summed weights {total} != {expect}", file=sys.stderr)
+    if not lastrec:
+        total = bufs["colsum_cache"].sum().item() + bufs["colsum_new"].sum().item()
+        expect = B * Hkv * S * (Hq // Hkv)
+        if abs(total - expect) > 1e-3 * expect:
+            print(f"[bench] WARNING: summed weights {total} != {expect}", file=sys.stderr)
 
     sched = chunk_schedule(wl)
     pairs = sum(pairs_per_head(n, S) for n in sched)
     f6 = 6.0 * D * Hq * B * pairs
     f4 = 4.0 * D * Hq * B * pairs
-    tflops = f6 / (ms_per_step * 1e-3) / 1e12
+    tflops = (f4 if lastrec else f6) / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = B * wl.seq_len / (ms_per_step * 1e-3)
 
     attn = timers["attn"]
@@ -376,24 +397,27 @@ def main():
     steady_n = [i for i, n in enumerate(sched) if n == NC]
 
     cpu = None
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and not lastrec:
         print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, args.cpu_budget)
 
     line = {
-        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": LASTREC_METRIC if lastrec else METRIC, "value": round(tflops, 3),
+        "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "capacity": NC, "recent_window": wl.recent_window,
                    "chunk": S, "seq_len": wl.seq_len, "chunks": wl.n_chunks,
+                   "policy": args.policy,
+                   **({"sink_tokens": args.sink} if lastrec else {}),
                    "parallelism": "single-gpu"},
         "timing": "hip_graph" if not args.no_graph else "eager",
         "ms_per_step_eager": round(eager_s / args.steps * 1e3, 4),
         "tokens_per_s": round(tokens_per_s, 1),
         "tflops_f4": round(f4 / (ms_per_step * 1e-3) / 1e12, 3),
-        "frac_bf16_peak_f6": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "frac_bf16_peak_f6": None if lastrec else round(tflops / PEAK_BF16_TFLOPS, 4),
         "kernel_mean_us": kernel_us,
         "steady_chunks": len(steady_n),
         "roofline": roofline,

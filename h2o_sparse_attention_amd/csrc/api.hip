@@ -104,6 +104,58 @@ void timer_end(int kernel, hipStream_t s) {
     }
 }
 
+// Shared body of the two eviction entry points.  mode: h2o_score_mode_t, or
+// kModeLastrec with `sink` protected leading positions (then colsum_new is NULL).
+h2o_status_t evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_t chunk_start,
+                              int32_t chunk_len, int mode, int sink, const void* k_new,
+                              const void* v_new, const float* colsum_new, int32_t* freed_slots,
+                              void* stream) {
+    h2o_status_t st;
+    if ((st = validate_dims(dims)) != H2O_OK) return st;
+    if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
+    if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
+    if (!k_new || !v_new || !freed_slots)
+        return fail(H2O_ERR_INVALID_ARG, "k_new, v_new and freed_slots must be non-NULL");
+    const int n = cache->n_valid, S = chunk_len, NC = dims->capacity;
+    const int k = n + S - NC;
+    const bool lastrec = mode == kModeLastrec;
+    const long long guard = lastrec ? sink : dims->recent_window;
+    if (k > 0 && (long long)S + guard > NC)
+        return fail(H2O_ERR_CAPACITY, "cannot evict %d slots: capacity %d < chunk_len %d + %s %lld",
+                    k, NC, S, lastrec ? "sink_tokens" : "recent_window", guard);
+    EvictArgs a;
+    a.kc = cache->k;
+    a.vc = cache->v;
+    a.pos = cache->pos;
+    a.score = cache->score;
+    a.kn = k_new;
+    a.vn = v_new;
+    a.cs_new = colsum_new;
+    a.freed = freed_slots;
+    a.B = dims->batch;
+    a.Hkv = dims->n_kv_heads;
+    a.D = dims->head_dim;
+    a.S = S;
+    a.NC = NC;
+    a.n = n;
+    a.W = dims->recent_window;
+    a.P = (int)chunk_start;
+    a.elem_bytes = dims->dtype == H2O_BF16 ? 2 : 4;
+    a.score_mode = mode;
+    a.sink = sink;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    timer_begin(H2O_KERNEL_SELECT, s);
+    hipError_t e = launch_select(a, s);
+    timer_end(H2O_KERNEL_SELECT, s);
+    if ((st = check_hip(e, "select launch")) != H2O_OK) return st;
+    timer_begin(H2O_KERNEL_INSERT, s);
+    e = launch_insert(a, s);
+    timer_end(H2O_KERNEL_INSERT, s);
+    if ((st = check_hip(e, "insert launch")) != H2O_OK) return st;
+    cache->n_valid = n + S < NC ? n + S : NC;
+    return ok();
+}
+
 }  // namespace h2o
 
 using namespace h2o;
@@ -132,8 +184,11 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
     if ((st = validate_dims(dims)) != H2O_OK) return st;
     if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
     if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
-    if (!q || !k_new || !v_new || !out || !lse || !colsum_cache || !colsum_new)
-        return fail(H2O_ERR_INVALID_ARG, "q, k_new, v_new, out, lse and colsum buffers must be non-NULL");
+    if (!q || !k_new || !v_new || !out || !lse)
+        return fail(H2O_ERR_INVALID_ARG, "q, k_new, v_new, out and lse must be non-NULL");
+    if ((colsum_cache == nullptr) != (colsum_new == nullptr))
+        return fail(H2O_ERR_INVALID_ARG, "colsum_cache and colsum_new must both be set or both be NULL");
+    const bool want_cs = colsum_cache != nullptr;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
         return fail(H2O_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
     {
@@ -172,7 +227,7 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int rows = a.B * a.Hkv;
 
-    if (a.n < a.NC) {
+    if (want_cs && a.n < a.NC) {
         if ((st = check_hip(launch_zero_f32(colsum_cache, a.NC - a.n, a.NC, rows, a.n, s),
                             "zero colsum tail")) != H2O_OK)
             return st;
@@ -187,6 +242,7 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
     hipError_t e = bf16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
     timer_end(H2O_KERNEL_ATTN, s);
     if ((st = check_hip(e, "attention launch")) != H2O_OK) return st;
+    if (!want_cs) return ok();
     timer_begin(H2O_KERNEL_COLSUM, s);
     e = bf16 ? launch_colsum_bf16(a, s) : launch_colsum_f32(a, s);
     timer_end(H2O_KERNEL_COLSUM, s);
@@ -217,50 +273,21 @@ h2o_status_t h2o_evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache,
                                   size_t workspace_bytes, void* stream) {
     (void)workspace;
     (void)workspace_bytes;
-    h2o_status_t st;
-    if ((st = validate_dims(dims)) != H2O_OK) return st;
-    if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
-    if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
-    if (!k_new || !v_new || !colsum_new || !freed_slots)
-        return fail(H2O_ERR_INVALID_ARG, "k_new, v_new, colsum_new and freed_slots must be non-NULL");
+    if (!colsum_new) return fail(H2O_ERR_INVALID_ARG, "colsum_new is NULL");
     if (score_mode != H2O_SCORE_H2O && score_mode != H2O_SCORE_H2O_NORM)
         return fail(H2O_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
-    const int n = cache->n_valid, S = chunk_len, NC = dims->capacity, W = dims->recent_window;
-    const int k = n + S - NC;
-    if (k > 0 && (long long)S + W > NC)
-        return fail(H2O_ERR_CAPACITY,
-                    "cannot evict %d slots: capacity %d < chunk_len %d + recent_window %d", k, NC,
-                    S, W);
-    EvictArgs a;
-    a.kc = cache->k;
-    a.vc = cache->v;
-    a.pos = cache->pos;
-    a.score = cache->score;
-    a.kn = k_new;
-    a.vn = v_new;
-    a.cs_new = colsum_new;
-    a.freed = freed_slots;
-    a.B = dims->batch;
-    a.Hkv = dims->n_kv_heads;
-    a.D = dims->head_dim;
-    a.S = S;
-    a.NC = NC;
-    a.n = n;
-    a.W = W;
-    a.P = (int)chunk_start;
-    a.elem_bytes = dims->dtype == H2O_BF16 ? 2 : 4;
-    a.score_mode = score_mode;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    timer_begin(H2O_KERNEL_SELECT, s);
-    hipError_t e = launch_select(a, s);
-    timer_end(H2O_KERNEL_SELECT, s);
-    if ((st = check_hip(e, "select launch")) != H2O_OK) return st;
-    timer_begin(H2O_KERNEL_INSERT, s);
-    e = launch_insert(a, s);
-    timer_end(H2O_KERNEL_INSERT, s);
-    if ((st = check_hip(e, "insert launch")) != H2O_OK) return st;
-    cache->n_valid = n + S < NC ? n + S : NC;
-    return ok();
+    return evict_and_insert(dims, cache, chunk_start, chunk_len, score_mode, 0, k_new, v_new,
+                            colsum_new, freed_slots, stream);
+}
+
+h2o_status_t h2o_evict_and_insert_lastrec(const h2o_dims_t* dims, h2o_cache_t* cache,
+                                          int64_t chunk_start, int32_t chunk_len,
+                                          int32_t sink_tokens, const void* k_new,
+                                          const void* v_new, int32_t* freed_slots,
+                                          void* stream) {
+    if (sink_tokens < 0) return fail(H2O_ERR_INVALID_ARG, "sink_tokens %d < 0", sink_tokens);
+    return evict_and_insert(dims, cache, chunk_start, chunk_len, kModeLastrec, sink_tokens,
+                            k_new, v_new, nullptr, freed_slots, stream);
 }
 
 h2o_status_t h2o_kernel_timer_start(int32_t kernel, int32_t max_launches) {

@@ -6,7 +6,7 @@
 // the generation setting of the metallab summary's Table 7.  With one query
 // row per head the pass is bound by reading the cache once, so:
 //
-//  decode_attn_kernel  one workgroup per (b, kv head, 1024-slot range).  Each
+//  decode_attn_kernel  one workgroup per (b, kv head, 4096-slot range).  Each
 //      of its 4 waves streams 32-slot tiles through a private LDS region (no
 //      workgroup barriers), forms S^T = K Q^T with the G query heads of the
 //      group as MFMA columns, writes the scaled logits (log2 units) of every
@@ -15,6 +15,8 @@
 //  decode_finish_kernel  merges the partials with the new token (its own key
 //      and value) into O and LSE, then turns the stored logits into the summed
 //      weights sum_{h in g} exp(s - LSE_h) per slot.
+//  When the caller asks for no summed weights, the logits are not stored and
+//  the finish kernel runs one workgroup per (b, kv head) for O and LSE only.
 //
 // P V uses ds_read_b64_tr_b16: a 16-lane group addresses four rows of four
 // consecutive bf16 (one key, four d each) and lane j receives column j%4 of
@@ -161,6 +163,7 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
                    8 * (j16 & 1);
     const int qpos = a.P;
     float* logit_row = ws.logits + ((size_t)bg * G + min(lq, G - 1)) * ws.ncp;
+    const bool want_logits = a.cs_cache != nullptr;     // only the summed weights read them
 
     // Wave w owns sub-tiles w, w+4, ...; the LDS region is private to the wave,
     // whose LDS operations complete in order, so no workgroup barrier is needed.
@@ -186,7 +189,7 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
                 if (!(kpv >= 0 && kpv <= qpos)) s[r] = -INFINITY;
             }
         }
-        if (lq < G) {
+        if (want_logits && lq < G) {
             const int k0 = k_begin + sub * kDecSub;
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -325,11 +328,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
     auto lload = [&](int hh, int u) {
         return __uint_as_float(bload4_stream(rlog, (hh * ws.ncp + j0 + tid + u * kDecThreads) * 4));
     };
+    const bool want_cs = a.cs_cache != nullptr;
     float vpre[kPre][U];
 #pragma unroll
     for (int hh = 0; hh < kPre; ++hh)
 #pragma unroll
-        for (int u = 0; u < U; ++u) vpre[hh][u] = hh < G ? lload(hh, u) : 0.f;
+        for (int u = 0; u < U; ++u) vpre[hh][u] = (want_cs && hh < G) ? lload(hh, u) : 0.f;
 
     // Per head: the new token's logit and the merged log-sum-exp (log2 units).
     for (int hh = wave; hh < G; hh += kDecWaves) {
@@ -386,12 +390,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
             static_cast<__hip_bfloat16*>(a.out)[oi] = __float2bfloat16(acc * inv);
             if (d == 0) a.lse[(size_t)(b * a.Hq + g * G + hh)] = sLse2[hh] * 0.6931471805599453f;
         }
-        if (tid == 0) {
+        if (want_cs && tid == 0) {
             float cs = 0.f;
             for (int hh = 0; hh < G; ++hh) cs += fast_exp2(sNew[hh] - sLse2[hh]);
             a.cs_new[bg] = cs;
         }
     }
+    if (!want_cs) return;
     float cs[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) cs[u] = 0.f;
@@ -465,7 +470,8 @@ hipError_t launch_decode(const ChunkArgs& a, void* workspace, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int kchunks = a.n > 0 ? (a.n + kFinishKeys - 1) / kFinishKeys : 1;
+    // Without summed weights only the first workgroup of each (b, g) has work.
+    const int kchunks = (a.n > 0 && a.cs_cache) ? (a.n + kFinishKeys - 1) / kFinishKeys : 1;
     timer_begin(H2O_KERNEL_DECODE_FINISH, s);
     hipLaunchKernelGGL(decode_finish_kernel<128>, dim3(kchunks, a.B * a.Hkv), dim3(kDecThreads), 0,
                        s, a, ws, nsplit_rt, kchunks);

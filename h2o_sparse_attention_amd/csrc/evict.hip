@@ -118,18 +118,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
         // All loads first (buffer loads past slot n return zero), then the keys.
         const dev::Rsrc rs = dev::make_rsrc(sc, n * 4), rp = dev::make_rsrc(ps, n * 4);
         uint32_t sraw[KPT], praw[KPT];
+        const bool need_score = a.score_mode != kModeLastrec;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            sraw[e] = dev::bload4(rs, (e * kSelThreads + tid) * 4);
+            sraw[e] = need_score ? dev::bload4(rs, (e * kSelThreads + tid) * 4) : 0u;
             praw[e] = dev::bload4(rp, (e * kSelThreads + tid) * 4);
         }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int j = e * kSelThreads + tid;
             const int pj = (int)praw[e];
-            float v = __uint_as_float(sraw[e]);
-            if (a.score_mode == H2O_SCORE_H2O_NORM) v = v / (float)(t_now - pj);
-            const uint32_t kv = j >= n ? kAbsent : (pj < thr ? order_key(v) : kIneligible);
+            uint32_t kv;
+            if (a.score_mode == kModeLastrec) {
+                // Positions are non-negative int32: their uint order is their order.
+                kv = j >= n ? kAbsent : (pj >= a.sink ? (uint32_t)pj : kIneligible);
+            } else {
+                float v = __uint_as_float(sraw[e]);
+                if (a.score_mode == H2O_SCORE_H2O_NORM) v = v / (float)(t_now - pj);
+                kv = j >= n ? kAbsent : (pj < thr ? order_key(v) : kIneligible);
+            }
             sKeys[j + j / 16] = kv;               // one pad word per 16: no bank conflicts
         }
         __syncthreads();
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(256) void insert_kernel(EvictArgs a) {
         if (tok < a.S) {
             const int slot = freed[tok];
             a.pos[(size_t)bg * a.NC + slot] = a.P + tok;
-            a.score[(size_t)bg * a.NC + slot] = a.cs_new[(size_t)bg * a.S + tok];
+            a.score[(size_t)bg * a.NC + slot] = a.cs_new ? a.cs_new[(size_t)bg * a.S + tok] : 0.f;
         }
     }
 }

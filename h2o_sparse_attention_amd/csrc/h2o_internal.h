@@ -35,7 +35,11 @@ struct EvictArgs {
     const float* cs_new;
     int32_t* freed;
     int B, Hkv, D, S, NC, n, W, P, elem_bytes, score_mode;
+    int sink;               // lastrec: slots at positions < sink are never evicted
 };
+
+// Internal ranking mode of the select kernel, beside h2o_score_mode_t.
+constexpr int kModeLastrec = 2;     // rank by position t(j), eligible iff t(j) >= sink
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_attn_bf16(const ChunkArgs& a, hipStream_t s);

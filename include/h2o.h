@@ -112,6 +112,9 @@ H2O_API size_t h2o_workspace_bytes(const h2o_dims_t *dims, int32_t chunk_len);
  *   colsum_new[b,g,i']  = sum_{h in g} sum_i m_{b,h,i,i'}    chunk keys
  * bf16: MFMA inputs are bf16, accumulation and softmax fp32; the weights are
  * rounded to bf16 only for the product with V; summed weights are fp32.
+ * colsum_cache and colsum_new may both be NULL: then only out and lse are
+ * formed and the summed-weights work is skipped (a policy that does not rank
+ * by attention, such as lastrec, needs no more).  Exactly one NULL is an error.
  * Requires 1 <= S, 0 <= n_valid <= N_C, chunk_start >= 0,
  * chunk_start + S <= INT32_MAX, sm_scale finite and > 0.  The cache is read only.
  */
@@ -149,6 +152,27 @@ H2O_API h2o_status_t h2o_evict_and_insert(const h2o_dims_t *dims, h2o_cache_t *c
                                   const void *k_new, const void *v_new,
                                   const float *colsum_new, int32_t *freed_slots,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * lastrec eviction and insertion ("Experimental Validation", the lr policy:
+ * the first beta tokens and the last N_C - beta tokens stay in the cache).
+ * With n = cache->n_valid, P = chunk_start, beta = sink_tokens:
+ *   k = max(0, n + S - N_C) slots are evicted among E = { j < n : t(j) >= beta },
+ *   the k of smallest position t(j) (positions are distinct: no ties);
+ *   targets, insertion, freed_slots and n_valid as in h2o_evict_and_insert,
+ *   except that an inserted slot gets score 0.  dims->recent_window is unused;
+ *   the scores are neither read nor ranked.
+ * Returns H2O_ERR_CAPACITY (nothing launched) when k > 0 and S + beta > N_C:
+ * at most beta distinct cached positions lie below beta, so |E| >= n - beta,
+ * and S + beta <= N_C guarantees |E| >= k.  If the caller breaks the
+ * distinct-position invariant and |E| < k on the device, the shortfall is
+ * taken from the other filled slots in slot order.  Requires sink_tokens >= 0.
+ */
+H2O_API h2o_status_t h2o_evict_and_insert_lastrec(const h2o_dims_t *dims, h2o_cache_t *cache,
+                                          int64_t chunk_start, int32_t chunk_len,
+                                          int32_t sink_tokens, const void *k_new,
+                                          const void *v_new, int32_t *freed_slots,
+                                          void *stream);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 H2O_API const char *h2o_last_error(void);

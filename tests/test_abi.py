@@ -126,6 +126,41 @@ def test_evict_rejects_bad_args():
     assert _evict(_dims(head_dim=32), 10, 8)[0] == _native.H2O_ERR_UNSUPPORTED
 
 
+def _lastrec(dims, n_valid, S, sink, P=1000, freed=FAKE):
+    cache = _native.CacheStruct(FAKE, FAKE, FAKE, FAKE, n_valid)
+    st = h2o.lib.h2o_evict_and_insert_lastrec(ctypes.byref(dims), ctypes.byref(cache), P, S,
+                                              sink, FAKE, FAKE, freed, None)
+    return st, cache.n_valid
+
+
+def test_lastrec_capacity_rule():
+    # full cache, S + beta > N_C: the first beta positions may leave too few eligible slots
+    st, n = _lastrec(_dims(capacity=256, recent_window=0), n_valid=256, S=64, sink=200)
+    assert st == _native.H2O_ERR_CAPACITY and n == 256
+    assert "sink_tokens" in h2o.lib.h2o_last_error().decode()
+    # the recent window plays no part in lastrec: S + W > N_C alone is not refused here
+    # (the call would launch, so only the refusal side is checked on the CPU)
+    st, _ = _lastrec(_dims(capacity=32, recent_window=0), n_valid=0, S=64, sink=0)
+    assert st == _native.H2O_ERR_CAPACITY
+
+
+def test_lastrec_rejects_bad_args():
+    assert _lastrec(_dims(), 10, 8, sink=-1)[0] == _native.H2O_ERR_INVALID_ARG
+    assert _lastrec(_dims(), 10, 8, sink=0, freed=None)[0] == _native.H2O_ERR_INVALID_ARG
+    assert _lastrec(_dims(), 10, 0, sink=0)[0] == _native.H2O_ERR_INVALID_ARG
+    assert _lastrec(_dims(head_dim=32), 10, 8, sink=0)[0] == _native.H2O_ERR_UNSUPPORTED
+
+
+def test_chunk_attn_summed_weights_both_or_neither():
+    d = _dims()
+    cache = _native.CacheStruct(FAKE, FAKE, FAKE, FAKE, 0)
+    for cs_cache, cs_new in ((FAKE, None), (None, FAKE)):
+        st = h2o.lib.h2o_chunk_attn(ctypes.byref(d), ctypes.byref(cache), 0, 64, 0.125, FAKE,
+                                    FAKE, FAKE, FAKE, FAKE, cs_cache, cs_new, None, 0, None)
+        assert st == _native.H2O_ERR_INVALID_ARG
+        assert "colsum" in h2o.lib.h2o_last_error().decode()
+
+
 def test_workspace_bytes_invalid_is_zero():
     assert h2o.lib.h2o_workspace_bytes(None, 1) == 0
     assert h2o.lib.h2o_workspace_bytes(ctypes.byref(_dims(head_dim=3)), 1) == 0
