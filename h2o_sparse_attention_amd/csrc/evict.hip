@@ -166,9 +166,52 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
             }
             return;
         }
-        uint32_t prefix = 0u, mask = 0u;
+        // Skip the leading digits that every candidate for T shares: T lies in
+        // [lo, hi] with lo the smallest key and hi the largest eligible key when
+        // at least k are eligible (else the largest possible key), so digits
+        // where lo and hi agree are T's digits too, and no key lies below them.
+        // Positions (lastrec) share their high bytes: their passes would pile
+        // every key into one histogram bin.
+        uint32_t lo = ~0u, hi = 0u;
+        int elig = 0;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            lo = min(lo, key[e]);
+            const bool is_e = key[e] < kIneligible;
+            hi = is_e ? max(hi, key[e]) : hi;
+            elig += is_e;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+            hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+            elig += __shfl_xor(elig, off);
+        }
+        __shared__ uint32_t sLo[kSelWaves], sHi[kSelWaves];
+        __shared__ int sElig[kSelWaves];
+        if (lane == 0) {
+            sLo[wave] = lo;
+            sHi[wave] = hi;
+            sElig[wave] = elig;
+        }
+        __syncthreads();
+        lo = ~0u;
+        hi = 0u;
+        elig = 0;
+#pragma unroll
+        for (int w = 0; w < kSelWaves; ++w) {
+            lo = min(lo, sLo[w]);
+            hi = max(hi, sHi[w]);
+            elig += sElig[w];
+        }
+        if (elig < k) hi = ~0u;
+        const uint32_t diff = lo ^ hi;
+        // Highest digit where lo and hi differ (-8: none, T == lo).
+        const int top = diff ? ((31 - __clz((int)diff)) & ~7) : -8;
+        uint32_t mask = top >= 24 ? 0u : ~0u << (top + 8);
+        uint32_t prefix = lo & mask;
         int k_rem = k;                        // rank of T among the keys matching prefix
-        for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int shift = top; shift >= 0; shift -= 8) {
             if (tid < 256) sHist[tid] = 0;
             __syncthreads();
 #pragma unroll

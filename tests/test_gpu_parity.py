@@ -120,6 +120,29 @@ def test_evict_isolated_bit_exact(score_mode, seed):
     assert cache.n_valid == st.n
 
 
+@pytest.mark.parametrize("fill", ["all_equal", "two_levels"])
+def test_evict_degenerate_scores(fill):
+    """Every eligible score equal (the k-th key is the smallest key: the radix select runs
+    no pass), or only two distinct values: victims are the lowest-index eligible slots."""
+    wl = W.WORKLOADS[2]
+    s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=5, tie_fraction=0.0)
+    phi = np.full_like(s["phi"], 3.0)
+    if fill == "two_levels":
+        phi[..., 1::3] = 2.0
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], phi, s["n"], s["start"])
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    x = W.chunk_inputs(wl, 0, 20)
+    cs_new = np.ones((wl.batch, wl.n_kv_heads, wl.chunk), np.float32)
+    k, v = H.dev(x["k"], torch.bfloat16), H.dev(x["v"], torch.bfloat16)
+    freed = h2o.evict_and_insert(cache, st.P, k, v, H.dev(cs_new, torch.float32))
+    torch.cuda.synchronize()
+    victims = oracle.select_victims(st, wl.chunk, wl.recent_window)
+    want = oracle.evict_and_insert(st, victims, x["k"], x["v"], cs_new)
+    assert (H.host(freed) == want).all()
+    assert (H.host(cache.pos) == st.pos).all()
+
+
 def test_evict_isolated_large_capacity():
     wl = W.workload(3, capacity=32768, chunk=2048, recent_window=512)
     freed, cache, st, want = _isolated_evict(wl, "h2o", 3)
