@@ -321,7 +321,9 @@ def main():
             "lse": torch.empty(B, Hq, S, dtype=torch.float32, device=dev),
             "colsum_cache": torch.empty(B, Hkv, NC, dtype=torch.float32, device=dev),
             "colsum_new": torch.empty(B, Hkv, S, dtype=torch.float32, device=dev),
-            "freed_slots": torch.empty(B, Hkv, S, dtype=torch.int32, device=dev)}
+            "freed_slots": torch.empty(B, Hkv, S, dtype=torch.int32, device=dev),
+            "workspace": torch.empty(max(1, h2o.workspace_bytes(dims, S)), dtype=torch.uint8,
+                                     device=dev)}
 
     step_kw = dict(policy=args.policy, sink_tokens=args.sink)
     lastrec = args.policy == "lastrec"

@@ -104,6 +104,29 @@ void timer_end(int kernel, hipStream_t s) {
     }
 }
 
+// The S = 1 split-KV specialisation (bf16, d = 128, at most 32 query heads per KV head).
+bool uses_decode(const h2o_dims_t* dims, int32_t chunk_len) {
+    return chunk_len == 1 && dims->dtype == H2O_BF16 && dims->head_dim == 128 &&
+           dims->n_q_heads / dims->n_kv_heads <= 32;
+}
+
+// Compute units of the current device, read once per device.
+hipError_t cu_count(int* cus) {
+    static int cached[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cached[dev] == 0) {
+        int v = 0;
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        cached[dev] = v > 0 ? v : 1;
+    }
+    *cus = cached[dev];
+    return hipSuccess;
+}
+
 // Shared body of the two eviction entry points.  mode: h2o_score_mode_t, or
 // kModeLastrec with `sink` protected leading positions (then colsum_new is NULL).
 h2o_status_t evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_t chunk_start,
@@ -168,10 +191,11 @@ const char* h2o_last_error(void) { return g_error.c_str(); }
 
 size_t h2o_workspace_bytes(const h2o_dims_t* dims, int32_t chunk_len) {
     if (validate_dims(dims) != H2O_OK || chunk_len < 1) return 0;
-    if (chunk_len == 1 && dims->dtype == H2O_BF16 && dims->head_dim == 128 &&
-        dims->n_q_heads / dims->n_kv_heads <= 32)
+    if (uses_decode(dims, chunk_len))
         return decode_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads,
                                       dims->capacity);
+    if (dims->dtype == H2O_BF16)
+        return colsum_workspace_bytes(dims->batch, dims->n_kv_heads, dims->capacity, chunk_len);
     return 0;
 }
 
@@ -198,7 +222,9 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
             return fail(H2O_ERR_UNSUPPORTED, "query heads per KV head (%lld) too large for chunk_len %d",
                         G, chunk_len);
     }
-    const size_t ws_need = h2o_workspace_bytes(dims, chunk_len);
+    const bool decode = uses_decode(dims, chunk_len);
+    // Without summed weights only the decode path uses the workspace.
+    const size_t ws_need = (decode || want_cs) ? h2o_workspace_bytes(dims, chunk_len) : 0;
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
         return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", ws_need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -227,24 +253,32 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int rows = a.B * a.Hkv;
 
-    if (want_cs && a.n < a.NC) {
+    const bool bf16 = dims->dtype == H2O_BF16;
+    int parts = 1;
+    if (want_cs && bf16 && !decode) {
+        int cus = 0;
+        if ((st = check_hip(cu_count(&cus), "device attributes")) != H2O_OK) return st;
+        parts = colsum_parts(a, cus);
+    }
+    // The reduction of a split colsum writes the empty slots itself.
+    if (want_cs && parts == 1 && a.n < a.NC) {
         if ((st = check_hip(launch_zero_f32(colsum_cache, a.NC - a.n, a.NC, rows, a.n, s),
                             "zero colsum tail")) != H2O_OK)
             return st;
     }
-    if (ws_need > 0) {
+    if (decode) {
         hipError_t e = launch_decode(a, workspace, s);     // times its two kernels
         if ((st = check_hip(e, "decode attention launch")) != H2O_OK) return st;
         return ok();
     }
-    const bool bf16 = dims->dtype == H2O_BF16;
     timer_begin(H2O_KERNEL_ATTN, s);
     hipError_t e = bf16 ? launch_attn_bf16(a, s) : launch_attn_f32(a, s);
     timer_end(H2O_KERNEL_ATTN, s);
     if ((st = check_hip(e, "attention launch")) != H2O_OK) return st;
     if (!want_cs) return ok();
     timer_begin(H2O_KERNEL_COLSUM, s);
-    e = bf16 ? launch_colsum_bf16(a, s) : launch_colsum_f32(a, s);
+    e = bf16 ? launch_colsum_bf16(a, parts, static_cast<float*>(workspace), s)
+             : launch_colsum_f32(a, s);
     timer_end(H2O_KERNEL_COLSUM, s);
     if ((st = check_hip(e, "colsum launch")) != H2O_OK) return st;
     return ok();

@@ -40,6 +40,7 @@ constexpr int kRowsPerBlock = 32 * kWaves;   // attention pass: 32 query rows pe
 constexpr int kKeysPerTile = 64;             // attention pass: keys staged per step
 constexpr int kKeysPerBlock = 32 * kWaves;   // colsum pass: 32 keys per wave
 constexpr int kRowsPerTile = 64;             // colsum pass: query rows staged per step
+constexpr int kColsumMaxParts = 4;           // colsum pass: row ranges per key block
 
 // ---------------------------------------------------------------------------
 // Key tiles.  The filled cache slots form ceil(n/64) tiles (the last one may be
@@ -468,7 +469,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 // are visible to every row; a chunk key is visible to the rows at or after its
 // own position, which only blocks near the diagonal have to test.
 //
-// Pipeline, per row tile rt (stage buffer (rt - tile0) & 1):
+// Load balance: a key block's work is every row tile after its first visible
+// one; with few blocks per CU, whole blocks leave CUs idle at the end (576
+// blocks on 768 resident slots at chunk 1k / 8192 slots).  The row tiles are
+// then split into `parts` contiguous ranges, one workgroup each, whose fp32
+// partial sums go to the workspace and are added in part order by
+// colsum_reduce_kernel, so the result does not depend on timing.
+//
+// Pipeline, per row tile rt (stage buffer (rt - t_lo) & 1):
 //   A: MFMAs of sub-tile 1 of tile rt, exponentials of sub-tile 0 of tile rt;
 //   barrier (tile rt+1 has landed; tile rt's buffer is free);
 //   B: start the loads of tile rt+2; MFMAs of sub-tile 0 of tile rt+1,
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 template <int D, bool EVEN_ROWS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
-void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
+void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restrict__ part_ws) {
     constexpr int KS = D / 16;
     constexpr int RB = 2 * D;                          // bytes per Q row
     constexpr int QT = kRowsPerTile * RB;              // bytes per Q tile
@@ -491,10 +499,11 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
     const int n = a.n, S = a.S, G = a.G;
     const int cache_blocks = (n + kKeysPerBlock - 1) / kKeysPerBlock;
     const int nkb = cache_blocks + (S + kKeysPerBlock - 1) / kKeysPerBlock;
-    const int total = nkb * a.B * a.Hkv;
+    const int total = nkb * a.B * a.Hkv * parts;
     const int t = xcd_tile(blockIdx.x, total);
     if (t >= total) return;
-    const int bg = t / nkb, kb = t % nkb;
+    // Consecutive tiles: key blocks of one (b, g, part), which read the same Q rows.
+    const int kb = t % nkb, part = (t / nkb) % parts, bg = t / nkb / parts;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const bool is_cache = kb < cache_blocks;
     const int block_first = (is_cache ? kb : kb - cache_blocks) * kKeysPerBlock;
@@ -523,6 +532,17 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
     const int ntile = (R + kRowsPerTile - 1) / kRowsPerTile;
     // Chunk keys are invisible to the rows before their own position.
     const int tile0 = is_cache ? 0 : (block_first * G) / kRowsPerTile;
+    // This workgroup's row tiles [t_lo, t_hi).
+    const int per_part = (ntile + parts - 1) / parts;
+    const int t_lo = max(tile0, part * per_part), t_hi = min(ntile, (part + 1) * per_part);
+    // Where this wave's 32 sums go: the output, or this part's workspace row.
+    float* dst = parts == 1
+        ? (is_cache ? a.cs_cache + (size_t)bg * a.NC : a.cs_new + (size_t)bg * S)
+        : part_ws + ((size_t)part * a.B * a.Hkv + bg) * (a.NC + S) + (is_cache ? 0 : a.NC);
+    if (t_lo >= t_hi) {                    // no visible row in this range
+        if (lane < 32 && first + lane < limit) dst[first + lane] = 0.f;
+        return;
+    }
 
     // The G query heads of KV head g are contiguous in Q and in LSE.
     const u16* Qg = static_cast<const u16*>(a.q) + (size_t)(b * a.Hq + g * G) * S * D;
@@ -653,34 +673,34 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
         return r;
     };
 
-    // Prologue: tiles tile0 and tile0+1; S of (tile0, sub 0).
-    issue(sQ0, sL0, tile0);
-    if (tile0 + 1 < ntile) issue(sQ1, sL1, tile0 + 1);
+    // Prologue: tiles t_lo and t_lo+1; S of (t_lo, sub 0).
+    issue(sQ0, sL0, t_lo);
+    if (t_lo + 1 < t_hi) issue(sQ1, sL1, t_lo + 1);
     publish_lds_loads();
     f32x16 s0 = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) s0 = mfma32(kf[ks], qread(sQ0, 0, ks), s0);
 
     auto step = [&](auto odd_c, int rt) {
-        constexpr bool odd = decltype(odd_c)::value;      // (rt - tile0) & 1
+        constexpr bool odd = decltype(odd_c)::value;      // (rt - t_lo) & 1
         unsigned char* qc = odd ? sQ1 : sQ0;              // tile rt
         unsigned char* qn = odd ? sQ0 : sQ1;              // tile rt+1
         float* lc = odd ? sL1 : sL0;
         float* ln = odd ? sL0 : sL1;
-        const bool has_next = rt + 1 < ntile;
+        const bool has_next = rt + 1 < t_hi;
         const float l0 = lse2_of(lc, rt, 0), l1 = lse2_of(lc, rt, 1);
         // A: MFMAs of (rt, 1) with the exponentials of (rt, 0).
         const f32x16 s1 = stage(qc, 1, s0, l0, full_tile(rt, 0), rt, 0, true);
         publish_lds_loads();
         // B: loads of tile rt+2 into tile rt's buffer; MFMAs of (rt+1, 0) with
         // the exponentials of (rt, 1).
-        if (rt + 2 < ntile) issue(qc, lc, rt + 2);
+        if (rt + 2 < t_hi) issue(qc, lc, rt + 2);
         s0 = stage(qn, 0, s1, l1, full_tile(rt, 1), rt, 1, has_next);
         (void)ln;
     };
-    for (int rt = tile0; rt < ntile; rt += 2) {
+    for (int rt = t_lo; rt < t_hi; rt += 2) {
         step(std::false_type{}, rt);
-        if (rt + 1 < ntile) step(std::true_type{}, rt + 1);
+        if (rt + 1 < t_hi) step(std::true_type{}, rt + 1);
     }
     publish_lds_loads();
 
@@ -692,10 +712,27 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic) {
 #pragma unroll 8
         for (int j = 0; j < 32; ++j) sum += sRed[wave][lane][j];
         const int idx = first + lane;
-        if (idx < limit) {
-            if (is_cache) a.cs_cache[(size_t)bg * a.NC + idx] = sum;
-            else a.cs_new[(size_t)bg * S + idx] = sum;
+        if (idx < limit) dst[idx] = sum;
+    }
+}
+
+// Sum of the parts' partial column sums, in part order; zero for the empty
+// slots [n, N_C).  One (b, kv head) row of N_C + S entries per blockIdx.y.
+__global__ __launch_bounds__(256) void colsum_reduce_kernel(ChunkArgs a, int parts,
+                                                            const float* __restrict__ part_ws) {
+    const int bg = blockIdx.y;
+    const int row = a.NC + a.S;
+    const size_t part_stride = (size_t)a.B * a.Hkv * row;
+    const float* src = part_ws + (size_t)bg * row;
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < row; j += gridDim.x * blockDim.x) {
+        const bool empty = j >= a.n && j < a.NC;
+        float sum = 0.f;
+        if (!empty) {
+            sum = src[j];
+            for (int p = 1; p < parts; ++p) sum += src[p * part_stride + j];
         }
+        if (j < a.NC) a.cs_cache[(size_t)bg * a.NC + j] = sum;
+        else a.cs_new[(size_t)bg * a.S + (j - a.NC)] = sum;
     }
 }
 
@@ -713,21 +750,51 @@ hipError_t launch_attn_bf16(const ChunkArgs& a, hipStream_t s) {
     return a.D == 128 ? launch_attn_d<128>(a, s) : launch_attn_d<64>(a, s);
 }
 
-hipError_t launch_colsum_bf16(const ChunkArgs& a, hipStream_t s) {
+size_t colsum_workspace_bytes(int B, int Hkv, int NC, int S) {
+    return (size_t)kColsumMaxParts * B * Hkv * (NC + S) * sizeof(float);
+}
+
+int colsum_parts(const ChunkArgs& a, int cus) {
+    // Key blocks as whole units of work; 3 workgroups fit on a CU.  Take the
+    // split that needs the fewest rounds of resident workgroups, counted in
+    // whole-block units (ties: the smaller split).
+    const long long units = (long long)((a.n + kKeysPerBlock - 1) / kKeysPerBlock +
+                                        (a.S + kKeysPerBlock - 1) / kKeysPerBlock) * a.B * a.Hkv;
+    const long long slots = 3LL * cus;
+    int best = 1;
+    double best_t = 1e30;
+    for (int p = 1; p <= kColsumMaxParts; p *= 2) {
+        const double rounds = (double)((units * p + slots - 1) / slots) / p;
+        if (rounds < best_t - 1e-9) {
+            best_t = rounds;
+            best = p;
+        }
+    }
+    return best;
+}
+
+hipError_t launch_colsum_bf16(const ChunkArgs& a, int parts, float* part_ws, hipStream_t s) {
     const int blocks = (a.n + kKeysPerBlock - 1) / kKeysPerBlock +
                        (a.S + kKeysPerBlock - 1) / kKeysPerBlock;
-    const int total = blocks * a.B * a.Hkv;
+    const int total = blocks * a.B * a.Hkv * parts;
     // floor(r / G) = umulhi(r, ceil(2^32 / G)) for r * G < 2^32 (checked by the caller)
     const uint32_t magic = a.G > 1 ? (uint32_t)((0x100000000ull + a.G - 1) / a.G) : 0u;
     const dim3 grid(xcd_grid(total)), block(kThreads);
     const bool even = kRowsPerTile % a.G == 0;
     if (a.D == 128) {
-        if (even) hipLaunchKernelGGL((colsum_bf16_kernel<128, true>), grid, block, 0, s, a, magic);
-        else hipLaunchKernelGGL((colsum_bf16_kernel<128, false>), grid, block, 0, s, a, magic);
+        if (even) hipLaunchKernelGGL((colsum_bf16_kernel<128, true>), grid, block, 0, s, a, magic, parts, part_ws);
+        else hipLaunchKernelGGL((colsum_bf16_kernel<128, false>), grid, block, 0, s, a, magic, parts, part_ws);
     } else {
-        if (even) hipLaunchKernelGGL((colsum_bf16_kernel<64, true>), grid, block, 0, s, a, magic);
-        else hipLaunchKernelGGL((colsum_bf16_kernel<64, false>), grid, block, 0, s, a, magic);
+        if (even) hipLaunchKernelGGL((colsum_bf16_kernel<64, true>), grid, block, 0, s, a, magic, parts, part_ws);
+        else hipLaunchKernelGGL((colsum_bf16_kernel<64, false>), grid, block, 0, s, a, magic, parts, part_ws);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || parts == 1) return e;
+    const int row = a.NC + a.S;
+    int bx = (row + 1023) / 1024;
+    if (bx > 64) bx = 64;
+    hipLaunchKernelGGL(colsum_reduce_kernel, dim3(bx, a.B * a.Hkv), dim3(256), 0, s, a, parts,
+                       part_ws);
     return hipGetLastError();
 }
 

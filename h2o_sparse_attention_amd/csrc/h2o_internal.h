@@ -43,7 +43,11 @@ constexpr int kModeLastrec = 2;     // rank by position t(j), eligible iff t(j) 
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_attn_bf16(const ChunkArgs& a, hipStream_t s);
-hipError_t launch_colsum_bf16(const ChunkArgs& a, hipStream_t s);
+// bf16 summed weights: `parts` row ranges per key block (1: written straight to
+// the outputs; else partial sums in part_ws, then a reduction launch).
+size_t colsum_workspace_bytes(int B, int Hkv, int NC, int S);
+int colsum_parts(const ChunkArgs& a, int cus);
+hipError_t launch_colsum_bf16(const ChunkArgs& a, int parts, float* part_ws, hipStream_t s);
 hipError_t launch_attn_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_colsum_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_zero_f32(float* p, size_t count_per_row, size_t row_stride, int rows,

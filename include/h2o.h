@@ -93,7 +93,11 @@ typedef struct {
     int32_t  n_valid;
 } h2o_cache_t;
 
-/* Bytes of workspace h2o_chunk_attn needs for this chunk length (0 = none). */
+/* Bytes of workspace h2o_chunk_attn needs for this chunk length (0 = none): the
+ * split-over-slots partial results of the S = 1 path (bf16, d = 128, at most 32
+ * query heads per KV head), or, for other bf16 chunks, partial summed weights
+ * (4 * B * Hkv * (N_C + S) floats; not needed when no summed weights are asked
+ * for).  The contents need no initialisation and are not preserved. */
 H2O_API size_t h2o_workspace_bytes(const h2o_dims_t *dims, int32_t chunk_len);
 
 /*
