@@ -189,20 +189,10 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
                 if (!(kpv >= 0 && kpv <= qpos)) s[r] = -INFINITY;
             }
         }
-        if (want_logits && lq < G) {
-            const int k0 = k_begin + sub * kDecSub;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                float4 w0, w1;
-                w0.x = s[8 * half + 0] * c; w0.y = s[8 * half + 1] * c;
-                w0.z = s[8 * half + 2] * c; w0.w = s[8 * half + 3] * c;
-                w1.x = s[8 * half + 4] * c; w1.y = s[8 * half + 5] * c;
-                w1.z = s[8 * half + 6] * c; w1.w = s[8 * half + 7] * c;
-                float* dst = logit_row + k0 + 16 * half + 8 * hh;
-                *reinterpret_cast<float4*>(dst) = w0;
-                *reinterpret_cast<float4*>(dst + 4) = w1;
-            }
-        }
+        // The logits are stored after this iteration's wait for the next tile:
+        // vmcnt counts stores too, so stores issued before that wait would be
+        // waited for as well.
+        const f32x16 s_log = s;
         float mt = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
@@ -247,6 +237,20 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
                 o[dt] = mfma32(as_bf16x8(av), pb[s2], o[dt]);
             }
         if (next < nsub) lstore();
+        if (want_logits && lq < G) {
+            const int k0 = k_begin + sub * kDecSub;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float4 w0, w1;
+                w0.x = s_log[8 * half + 0] * c; w0.y = s_log[8 * half + 1] * c;
+                w0.z = s_log[8 * half + 2] * c; w0.w = s_log[8 * half + 3] * c;
+                w1.x = s_log[8 * half + 4] * c; w1.y = s_log[8 * half + 5] * c;
+                w1.z = s_log[8 * half + 6] * c; w1.w = s_log[8 * half + 7] * c;
+                float* dst = logit_row + k0 + 16 * half + 8 * hh;
+                *reinterpret_cast<float4*>(dst) = w0;
+                *reinterpret_cast<float4*>(dst + 4) = w1;
+            }
+        }
     }
 
     // Merge the four waves' states, then write this split's partial.
