@@ -334,6 +334,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
         if (!tile_all_visible(0)) apply_mask(sA, tile_lim(0));
         mc = rescale_for(rowmax(sA));
     }
+    // Iteration 0 loads K(2) into K(0)'s buffer: every wave must be done
+    // reading K(0) first.  (The reads have completed once their MFMAs issued.)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 
     // Iteration jt: S(jt) is masked and mc is its exponent offset; K stage
     // jt&1 is free (K(jt) was consumed), K stage (jt+1)&1 holds K(jt+1), V
