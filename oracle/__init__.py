@@ -16,7 +16,9 @@ replay on tiny caches, and conservation / invariance properties.
 """
 from .h2o_oracle import (  # noqa: F401
     H2OState,
+    attend_buffer,
     attend_chunk,
+    buffer_step,
     evict_and_insert,
     h2o_step,
     lastrec_step,

@@ -30,7 +30,11 @@ Readings taken where the pages are silent or garbled:
 * h2o-norm divides the score by the age t - t(j) with t = P + S, in float32;
 * lastrec ("Experimental Validation", the lr policy: the first beta and the
   last N_C - beta tokens stay) evicts the k oldest filled slots whose position
-  is at least beta, and refuses a chunk when fewer are eligible.
+  is at least beta, and refuses a chunk when fewer are eligible;
+* the insert-first buffer form (the positional mask of "Kernel Support Needs"
+  over the fixed-size buffer) chooses the victims on the scores before the
+  chunk, writes the chunk with score 0, then attends over the N_C slots; the
+  new tokens' scores are then their own summed weights, as in the other order.
 """
 from __future__ import annotations
 
@@ -243,4 +247,57 @@ def lastrec_step(state: H2OState, q, k_new, v_new, sm_scale: float, beta: int):
     freed = evict_and_insert(state, victims, np.asarray(k_new, np.float64),
                              np.asarray(v_new, np.float64), np.zeros(np.shape(cs_new)))
     return {"out": out, "lse": lse, "victims": victims, "freed_slots": freed}
+
+
+# ------------------------------------------------------------ insert-first buffer form
+def attend_buffer(state: H2OState, q, P: int, sm_scale: float):
+    """Chunk attention over the slot buffer alone, the chunk already written into it.
+
+    Query row i sits at position P + i and sees slot j iff 0 <= t(j) <= P + i
+    (the positional mask over the fixed-size buffer, "Kernel Support Needs").
+    Returns O, lse and the summed weights per slot (B, Hkv, N_C), zero beyond n.
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, S, d = q.shape
+    Hkv = state.K.shape[1]
+    G = Hq // Hkv
+    n, NC = state.n, state.capacity
+    out = np.zeros((B, Hq, S, d))
+    lse = np.zeros((B, Hq, S))
+    colsum = np.zeros((B, Hkv, NC))
+    q_pos = P + np.arange(S)
+    for b in range(B):
+        for g in range(Hkv):
+            keys, values, t = state.K[b, g, :n], state.V[b, g, :n], state.pos[b, g, :n]
+            visible = (t[None, :] >= 0) & (t[None, :] <= q_pos[:, None])
+            for hh in range(G):
+                h = g * G + hh
+                s = np.where(visible, sm_scale * (q[b, h] @ keys.T), -np.inf)
+                row_max = s.max(axis=1, keepdims=True)
+                e = np.exp(s - row_max)
+                row_sum = e.sum(axis=1, keepdims=True)
+                m = e / row_sum
+                out[b, h] = m @ values
+                lse[b, h] = row_max[:, 0] + np.log(row_sum[:, 0])
+                colsum[b, g, :n] += m.sum(axis=0)
+    return out, lse, colsum
+
+
+def buffer_step(state: H2OState, q, k_new, v_new, sm_scale: float, W: int,
+                score_mode: str = "h2o"):
+    """One chunk in the insert-first buffer form: the victims are chosen on the
+    scores before the chunk, the chunk is written into the targets with score 0,
+    the chunk attends over the N_C-slot buffer under the positional mask, and
+    every filled slot's score accumulates its summed weight.  Mutates ``state``."""
+    B, Hkv, S, _ = np.shape(k_new)
+    P = state.P
+    victims = select_victims(state, S, W, score_mode)
+    evicted_phi = np.take_along_axis(state.phi, victims, axis=2) if victims.size else \
+        np.zeros(victims.shape)
+    freed = evict_and_insert(state, victims, np.asarray(k_new, np.float64),
+                             np.asarray(v_new, np.float64), np.zeros((B, Hkv, S)))
+    out, lse, colsum = attend_buffer(state, q, P, sm_scale)
+    update_scores(state, colsum)
+    return {"out": out, "lse": lse, "colsum": colsum, "victims": victims,
+            "evicted_phi": evicted_phi, "freed_slots": freed}
 

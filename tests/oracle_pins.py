@@ -396,8 +396,75 @@ def check_lastrec_capacity_error(orc):
     raise AssertionError("lastrec accepted more victims than eligible slots")
 
 
+def check_buffer_without_eviction_is_attend_first(orc, seed=11):
+    """While nothing is evicted the two orders see the same keys: the buffer form gives
+    the outputs, log-sum-exps, positions and scores of the attend-first step."""
+    q, k, v = random_problem(seed, N=30)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    a = orc.H2OState.empty(B, Hkv, 32, d)
+    b = orc.H2OState.empty(B, Hkv, 32, d)
+    for c0 in range(0, N, 7):
+        x = (q[:, :, c0:c0 + 7], k[:, :, c0:c0 + 7], v[:, :, c0:c0 + 7])
+        ra = orc.h2o_step(a, *x, 0.5, 3)
+        rb = orc.buffer_step(b, *x, 0.5, 3)
+        np.testing.assert_allclose(rb["out"], ra["out"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(rb["lse"], ra["lse"], rtol=0, atol=1e-12)
+        assert (a.pos == b.pos).all()
+        np.testing.assert_allclose(b.phi, a.phi, rtol=1e-12, atol=1e-15)
+
+
+def check_buffer_dense_replay(orc, seed=12):
+    """Replay the buffer form over the full token history: every chunk recomputed with
+    torch's fp64 SDPA under a mask built only from the freed-slot log (the resident tokens
+    after insertion, causal by position) must give the slot-based outputs, and scores
+    rebuilt from those weights -- before the chunk -- must pick the same victims."""
+    B, Hq, Hkv, d, N = 1, 4, 2, 8, 44
+    S, NC, W, sm = 4, 12, 2, 0.8
+    G = Hq // Hkv
+    q, k, v = random_problem(seed, B=B, Hq=Hq, Hkv=Hkv, d=d, N=N)
+    st = orc.H2OState.empty(B, Hkv, NC, d)
+    slot_tok = np.full((B, Hkv, NC), -1)
+    phi_tok = np.zeros((B, Hkv, N))
+    for c0 in range(0, N, S):
+        c1 = min(N, c0 + S)
+        res = orc.buffer_step(st, q[:, :, c0:c1], k[:, :, c0:c1], v[:, :, c0:c1], sm, W)
+        for b in range(B):
+            for g in range(Hkv):
+                n_before = int((slot_tok[b, g] >= 0).sum())
+                kk = max(0, n_before + (c1 - c0) - NC)
+                elig = [j for j in range(n_before) if slot_tok[b, g, j] < c0 - W]
+                order = sorted(elig, key=lambda j: (phi_tok[b, g, slot_tok[b, g, j]], j))
+                assert sorted(order[:kk]) == res["victims"][b, g].tolist()
+                targets = sorted(order[:kk] + list(range(n_before, min(NC, n_before + c1 - c0))))
+                assert res["freed_slots"][b, g].tolist() == targets
+                for i, j in enumerate(targets):
+                    slot_tok[b, g, j] = c0 + i
+                keys = [int(t) for t in slot_tok[b, g] if t >= 0]
+                mask = torch.from_numpy(np.array(keys)[None, :] <= np.arange(c0, c1)[:, None])
+                for hh in range(G):
+                    h = g * G + hh
+                    qt = torch.from_numpy(q[b, h, c0:c1])
+                    kt = torch.from_numpy(k[b, g, keys])
+                    want = torch.nn.functional.scaled_dot_product_attention(
+                        qt, kt, torch.from_numpy(v[b, g, keys]), attn_mask=mask, scale=sm).numpy()
+                    np.testing.assert_allclose(res["out"][b, h], want, rtol=0, atol=1e-12)
+                    w = torch.nn.functional.scaled_dot_product_attention(
+                        qt, kt, torch.eye(len(keys), dtype=torch.float64), attn_mask=mask,
+                        scale=sm).numpy()
+                    for t, cs in zip(keys, w.sum(axis=0)):
+                        phi_tok[b, g, t] += cs
+    for b in range(B):
+        for g in range(Hkv):
+            for j in range(NC):
+                if slot_tok[b, g, j] >= 0:
+                    np.testing.assert_allclose(st.phi[b, g, j], phi_tok[b, g, slot_tok[b, g, j]],
+                                               rtol=1e-12, atol=1e-15)
+
+
 ALL_CHECKS = [check_golden, check_rows_normalised, check_exact_when_no_eviction,
               check_chunk_size_invariance, check_uniform_closed_form,
               check_bruteforce_selection, check_decode_is_argmin, check_dense_masked_replay,
               check_conservation_and_monotonicity, check_slot_permutation_invariance,
-              check_lastrec_closed_form, check_lastrec_capacity_error]
+              check_lastrec_closed_form, check_lastrec_capacity_error,
+              check_buffer_without_eviction_is_attend_first, check_buffer_dense_replay]

@@ -43,6 +43,13 @@ MUTANTS = [
     ("t_now = state.P + S", "t_now = state.P", "h2o-norm age off by S"),
     ("state.pos[b, g, :n] >= beta", "state.pos[b, g, :n] > beta", "lastrec sink off by one"),
     ("np.sort(eligible[oldest[:k]])", "np.sort(eligible[oldest[-k:]])", "lastrec evicts newest"),
+    ("    update_scores(state, colsum)\n", "    update_scores(state, colsum * 0.5)\n",
+     "buffer form halves the scores"),
+    ("np.asarray(v_new, np.float64), np.zeros((B, Hkv, S)))",
+     "np.asarray(v_new, np.float64), np.ones((B, Hkv, S)))", "buffer form new score not zero"),
+    ("            keys, values, t = state.K[b, g, :n], state.V[b, g, :n], state.pos[b, g, :n]",
+     "            keys, values, t = state.K[b, g, :n], state.V[b, g, :n], state.pos[b, g, :n] - 1",
+     "buffer mask off by one"),
 ]
 
 
