@@ -117,6 +117,9 @@ def copy_probe(mib: int) -> None:
 DECODE_METRIC = "H2O decode step (attn+score+evict) tokens/s, % HBM roofline"
 LASTREC_METRIC = "lastrec chunk-attn+evict TFLOP/s & tokens/s (chunk 1k, 64k ctx), % roofline"
 LASTREC_DECODE_METRIC = "lastrec decode step (attn+evict) tokens/s, % HBM roofline"
+BUFFER_METRIC = ("H2O insert-first buffer chunk-attn+score+evict TFLOP/s & tokens/s "
+                 "(chunk 1k, 64k ctx), % roofline")
+BUFFER_DECODE_METRIC = "H2O insert-first buffer decode step tokens/s, % HBM roofline"
 
 
 def decode_slot_bytes(wl, policy="h2o") -> int:
@@ -246,7 +249,8 @@ def run_decode(args):
     kv_bytes = B * Hkv * NC * 2 * D * 2            # K and V rows read by the attention launch
     achieved = kv_bytes / (dec.mean_ms * 1e-3) / 1e9
     line = {
-        "metric": DECODE_METRIC if args.policy == "h2o" else LASTREC_DECODE_METRIC,
+        "metric": {"h2o": DECODE_METRIC, "h2o_buffer": BUFFER_DECODE_METRIC,
+                   "lastrec": LASTREC_DECODE_METRIC}[args.policy],
         "value": round(n_tok / total_s, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(total_s / args.steps * 1e3, 3), "higher_is_better": True,
@@ -284,7 +288,9 @@ def main():
                     help="time eager launches instead of replaying a captured HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run plain copies of this size first (HBM counter calibration)")
-    ap.add_argument("--policy", choices=("h2o", "lastrec"), default="h2o")
+    ap.add_argument("--policy", choices=("h2o", "h2o_buffer", "lastrec"), default="h2o",
+                    help="h2o: attend, then evict; h2o_buffer: the insert-first buffer form; "
+                         "lastrec: keep the first --sink and the most recent tokens")
     ap.add_argument("--sink", type=int, default=64,
                     help="lastrec: leading tokens kept (beta); the pages give no value")
     args = ap.parse_args()
@@ -380,7 +386,12 @@ def main():
             print(f"[bench] WARNING: summed weights {total} != {expect}", file=sys.stderr)
 
     sched = chunk_schedule(wl)
-    pairs = sum(pairs_per_head(n, S) for n in sched)
+    # keys per row: the filled slots (minus those the buffer form overwrites first)
+    # and the chunk's own causal keys
+    if args.policy == "h2o_buffer":
+        pairs = sum(pairs_per_head(n - max(0, n + S - NC), S) for n in sched)
+    else:
+        pairs = sum(pairs_per_head(n, S) for n in sched)
     f6 = 6.0 * D * Hq * B * pairs
     f4 = 4.0 * D * Hq * B * pairs
     tflops = (f4 if lastrec else f6) / (ms_per_step * 1e-3) / 1e12
@@ -399,12 +410,13 @@ def main():
     steady_n = [i for i, n in enumerate(sched) if n == NC]
 
     cpu = None
-    if args.cpu_budget > 0 and not lastrec:
+    if args.cpu_budget > 0 and args.policy == "h2o":
         print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, args.cpu_budget)
 
     line = {
-        "metric": LASTREC_METRIC if lastrec else METRIC, "value": round(tflops, 3),
+        "metric": LASTREC_METRIC if lastrec else (BUFFER_METRIC if args.policy == "h2o_buffer"
+                                                  else METRIC), "value": round(tflops, 3),
         "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

@@ -170,6 +170,85 @@ def evict_and_insert(cache: H2OCache, chunk_start: int, k_new, v_new, colsum_new
     return freed_slots
 
 
+def select_slots(cache: H2OCache, chunk_start: int, chunk_len: int, freed_slots=None,
+                 score_mode="h2o", stream=None):
+    """h2o_select_slots: the chunk's targets [B,Hkv,S] from the current scores; the cache
+    is not modified."""
+    d = cache.dims
+    dev = cache.k.device
+    if freed_slots is None:
+        freed_slots = torch.empty(d.batch, d.n_kv_heads, chunk_len, dtype=torch.int32,
+                                  device=dev)
+    _need(freed_slots, (d.batch, d.n_kv_heads, chunk_len), torch.int32, "freed_slots")
+    check(lib.h2o_select_slots(ctypes.byref(d.c()), ctypes.byref(cache.c()), int(chunk_start),
+                               int(chunk_len), SCORE_MODES[score_mode], freed_slots.data_ptr(),
+                               _stream_ptr(stream, dev)))
+    return freed_slots
+
+
+def buffer_attn(cache: H2OCache, chunk_start: int, q, k_new, v_new, freed_slots,
+                sm_scale: float, out=None, lse=None, colsum_cache=None, colsum_new=None,
+                workspace=None, stream=None, summed_weights=True):
+    """h2o_buffer_attn: returns (out, lse, colsum_cache, colsum_new); the targets below
+    n_valid in freed_slots are not keys."""
+    d = cache.dims
+    B, Hq, Hkv, D, NC = d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim, d.capacity
+    S = q.shape[2]
+    dev = cache.k.device
+    _need(q, (B, Hq, S, D), d.torch_dtype, "q")
+    _need(k_new, (B, Hkv, S, D), d.torch_dtype, "k_new")
+    _need(v_new, (B, Hkv, S, D), d.torch_dtype, "v_new")
+    _need(freed_slots, (B, Hkv, S), torch.int32, "freed_slots")
+    if out is None:
+        out = torch.empty(B, Hq, S, D, dtype=d.torch_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(B, Hq, S, dtype=torch.float32, device=dev)
+    _need(out, (B, Hq, S, D), d.torch_dtype, "out")
+    _need(lse, (B, Hq, S), torch.float32, "lse")
+    if summed_weights:
+        if colsum_cache is None:
+            colsum_cache = torch.empty(B, Hkv, NC, dtype=torch.float32, device=dev)
+        if colsum_new is None:
+            colsum_new = torch.empty(B, Hkv, S, dtype=torch.float32, device=dev)
+        _need(colsum_cache, (B, Hkv, NC), torch.float32, "colsum_cache")
+        _need(colsum_new, (B, Hkv, S), torch.float32, "colsum_new")
+        cs_ptrs = (colsum_cache.data_ptr(), colsum_new.data_ptr())
+    else:
+        colsum_cache = colsum_new = None
+        cs_ptrs = (None, None)
+    ws_need = workspace_bytes(d, S)
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.h2o_buffer_attn(ctypes.byref(d.c()), ctypes.byref(cache.c()), int(chunk_start), S,
+                              float(sm_scale), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                              freed_slots.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              cs_ptrs[0], cs_ptrs[1], ws_ptr, ws_len, _stream_ptr(stream, dev)))
+    return out, lse, colsum_cache, colsum_new
+
+
+def insert(cache: H2OCache, chunk_start: int, k_new, v_new, freed_slots, colsum_new=None,
+           stream=None):
+    """h2o_insert: chunk token i into freed_slots[..., i] (score colsum_new, or 0)."""
+    d = cache.dims
+    B, Hkv, D = d.batch, d.n_kv_heads, d.head_dim
+    S = k_new.shape[2]
+    dev = cache.k.device
+    _need(k_new, (B, Hkv, S, D), d.torch_dtype, "k_new")
+    _need(v_new, (B, Hkv, S, D), d.torch_dtype, "v_new")
+    _need(freed_slots, (B, Hkv, S), torch.int32, "freed_slots")
+    if colsum_new is not None:
+        _need(colsum_new, (B, Hkv, S), torch.float32, "colsum_new")
+    cs = cache.c()
+    check(lib.h2o_insert(ctypes.byref(d.c()), ctypes.byref(cs), int(chunk_start), S,
+                         k_new.data_ptr(), v_new.data_ptr(),
+                         colsum_new.data_ptr() if colsum_new is not None else None,
+                         freed_slots.data_ptr(), _stream_ptr(stream, dev)))
+    cache.n_valid = cs.n_valid
+    cache.next_pos = int(chunk_start) + S
+
+
 def evict_and_insert_lastrec(cache: H2OCache, chunk_start: int, k_new, v_new, sink_tokens: int,
                              freed_slots=None, stream=None):
     """h2o_evict_and_insert_lastrec: returns freed_slots [B,Hkv,S], advances cache.n_valid."""
@@ -195,11 +274,24 @@ def evict_and_insert_lastrec(cache: H2OCache, chunk_start: int, k_new, v_new, si
 def step(cache: H2OCache, q, k_new, v_new, sm_scale: float, score_mode="h2o", bufs=None,
          stream=None, policy="h2o", sink_tokens=0):
     """One chunk at position cache.next_pos.  policy "h2o": attention with summed weights,
-    score update, eviction by ``score_mode``.  policy "lastrec": attention alone, then
-    eviction by position keeping the first ``sink_tokens``.  ``bufs`` (a dict holding out,
-    lse, colsum_cache, colsum_new, freed_slots, workspace) is reused if given."""
+    score update, eviction by ``score_mode``.  policy "h2o_buffer": the insert-first buffer
+    form (targets from the scores before the chunk, attention over the buffer, score
+    update, insertion).  policy "lastrec": attention alone, then eviction by position
+    keeping the first ``sink_tokens``.  ``bufs`` (a dict holding out, lse, colsum_cache,
+    colsum_new, freed_slots, workspace) is reused if given."""
     b = bufs or {}
     P = cache.next_pos
+    if policy == "h2o_buffer":
+        S = q.shape[2]
+        freed = select_slots(cache, P, S, b.get("freed_slots"), score_mode, stream)
+        out, lse, cs_cache, cs_new = buffer_attn(cache, P, q, k_new, v_new, freed, sm_scale,
+                                                 b.get("out"), b.get("lse"),
+                                                 b.get("colsum_cache"), b.get("colsum_new"),
+                                                 b.get("workspace"), stream)
+        update_scores(cache, cs_cache, stream)
+        insert(cache, P, k_new, v_new, freed, cs_new, stream)
+        return {"out": out, "lse": lse, "colsum_cache": cs_cache, "colsum_new": cs_new,
+                "freed_slots": freed}
     if policy == "lastrec":
         out, lse, _, _ = chunk_attn(cache, P, q, k_new, v_new, sm_scale, b.get("out"),
                                     b.get("lse"), workspace=b.get("workspace"), stream=stream,

@@ -53,6 +53,13 @@ _SIGNATURES = {
     "h2o_evict_and_insert_lastrec": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64,
                                                c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                                c_void_p]),
+    "h2o_select_slots": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32,
+                                   c_int32, c_void_p, c_void_p]),
+    "h2o_buffer_attn": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32, c_float,
+                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "h2o_insert": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32, c_void_p,
+                             c_void_p, c_void_p, c_void_p, c_void_p]),
     "h2o_last_error": (c_char_p, []),
     "h2o_abi_version": (c_int32, []),
     "h2o_kernel_timer_start": (c_int32, [c_int32, c_int32]),

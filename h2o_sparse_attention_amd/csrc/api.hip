@@ -127,17 +127,31 @@ hipError_t cu_count(int* cus) {
     return hipSuccess;
 }
 
-// Shared body of the two eviction entry points.  mode: h2o_score_mode_t, or
-// kModeLastrec with `sink` protected leading positions (then colsum_new is NULL).
+// Workspace layout of a non-decode chunk: the split summed-weights partials
+// (bf16) and then, 256-byte aligned, the exclusion bits of the buffer form.
+size_t excl_offset(const h2o_dims_t* dims, int32_t chunk_len) {
+    if (dims->dtype != H2O_BF16) return 0;
+    const size_t b = colsum_workspace_bytes(dims->batch, dims->n_kv_heads, dims->capacity,
+                                            chunk_len);
+    return (b + 255) / 256 * 256;
+}
+size_t excl_bytes(const h2o_dims_t* dims) {
+    return (size_t)dims->batch * dims->n_kv_heads * excl_tiles(dims->capacity) * sizeof(uint64_t);
+}
+
+// Shared body of the eviction entry points.  mode: h2o_score_mode_t, or
+// kModeLastrec with `sink` protected leading positions; colsum_new NULL gives
+// inserted slots score 0.  do_select / do_insert: run the selection (targets
+// into freed_slots) and / or the insertion (from freed_slots).
 h2o_status_t evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_t chunk_start,
                               int32_t chunk_len, int mode, int sink, const void* k_new,
                               const void* v_new, const float* colsum_new, int32_t* freed_slots,
-                              void* stream) {
+                              void* stream, bool do_select = true, bool do_insert = true) {
     h2o_status_t st;
     if ((st = validate_dims(dims)) != H2O_OK) return st;
     if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
     if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
-    if (!k_new || !v_new || !freed_slots)
+    if ((do_insert && (!k_new || !v_new)) || !freed_slots)
         return fail(H2O_ERR_INVALID_ARG, "k_new, v_new and freed_slots must be non-NULL");
     const int n = cache->n_valid, S = chunk_len, NC = dims->capacity;
     const int k = n + S - NC;
@@ -167,15 +181,19 @@ h2o_status_t evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_
     a.score_mode = mode;
     a.sink = sink;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    timer_begin(H2O_KERNEL_SELECT, s);
-    hipError_t e = launch_select(a, s);
-    timer_end(H2O_KERNEL_SELECT, s);
-    if ((st = check_hip(e, "select launch")) != H2O_OK) return st;
-    timer_begin(H2O_KERNEL_INSERT, s);
-    e = launch_insert(a, s);
-    timer_end(H2O_KERNEL_INSERT, s);
-    if ((st = check_hip(e, "insert launch")) != H2O_OK) return st;
-    cache->n_valid = n + S < NC ? n + S : NC;
+    if (do_select) {
+        timer_begin(H2O_KERNEL_SELECT, s);
+        hipError_t e = launch_select(a, s);
+        timer_end(H2O_KERNEL_SELECT, s);
+        if ((st = check_hip(e, "select launch")) != H2O_OK) return st;
+    }
+    if (do_insert) {
+        timer_begin(H2O_KERNEL_INSERT, s);
+        hipError_t e = launch_insert(a, s);
+        timer_end(H2O_KERNEL_INSERT, s);
+        if ((st = check_hip(e, "insert launch")) != H2O_OK) return st;
+        cache->n_valid = n + S < NC ? n + S : NC;
+    }
     return ok();
 }
 
@@ -194,17 +212,22 @@ size_t h2o_workspace_bytes(const h2o_dims_t* dims, int32_t chunk_len) {
     if (uses_decode(dims, chunk_len))
         return decode_workspace_bytes(dims->batch, dims->n_q_heads, dims->n_kv_heads,
                                       dims->capacity);
-    if (dims->dtype == H2O_BF16)
-        return colsum_workspace_bytes(dims->batch, dims->n_kv_heads, dims->capacity, chunk_len);
-    return 0;
+    return excl_offset(dims, chunk_len) + excl_bytes(dims);
 }
 
-h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
-                            int64_t chunk_start, int32_t chunk_len, float sm_scale,
-                            const void* q, const void* k_new, const void* v_new, void* out,
-                            float* lse, float* colsum_cache, float* colsum_new,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace h2o {
+
+// Shared body of h2o_chunk_attn and h2o_buffer_attn (freed != NULL: the
+// victims among the targets are not keys).
+h2o_status_t chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache, int64_t chunk_start,
+                        int32_t chunk_len, float sm_scale, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* freed, void* out, float* lse,
+                        float* colsum_cache, float* colsum_new, void* workspace,
+                        size_t workspace_bytes, void* stream) {
     h2o_status_t st;
+
     if ((st = validate_dims(dims)) != H2O_OK) return st;
     if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
     if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
@@ -223,8 +246,12 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
                         G, chunk_len);
     }
     const bool decode = uses_decode(dims, chunk_len);
-    // Without summed weights only the decode path uses the workspace.
-    const size_t ws_need = (decode || want_cs) ? h2o_workspace_bytes(dims, chunk_len) : 0;
+    // Workspace: the decode partials; else the split summed-weights partials
+    // (bf16, when summed weights are asked for) and the exclusion bits (buffer form).
+    size_t ws_need = 0;
+    if (decode) ws_need = h2o_workspace_bytes(dims, chunk_len);
+    else if (freed) ws_need = excl_offset(dims, chunk_len) + excl_bytes(dims);
+    else if (want_cs && dims->dtype == H2O_BF16) ws_need = excl_offset(dims, chunk_len);
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
         return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", ws_need,
                     workspace ? workspace_bytes : (size_t)0);
@@ -250,8 +277,16 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
     a.n = cache->n_valid;
     a.P = (int)chunk_start;
     a.sm_scale = sm_scale;
+    a.freed = freed;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int rows = a.B * a.Hkv;
+    if (freed && !decode) {
+        uint64_t* excl = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) +
+                                                     excl_offset(dims, chunk_len));
+        if ((st = check_hip(launch_build_excl(a, excl, s), "exclusion masks")) != H2O_OK)
+            return st;
+        a.excl = excl;
+    }
 
     const bool bf16 = dims->dtype == H2O_BF16;
     int parts = 1;
@@ -282,6 +317,32 @@ h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
     timer_end(H2O_KERNEL_COLSUM, s);
     if ((st = check_hip(e, "colsum launch")) != H2O_OK) return st;
     return ok();
+}
+
+
+}  // namespace h2o
+
+extern "C" {
+
+h2o_status_t h2o_chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
+                            int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                            const void* q, const void* k_new, const void* v_new, void* out,
+                            float* lse, float* colsum_cache, float* colsum_new,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_attn(dims, cache, chunk_start, chunk_len, sm_scale, q, k_new, v_new, nullptr,
+                      out, lse, colsum_cache, colsum_new, workspace, workspace_bytes, stream);
+}
+
+h2o_status_t h2o_buffer_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
+                             int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                             const void* q, const void* k_new, const void* v_new,
+                             const int32_t* freed_slots, void* out, float* lse,
+                             float* colsum_cache, float* colsum_new, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (!freed_slots) return fail(H2O_ERR_INVALID_ARG, "freed_slots is NULL");
+    return chunk_attn(dims, cache, chunk_start, chunk_len, sm_scale, q, k_new, v_new,
+                      freed_slots, out, lse, colsum_cache, colsum_new, workspace,
+                      workspace_bytes, stream);
 }
 
 h2o_status_t h2o_update_scores(const h2o_dims_t* dims, const h2o_cache_t* cache,
@@ -322,6 +383,24 @@ h2o_status_t h2o_evict_and_insert_lastrec(const h2o_dims_t* dims, h2o_cache_t* c
     if (sink_tokens < 0) return fail(H2O_ERR_INVALID_ARG, "sink_tokens %d < 0", sink_tokens);
     return evict_and_insert(dims, cache, chunk_start, chunk_len, kModeLastrec, sink_tokens,
                             k_new, v_new, nullptr, freed_slots, stream);
+}
+
+h2o_status_t h2o_select_slots(const h2o_dims_t* dims, const h2o_cache_t* cache,
+                              int64_t chunk_start, int32_t chunk_len, int32_t score_mode,
+                              int32_t* freed_slots, void* stream) {
+    if (score_mode != H2O_SCORE_H2O && score_mode != H2O_SCORE_H2O_NORM)
+        return fail(H2O_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
+    if (!cache) return fail(H2O_ERR_INVALID_ARG, "cache is NULL");
+    h2o_cache_t c = *cache;                      // n_valid is not advanced
+    return evict_and_insert(dims, &c, chunk_start, chunk_len, score_mode, 0, nullptr, nullptr,
+                            nullptr, freed_slots, stream, true, false);
+}
+
+h2o_status_t h2o_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_t chunk_start,
+                        int32_t chunk_len, const void* k_new, const void* v_new,
+                        const float* colsum_new, const int32_t* freed_slots, void* stream) {
+    return evict_and_insert(dims, cache, chunk_start, chunk_len, H2O_SCORE_H2O, 0, k_new, v_new,
+                            colsum_new, const_cast<int32_t*>(freed_slots), stream, false, true);
 }
 
 h2o_status_t h2o_kernel_timer_start(int32_t kernel, int32_t max_launches) {

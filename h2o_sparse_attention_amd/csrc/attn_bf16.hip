@@ -252,15 +252,26 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
         return tr.valid == kKeysPerTile &&
                (tr.cache || tr.first + kKeysPerTile - 1 <= qpos_wave_min - a.P);
     };
-    // -inf for this lane's keys k > lim (the lane holds keys
-    // 32*sub + 16*(r/8) + 8*hh + r%8 of the tile).
-    auto apply_mask = [&](f32x16 (&sv)[2], int lim) {
+    // Buffer form: bits of the tile's slots that the chunk overwrites (cache
+    // tiles only; those slots are not keys).
+    const uint64_t* exrow = a.excl ? a.excl + (size_t)bg * excl_tiles(a.NC) : nullptr;
+    auto tile_excl = [&](int jt) -> uint64_t {
+        const int tile = 2 * jt + kh;
+        return (exrow != nullptr && tile < cache_tiles) ? exrow[tile] : 0ull;
+    };
+    // -inf for this lane's keys k > lim and for excluded slots (the lane holds
+    // keys 32*sub + 16*(r/8) + 8*hh + r%8 of the tile: bytes 4*sub + 2*(r/8) +
+    // hh of the tile's bits, gathered by one byte permute into bit 16*sub + r).
+    auto apply_mask = [&](f32x16 (&sv)[2], int lim, uint64_t ex) {
         const int d = lim - 8 * hh;
+        const uint32_t lb = __builtin_amdgcn_perm((uint32_t)(ex >> 32), (uint32_t)ex,
+                                                  hh ? 0x07050301u : 0x06040200u);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (sub * 32 + 16 * (r >> 3) + (r & 7) > d) sv[sub][r] = -INFINITY;
+                if (sub * 32 + 16 * (r >> 3) + (r & 7) > d || ((lb >> (16 * sub + r)) & 1u))
+                    sv[sub][r] = -INFINITY;
     };
     // Row max over both lane halves, running-max update and (rarely) the
     // rescale of O and l; returns m_run * c for the exponentials.
@@ -331,7 +342,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     publish_lds_loads();
     if (mine > 0) {
         qk(sK0[kh], sA);
-        if (!tile_all_visible(0)) apply_mask(sA, tile_lim(0));
+        const uint64_t ex0 = tile_excl(0);
+        if (!tile_all_visible(0) || ex0 != 0) apply_mask(sA, tile_lim(0), ex0);
         mc = rescale_for(rowmax(sA));
     }
     // Iteration 0 loads K(2) into K(0)'s buffer: every wave must be done
@@ -401,7 +413,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
             asm volatile("" : : "v"(lsum));
             l_run += lsum;
             // The next tile's mask (rare: partial or diagonal tiles).
-            if (has_next && !tile_all_visible(jt + 1)) apply_mask(snext, tile_lim(jt + 1));
+            if (has_next) {
+                const uint64_t exn = tile_excl(jt + 1);
+                if (!tile_all_visible(jt + 1) || exn != 0) apply_mask(snext, tile_lim(jt + 1), exn);
+            }
             // Phase B: P V of this tile with the next tile's row max.
             const float mt = pv_max(vcur, pb, snext);
             asm volatile("" : : "v"(mt));         // keep the maxima under the MFMAs
@@ -717,7 +732,12 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
 #pragma unroll 8
         for (int j = 0; j < 32; ++j) sum += sRed[wave][lane][j];
         const int idx = first + lane;
-        if (idx < limit) dst[idx] = sum;
+        // Buffer form: a slot the chunk overwrites is not a key (weight 0).
+        if (idx < limit) {
+            const bool ex = is_cache && a.excl != nullptr &&
+                            ((a.excl[(size_t)bg * excl_tiles(a.NC) + idx / 64] >> (idx % 64)) & 1);
+            dst[idx] = ex ? 0.f : sum;
+        }
     }
 }
 

@@ -58,6 +58,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(ChunkArgs a) {
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         if (!(kp >= 0 && kp <= qpos)) continue;
+        if (cached && a.excl && ((a.excl[(size_t)bg * excl_tiles(a.NC) + kk / 64] >> (kk % 64)) & 1))
+            continue;                              // a slot the chunk overwrites
         s *= a.sm_scale;
         const float m_new = fmaxf(m, s);
         const float alpha = expf(m - m_new);       // m = -inf gives 0
@@ -109,6 +111,8 @@ __global__ __launch_bounds__(kThreads) void colsum_f32_kernel(ChunkArgs a) {
         if (kp >= 0 && kp <= a.P + i) acc += expf(s * a.sm_scale - a.lse[qi]);
     }
     if (!key_ok || part != 0) return;
+    if (cached && a.excl && ((a.excl[(size_t)bg * excl_tiles(a.NC) + kk / 64] >> (kk % 64)) & 1))
+        acc = 0.f;                                 // not a key in the buffer form
     if (kk < a.n) a.cs_cache[(size_t)bg * a.NC + kk] = acc;
     else a.cs_new[(size_t)bg * a.S + (kk - a.n)] = acc;
 }

@@ -108,6 +108,7 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
     const u16* Kc = static_cast<const u16*>(a.kc) + (size_t)bg * NC * D;
     const u16* Vc = static_cast<const u16*>(a.vc) + (size_t)bg * NC * D;
     const int32_t* posg = a.pos + (size_t)bg * NC;
+    const int victim = a.freed != nullptr ? a.freed[bg] : -1;   // S = 1: one target
     const int k_begin = split * kDecSplit;
     const int k_end = min(n, k_begin + kDecSplit);
     const int nsub = (k_end - k_begin + kDecSub - 1) / kDecSub;
@@ -133,6 +134,7 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
             const Rsrc rp = make_rsrc(posg + k0, valid * 4);
             preg = (int)bload4(rp, lane * 4);
             pvalid = lane < valid;
+            if (k0 + lane == victim) preg = -1;   // buffer form: the slot being overwritten
         }
     };
     // LDS byte offsets of this lane's chunks (row row0 + it*RPL, chunk lane%CH);

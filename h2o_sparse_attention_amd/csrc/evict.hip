@@ -276,6 +276,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
     for (int e = tid; e < n_new - n; e += kSelThreads) freed[k + e] = n + e;
 }
 
+// ------------------------------------------------------------- exclusion masks
+// One thread per (b, kv head, 64-slot tile): the targets are ascending, so the
+// victims in the tile form one run, found by binary search.
+__global__ __launch_bounds__(256) void build_excl_kernel(const int32_t* __restrict__ freed,
+                                                         uint64_t* __restrict__ excl, int S,
+                                                         int n, int ntc, int rows) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= rows * ntc) return;
+    const int bg = idx / ntc, t = idx % ntc;
+    const int32_t* f = freed + (size_t)bg * S;
+    const int lo_slot = 64 * t, hi_slot = min(n, 64 * t + 64);
+    int lo = 0, hi = S;                     // first target >= lo_slot
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (f[mid] < lo_slot) lo = mid + 1;
+        else hi = mid;
+    }
+    uint64_t bits = 0;
+    for (int i = lo; i < S && f[i] < hi_slot; ++i) bits |= 1ull << (f[i] - lo_slot);
+    excl[idx] = bits;
+}
+
 // ------------------------------------------------------------------ insert
 constexpr int kInsTokens = 16;
 
@@ -357,6 +379,14 @@ hipError_t launch_select(const EvictArgs& a, hipStream_t s) {
     if (p2 <= 8) return go(select_kernel<8>);
     if (p2 <= 16) return go(select_kernel<16>);
     return go(select_kernel<32>);
+}
+
+hipError_t launch_build_excl(const ChunkArgs& a, uint64_t* excl, hipStream_t s) {
+    const int rows = a.B * a.Hkv, ntc = excl_tiles(a.NC);
+    const int total = rows * ntc;
+    hipLaunchKernelGGL(build_excl_kernel, dim3((total + 255) / 256), dim3(256), 0, s, a.freed,
+                       excl, a.S, a.n, ntc, rows);
+    return hipGetLastError();
 }
 
 hipError_t launch_insert(const EvictArgs& a, hipStream_t s) {

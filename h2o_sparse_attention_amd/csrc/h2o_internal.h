@@ -23,7 +23,13 @@ struct ChunkArgs {
     int B, Hq, Hkv, G, D, S, NC, n;
     int P;                  // absolute position of the chunk's first query row
     float sm_scale;
+    // Buffer form: cache slots the chunk is about to overwrite are not keys.
+    const int32_t* freed = nullptr;   // [B][Hkv][S] targets, ascending (victims are < n)
+    const uint64_t* excl = nullptr;   // [B][Hkv][ceil(NC/64)] excluded-slot bits per 64 slots
 };
+
+// Tiles of 64 slots per (b, kv head) row of the exclusion masks.
+__host__ __device__ inline int excl_tiles(int NC) { return (NC + 63) / 64; }
 
 struct EvictArgs {
     void* kc;
@@ -55,6 +61,8 @@ hipError_t launch_zero_f32(float* p, size_t count_per_row, size_t row_stride, in
 hipError_t launch_update_scores(float* score, const float* cs, int rows, int NC, int n,
                                 hipStream_t s);
 hipError_t launch_select(const EvictArgs& a, hipStream_t s);
+// excl[bg][t] = bits of the victims (freed slots below n) among slots 64t .. 64t+63.
+hipError_t launch_build_excl(const ChunkArgs& a, uint64_t* excl, hipStream_t s);
 hipError_t launch_insert(const EvictArgs& a, hipStream_t s);
 
 // Decode (S = 1) specialisation.

@@ -93,11 +93,14 @@ typedef struct {
     int32_t  n_valid;
 } h2o_cache_t;
 
-/* Bytes of workspace h2o_chunk_attn needs for this chunk length (0 = none): the
- * split-over-slots partial results of the S = 1 path (bf16, d = 128, at most 32
- * query heads per KV head), or, for other bf16 chunks, partial summed weights
- * (4 * B * Hkv * (N_C + S) floats; not needed when no summed weights are asked
- * for).  The contents need no initialisation and are not preserved. */
+/* Bytes of workspace h2o_chunk_attn and h2o_buffer_attn need for this chunk
+ * length (enough for either): the split-over-slots partial results of the S = 1
+ * path (bf16, d = 128, at most 32 query heads per KV head); or, for other
+ * chunks, the partial summed weights of bf16 (4 * B * Hkv * (N_C + S) floats;
+ * h2o_chunk_attn needs nothing else, and nothing at all without summed weights
+ * or in f32) followed by the exclusion bits of h2o_buffer_attn
+ * (B * Hkv * ceil(N_C / 64) 64-bit words).  The contents need no
+ * initialisation and are not preserved. */
 H2O_API size_t h2o_workspace_bytes(const h2o_dims_t *dims, int32_t chunk_len);
 
 /*
@@ -156,6 +159,55 @@ H2O_API h2o_status_t h2o_evict_and_insert(const h2o_dims_t *dims, h2o_cache_t *c
                                   const void *k_new, const void *v_new,
                                   const float *colsum_new, int32_t *freed_slots,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Insert-first buffer form ("Kernel Support Needs": attention over the fixed
+ * N_C-slot buffer under the positional mask -inf * 1[P+i < t(b,h,j)]).  The
+ * victims are chosen on the scores before the chunk and the chunk is written
+ * into the targets before it attends, so it sees the slots that survive and
+ * its own keys, causally -- never the slots it overwrites.  One chunk is:
+ *   h2o_select_slots -> h2o_buffer_attn -> h2o_update_scores -> h2o_insert.
+ *
+ * h2o_select_slots: the targets of h2o_evict_and_insert (the k = max(0, n+S-N_C)
+ * eligible slots of smallest (score, slot index) -- h2o or h2o-norm as
+ * score_mode -- with the empty slots [n, min(N_C, n+S)), ascending) into
+ * freed_slots, from the current scores.  The cache is not modified.  Errors
+ * as h2o_evict_and_insert (H2O_ERR_CAPACITY when k > 0 and S + W > N_C).
+ */
+H2O_API h2o_status_t h2o_select_slots(const h2o_dims_t *dims, const h2o_cache_t *cache,
+                              int64_t chunk_start, int32_t chunk_len, int32_t score_mode,
+                              int32_t *freed_slots, void *stream);
+
+/*
+ * h2o_buffer_attn: the chunk attention of h2o_chunk_attn (same arguments,
+ * layouts, precision and precondition) over the buffer as it stands once the
+ * chunk is written into freed_slots (the output of h2o_select_slots for this
+ * cache, P and S): the targets below n_valid are not keys.  Equivalently, a
+ * slot j of the buffer with position t(j) is visible to row i iff
+ * t(j) <= P + i, the chunk's token i' sitting in slot freed_slots[b,g,i'].
+ *   colsum_cache[b,g,j] = 0 for the slots being overwritten and j >= n_valid;
+ *   colsum_new[b,g,i']  = the summed weight of chunk token i' (its slot's).
+ * colsum_cache and colsum_new may both be NULL.  The workspace must hold
+ * h2o_workspace_bytes(dims, chunk_len) bytes (the exclusion bits of the
+ * overwritten slots live there).
+ */
+H2O_API h2o_status_t h2o_buffer_attn(const h2o_dims_t *dims, const h2o_cache_t *cache,
+                             int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                             const void *q, const void *k_new, const void *v_new,
+                             const int32_t *freed_slots, void *out, float *lse,
+                             float *colsum_cache, float *colsum_new, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * h2o_insert: the insertion half of h2o_evict_and_insert for given targets:
+ * chunk token i goes to freed_slots[b,g,i] (K, V copied, t = P + i, score =
+ * colsum_new[b,g,i], or 0 when colsum_new is NULL); then
+ * cache->n_valid = min(N_C, n + S).  freed_slots must come from
+ * h2o_select_slots for the same cache, P and S.
+ */
+H2O_API h2o_status_t h2o_insert(const h2o_dims_t *dims, h2o_cache_t *cache, int64_t chunk_start,
+                        int32_t chunk_len, const void *k_new, const void *v_new,
+                        const float *colsum_new, const int32_t *freed_slots, void *stream);
 
 /*
  * lastrec eviction and insertion ("Experimental Validation", the lr policy:

@@ -24,5 +24,6 @@ from .h2o_oracle import (  # noqa: F401
     lastrec_step,
     select_victims,
     select_victims_lastrec,
+    selection_scores,
     update_scores,
 )

@@ -161,6 +161,40 @@ def test_chunk_attn_summed_weights_both_or_neither():
         assert "colsum" in h2o.lib.h2o_last_error().decode()
 
 
+def test_buffer_form_rejects_bad_args():
+    d = _dims(capacity=256, recent_window=200)
+    cache = _native.CacheStruct(FAKE, FAKE, FAKE, FAKE, 256)
+    # selection: full cache, S + W > N_C
+    st = h2o.lib.h2o_select_slots(ctypes.byref(d), ctypes.byref(cache), 1000, 64, 0, FAKE, None)
+    assert st == _native.H2O_ERR_CAPACITY and cache.n_valid == 256
+    assert h2o.lib.h2o_select_slots(ctypes.byref(_dims()), ctypes.byref(cache), 1000, 8, 9,
+                                    FAKE, None) == _native.H2O_ERR_INVALID_ARG
+    assert h2o.lib.h2o_select_slots(ctypes.byref(_dims()), ctypes.byref(cache), 1000, 8, 0,
+                                    None, None) == _native.H2O_ERR_INVALID_ARG
+    # attention over the buffer needs the targets and a workspace
+    d = _dims()
+    cache = _native.CacheStruct(FAKE, FAKE, FAKE, FAKE, 0)
+    assert h2o.lib.h2o_buffer_attn(ctypes.byref(d), ctypes.byref(cache), 0, 64, 0.125, FAKE,
+                                   FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                   None) == _native.H2O_ERR_INVALID_ARG
+    st = h2o.lib.h2o_buffer_attn(ctypes.byref(d), ctypes.byref(cache), 0, 64, 0.125, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == _native.H2O_ERR_WORKSPACE
+    # insertion needs its targets
+    assert h2o.lib.h2o_insert(ctypes.byref(d), ctypes.byref(cache), 0, 64, FAKE, FAKE, None,
+                              None, None) == _native.H2O_ERR_INVALID_ARG
+    assert cache.n_valid == 0
+
+
+def test_workspace_bytes_cover_both_attention_calls():
+    d = _dims(capacity=8192, head_dim=128, n_q_heads=32, n_kv_heads=8)
+    parts = 4 * 1 * 8 * (8192 + 1024) * 4
+    words = 1 * 8 * (8192 // 64) * 8
+    assert h2o.lib.h2o_workspace_bytes(ctypes.byref(d), 1024) == (parts + 255) // 256 * 256 + words
+    f32 = _dims(dtype=_native.H2O_F32)
+    assert h2o.lib.h2o_workspace_bytes(ctypes.byref(f32), 64) == 1 * 2 * 4 * 8
+
+
 def test_workspace_bytes_invalid_is_zero():
     assert h2o.lib.h2o_workspace_bytes(None, 1) == 0
     assert h2o.lib.h2o_workspace_bytes(ctypes.byref(_dims(head_dim=3)), 1) == 0
