@@ -18,6 +18,7 @@ from .h2o_oracle import (  # noqa: F401
     H2OState,
     attend_buffer,
     attend_chunk,
+    attend_chunk_backward,
     buffer_step,
     evict_and_insert,
     h2o_step,

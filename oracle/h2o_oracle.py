@@ -34,7 +34,10 @@ Readings taken where the pages are silent or garbled:
 * the insert-first buffer form (the positional mask of "Kernel Support Needs"
   over the fixed-size buffer) chooses the victims on the scores before the
   chunk, writes the chunk with score 0, then attends over the N_C slots; the
-  new tokens' scores are then their own summed weights, as in the other order.
+  new tokens' scores are then their own summed weights, as in the other order;
+* the backward ("Gradient Computation Strategy", item 1: the policy's choices
+  are replayed, not differentiated) is that of masked softmax attention over
+  the chunk's fixed keys and mask.
 """
 from __future__ import annotations
 
@@ -300,4 +303,61 @@ def buffer_step(state: H2OState, q, k_new, v_new, sm_scale: float, W: int,
     update_scores(state, colsum)
     return {"out": out, "lse": lse, "colsum": colsum, "victims": victims,
             "evicted_phi": evicted_phi, "freed_slots": freed}
+
+
+# ------------------------------------------------------------------- backward
+def attend_chunk_backward(state: H2OState, q, k_new, v_new, dout, sm_scale: float,
+                          excluded=None):
+    """Gradients of the chunk attention's output with the cache decisions fixed.
+
+    The policy's choices are replayed rather than differentiated (montaan paper
+    page, "Gradient Computation Strategy", item 1), so the keys and the mask of
+    ``attend_chunk`` are constants here and the gradient is that of masked
+    softmax attention.  ``excluded`` (B, Hkv, N_C) bool marks cache slots that
+    are not keys (the buffer form's overwritten slots).
+
+    Per query head, with m = softmax(s) over the visible keys and dm = dO V^T:
+        dV += m^T dO,  ds = m * (dm - rowsum(dO * O)),
+        dQ = sm_scale * ds K,  dK += sm_scale * ds^T Q.
+    Returns dq (B,Hq,S,d), dk_new, dv_new (B,Hkv,S,d) and dk_cache, dv_cache
+    (B,Hkv,N_C,d), zero beyond n and at excluded slots.
+    """
+    q = np.asarray(q, np.float64)
+    k_new = np.asarray(k_new, np.float64)
+    v_new = np.asarray(v_new, np.float64)
+    dout = np.asarray(dout, np.float64)
+    B, Hq, S, d = q.shape
+    Hkv = k_new.shape[1]
+    G = Hq // Hkv
+    n, P, NC = state.n, state.P, state.capacity
+    dq = np.zeros((B, Hq, S, d))
+    dk_new = np.zeros((B, Hkv, S, d))
+    dv_new = np.zeros((B, Hkv, S, d))
+    dk_cache = np.zeros((B, Hkv, NC, d))
+    dv_cache = np.zeros((B, Hkv, NC, d))
+    q_pos = P + np.arange(S)
+    for b in range(B):
+        for g in range(Hkv):
+            keys = np.concatenate([state.K[b, g, :n], k_new[b, g]])
+            values = np.concatenate([state.V[b, g, :n], v_new[b, g]])
+            t = np.concatenate([state.pos[b, g, :n], q_pos])
+            visible = (t[None, :] >= 0) & (t[None, :] <= q_pos[:, None])
+            if excluded is not None:
+                visible[:, :n] &= ~np.asarray(excluded[b, g, :n], bool)[None, :]
+            dkeys = np.zeros_like(keys)
+            dvalues = np.zeros_like(values)
+            for hh in range(G):
+                h = g * G + hh
+                s = np.where(visible, sm_scale * (q[b, h] @ keys.T), -np.inf)
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                m = e / e.sum(axis=1, keepdims=True)
+                o = m @ values
+                dm = dout[b, h] @ values.T
+                ds = m * (dm - (dout[b, h] * o).sum(axis=1, keepdims=True))
+                dvalues += m.T @ dout[b, h]
+                dq[b, h] = sm_scale * (ds @ keys)
+                dkeys += sm_scale * (ds.T @ q[b, h])
+            dk_cache[b, g, :n], dk_new[b, g] = dkeys[:n], dkeys[n:]
+            dv_cache[b, g, :n], dv_new[b, g] = dvalues[:n], dvalues[n:]
+    return dq, dk_new, dv_new, dk_cache, dv_cache
 

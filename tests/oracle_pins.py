@@ -462,9 +462,84 @@ def check_buffer_dense_replay(orc, seed=12):
                                                rtol=1e-12, atol=1e-15)
 
 
+def check_backward_is_autograd(orc, seed=13):
+    """The gradients equal torch autograd through fp64 SDPA over the same keys under the
+    same mask: the filled slots (some excluded) and the chunk's causal keys."""
+    r = np.random.default_rng(seed)
+    B, Hq, Hkv, d, NC, n, S, P = 2, 4, 2, 8, 24, 17, 6, 30
+    G = Hq // Hkv
+    K = r.standard_normal((B, Hkv, NC, d))
+    V = r.standard_normal((B, Hkv, NC, d))
+    pos = np.stack([np.stack([np.sort(r.choice(P, NC, replace=False)) for _ in range(Hkv)])
+                    for _ in range(B)])
+    st = orc.H2OState.from_arrays(K, V, pos, np.zeros((B, Hkv, NC)), n, P)
+    q = r.standard_normal((B, Hq, S, d))
+    kn = r.standard_normal((B, Hkv, S, d))
+    vn = r.standard_normal((B, Hkv, S, d))
+    dout = r.standard_normal((B, Hq, S, d))
+    excl = r.random((B, Hkv, NC)) < 0.25
+    sm = 0.45
+    got = orc.attend_chunk_backward(st, q, kn, vn, dout, sm, excluded=excl)
+    qt = torch.from_numpy(q).requires_grad_()
+    kc = torch.from_numpy(K[:, :, :n].copy()).requires_grad_()
+    vc = torch.from_numpy(V[:, :, :n].copy()).requires_grad_()
+    knt = torch.from_numpy(kn).requires_grad_()
+    vnt = torch.from_numpy(vn).requires_grad_()
+    keys = torch.cat([kc, knt], dim=2).repeat_interleave(G, dim=1)
+    vals = torch.cat([vc, vnt], dim=2).repeat_interleave(G, dim=1)
+    t = np.concatenate([pos[:, :, :n], np.broadcast_to(P + np.arange(S), (B, Hkv, S))], axis=2)
+    vis = (t[:, :, None, :] <= (P + np.arange(S))[None, None, :, None])
+    vis[:, :, :, :n] &= ~excl[:, :, None, :n]
+    mask = torch.from_numpy(np.repeat(vis, G, axis=1))
+    out = torch.nn.functional.scaled_dot_product_attention(qt, keys, vals, attn_mask=mask, scale=sm)
+    out.backward(torch.from_numpy(dout))
+    want = [qt.grad, knt.grad, vnt.grad, kc.grad, vc.grad]
+    for gi, wi in zip(got[:3], want[:3]):
+        np.testing.assert_allclose(gi, wi.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(got[3][:, :, :n], want[3].numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(got[4][:, :, :n], want[4].numpy(), rtol=1e-9, atol=1e-11)
+    assert (got[3][:, :, n:] == 0).all() and (got[4][:, :, n:] == 0).all()
+    assert (got[3][excl & (np.arange(NC) < n)] == 0).all()
+
+
+def check_backward_finite_differences(orc, seed=14):
+    """Central differences of L = sum(O * dO) on a tiny case match the gradients."""
+    r = np.random.default_rng(seed)
+    B, Hq, Hkv, d, NC, n, S, P = 1, 2, 1, 3, 5, 4, 3, 7
+    K = r.standard_normal((B, Hkv, NC, d))
+    V = r.standard_normal((B, Hkv, NC, d))
+    pos = np.array([[[0, 2, 5, 6, -1]]])
+    q = r.standard_normal((B, Hq, S, d))
+    kn = r.standard_normal((B, Hkv, S, d))
+    vn = r.standard_normal((B, Hkv, S, d))
+    dout = r.standard_normal((B, Hq, S, d))
+    sm = 0.7
+
+    def loss(K_, V_, q_, kn_, vn_):
+        st = orc.H2OState.from_arrays(K_, V_, pos, np.zeros((B, Hkv, NC)), n, P)
+        return (orc.attend_chunk(st, q_, kn_, vn_, sm)[0] * dout).sum()
+    st = orc.H2OState.from_arrays(K, V, pos, np.zeros((B, Hkv, NC)), n, P)
+    got = orc.attend_chunk_backward(st, q, kn, vn, dout, sm)
+    args = [K, V, q, kn, vn]
+    names = {2: 0, 3: 1, 4: 2, 0: 3, 1: 4}          # argument -> index in got
+    eps = 1e-6
+    for ai, arr in enumerate(args):
+        g = got[names[ai]]
+        for idx in np.ndindex(arr.shape):
+            if ai in (0, 1) and idx[2] >= n:
+                continue
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[ai][idx] += eps
+            minus[ai][idx] -= eps
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert abs(fd - g[idx]) <= 1e-6 * max(1.0, abs(fd)), (ai, idx, fd, g[idx])
+
+
 ALL_CHECKS = [check_golden, check_rows_normalised, check_exact_when_no_eviction,
               check_chunk_size_invariance, check_uniform_closed_form,
               check_bruteforce_selection, check_decode_is_argmin, check_dense_masked_replay,
               check_conservation_and_monotonicity, check_slot_permutation_invariance,
               check_lastrec_closed_form, check_lastrec_capacity_error,
-              check_buffer_without_eviction_is_attend_first, check_buffer_dense_replay]
+              check_buffer_without_eviction_is_attend_first, check_buffer_dense_replay,
+              check_backward_is_autograd, check_backward_finite_differences]

@@ -50,6 +50,10 @@ MUTANTS = [
     ("            keys, values, t = state.K[b, g, :n], state.V[b, g, :n], state.pos[b, g, :n]",
      "            keys, values, t = state.K[b, g, :n], state.V[b, g, :n], state.pos[b, g, :n] - 1",
      "buffer mask off by one"),
+    ("ds = m * (dm - (dout[b, h] * o).sum(axis=1, keepdims=True))", "ds = m * dm",
+     "backward without the row term"),
+    ("dkeys += sm_scale * (ds.T @ q[b, h])", "dkeys += ds.T @ q[b, h]", "backward dK unscaled"),
+    ("dvalues += m.T @ dout[b, h]", "dvalues += 0.5 * (m.T @ dout[b, h])", "backward dV halved"),
 ]
 
 
