@@ -249,6 +249,45 @@ def insert(cache: H2OCache, chunk_start: int, k_new, v_new, freed_slots, colsum_
     cache.next_pos = int(chunk_start) + S
 
 
+def chunk_attn_backward(cache: H2OCache, chunk_start: int, q, k_new, v_new, out, lse, dout,
+                        sm_scale: float, freed_slots=None, grads=None, workspace=None,
+                        stream=None):
+    """h2o_chunk_attn_backward: returns (dq, dk_new, dv_new, dk_cache, dv_cache), float32.
+    The cache must be as it stood for the forward call that produced out and lse."""
+    d = cache.dims
+    B, Hq, Hkv, D, NC = d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim, d.capacity
+    S = q.shape[2]
+    dev = cache.k.device
+    _need(q, (B, Hq, S, D), d.torch_dtype, "q")
+    _need(k_new, (B, Hkv, S, D), d.torch_dtype, "k_new")
+    _need(v_new, (B, Hkv, S, D), d.torch_dtype, "v_new")
+    _need(out, (B, Hq, S, D), d.torch_dtype, "out")
+    _need(lse, (B, Hq, S), torch.float32, "lse")
+    _need(dout, (B, Hq, S, D), d.torch_dtype, "dout")
+    if freed_slots is not None:
+        _need(freed_slots, (B, Hkv, S), torch.int32, "freed_slots")
+    g = grads or {}
+    shapes = {"dq": (B, Hq, S, D), "dk_new": (B, Hkv, S, D), "dv_new": (B, Hkv, S, D),
+              "dk_cache": (B, Hkv, NC, D), "dv_cache": (B, Hkv, NC, D)}
+    res = []
+    for name, shape in shapes.items():
+        t = g.get(name)
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+        _need(t, shape, torch.float32, name)
+        res.append(t)
+    ws_need = int(lib.h2o_backward_workspace_bytes(ctypes.byref(d.c()), S))
+    if workspace is None:
+        workspace = torch.empty(max(1, ws_need), dtype=torch.uint8, device=dev)
+    check(lib.h2o_chunk_attn_backward(
+        ctypes.byref(d.c()), ctypes.byref(cache.c()), int(chunk_start), S, float(sm_scale),
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        dout.data_ptr(), freed_slots.data_ptr() if freed_slots is not None else None,
+        *[t.data_ptr() for t in res], workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev)))
+    return tuple(res)
+
+
 def evict_and_insert_lastrec(cache: H2OCache, chunk_start: int, k_new, v_new, sink_tokens: int,
                              freed_slots=None, stream=None):
     """h2o_evict_and_insert_lastrec: returns freed_slots [B,Hkv,S], advances cache.n_valid."""

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "H2O_OK", -1: "H2O_ERR_INVALID_ARG", -2: "H2O_ERR_UNSUPPORTED
 H2O_F32, H2O_BF16 = 0, 1
 H2O_SCORE_H2O, H2O_SCORE_H2O_NORM = 0, 1
 KERNEL_IDS = {"attn": 0, "colsum": 1, "update": 2, "select": 3, "insert": 4, "decode": 5,
-              "decode_finish": 6}
+              "decode_finish": 6, "backward": 7}
 
 # Every function include/h2o.h declares, with its ctypes signature.
 EXPORTS = {}
@@ -60,6 +60,9 @@ _SIGNATURES = {
                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "h2o_insert": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32, c_void_p,
                              c_void_p, c_void_p, c_void_p, c_void_p]),
+    "h2o_backward_workspace_bytes": (c_size_t, [POINTER(Dims), c_int32]),
+    "h2o_chunk_attn_backward": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32,
+                                          c_float] + [c_void_p] * 12 + [c_size_t, c_void_p]),
     "h2o_last_error": (c_char_p, []),
     "h2o_abi_version": (c_int32, []),
     "h2o_kernel_timer_start": (c_int32, [c_int32, c_int32]),

@@ -345,6 +345,89 @@ h2o_status_t h2o_buffer_attn(const h2o_dims_t* dims, const h2o_cache_t* cache,
                       workspace_bytes, stream);
 }
 
+size_t h2o_backward_workspace_bytes(const h2o_dims_t* dims, int32_t chunk_len) {
+    if (validate_dims(dims) != H2O_OK || chunk_len < 1) return 0;
+    return backward_workspace_bytes(dims->batch, dims->n_q_heads, chunk_len) + excl_bytes(dims);
+}
+
+h2o_status_t h2o_chunk_attn_backward(const h2o_dims_t* dims, const h2o_cache_t* cache,
+                                     int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                                     const void* q, const void* k_new, const void* v_new,
+                                     const void* out, const float* lse, const void* dout,
+                                     const int32_t* freed_slots, float* dq, float* dk_new,
+                                     float* dv_new, float* dk_cache, float* dv_cache,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    h2o_status_t st;
+    if ((st = validate_dims(dims)) != H2O_OK) return st;
+    if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
+    if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
+    if (!q || !k_new || !v_new || !out || !lse || !dout)
+        return fail(H2O_ERR_INVALID_ARG, "q, k_new, v_new, out, lse and dout must be non-NULL");
+    if (!dq || !dk_new || !dv_new || !dk_cache || !dv_cache)
+        return fail(H2O_ERR_INVALID_ARG, "gradient buffers must be non-NULL");
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+        return fail(H2O_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+    {
+        const long long G = dims->n_q_heads / dims->n_kv_heads;
+        if (G * G * (long long)chunk_len >= (1LL << 31) ||
+            G * (long long)chunk_len * dims->head_dim * 4 >= (1LL << 31))
+            return fail(H2O_ERR_UNSUPPORTED, "query heads per KV head (%lld) too large for chunk_len %d",
+                        G, chunk_len);
+    }
+    const size_t ws_drow = backward_workspace_bytes(dims->batch, dims->n_q_heads, chunk_len);
+    const size_t ws_need = ws_drow + (freed_slots ? excl_bytes(dims) : 0);
+    if (!workspace || workspace_bytes < ws_need)
+        return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", ws_need,
+                    workspace ? workspace_bytes : (size_t)0);
+    ChunkArgs a;
+    a.q = q;
+    a.kc = cache->k;
+    a.vc = cache->v;
+    a.kn = k_new;
+    a.vn = v_new;
+    a.pos = cache->pos;
+    a.out = const_cast<void*>(out);
+    a.lse = const_cast<float*>(lse);
+    a.cs_cache = nullptr;
+    a.cs_new = nullptr;
+    a.B = dims->batch;
+    a.Hq = dims->n_q_heads;
+    a.Hkv = dims->n_kv_heads;
+    a.G = dims->n_q_heads / dims->n_kv_heads;
+    a.D = dims->head_dim;
+    a.S = chunk_len;
+    a.NC = dims->capacity;
+    a.n = cache->n_valid;
+    a.P = (int)chunk_start;
+    a.sm_scale = sm_scale;
+    a.freed = freed_slots;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* drow = static_cast<float*>(workspace);
+    if (freed_slots) {
+        uint64_t* excl = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + ws_drow);
+        if ((st = check_hip(launch_build_excl(a, excl, s), "exclusion masks")) != H2O_OK) return st;
+        a.excl = excl;
+    }
+    const int rows = a.B * a.Hkv;
+    if (a.n < a.NC) {
+        const size_t per = (size_t)(a.NC - a.n) * a.D, stride = (size_t)a.NC * a.D;
+        if ((st = check_hip(launch_zero_f32(dk_cache, per, stride, rows, (size_t)a.n * a.D, s),
+                            "zero dk tail")) != H2O_OK ||
+            (st = check_hip(launch_zero_f32(dv_cache, per, stride, rows, (size_t)a.n * a.D, s),
+                            "zero dv tail")) != H2O_OK)
+            return st;
+    }
+    timer_begin(H2O_KERNEL_BACKWARD, s);
+    hipError_t e = dims->dtype == H2O_BF16
+                       ? launch_backward_bf16(a, out, dout, drow, dq, dk_new, dv_new, dk_cache,
+                                              dv_cache, s)
+                       : launch_backward_f32(a, out, dout, drow, dq, dk_new, dv_new, dk_cache,
+                                             dv_cache, s);
+    timer_end(H2O_KERNEL_BACKWARD, s);
+    if ((st = check_hip(e, "backward launch")) != H2O_OK) return st;
+    return ok();
+}
+
 h2o_status_t h2o_update_scores(const h2o_dims_t* dims, const h2o_cache_t* cache,
                                const float* colsum_cache, void* stream) {
     h2o_status_t st;

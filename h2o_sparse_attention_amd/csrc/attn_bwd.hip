@@ -1,0 +1,627 @@
+// Backward of the chunk attention with the cache decisions fixed.
+//
+// "Learning how to Forget: Fine-tuning for Long-Context Sparse Attention",
+// montaan paper page, "Gradient Computation Strategy", item 1: the policy's
+// choices are replayed, not differentiated, so the keys and the mask of a chunk
+// are constants and the gradient is that of masked softmax attention.  With
+// m = softmax(sm_scale * q.k) over the visible keys, per query row i:
+//   D_i = sum_d dO[i,d] O[i,d],   ds_ij = m_ij (dO_i . v_j - D_i),
+//   dQ_i = sm_scale sum_j ds_ij k_j,   dK_j = sm_scale sum_i ds_ij q_i,
+//   dV_j = sum_i m_ij dO_i   (dK, dV summed over the G query heads of a KV head).
+// Visibility is that of the forward pass: every filled slot (minus the slots the
+// buffer form overwrites) for every row, chunk key i' for rows i >= i'.
+// All gradients are fp32.
+#include "h2o_internal.h"
+#include "device_common.h"
+
+#include <hip/hip_bf16.h>
+
+#include <climits>
+#include <cmath>
+
+namespace h2o {
+namespace {
+
+using namespace dev;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(u16 x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ bool excluded(const ChunkArgs& a, int bg, int slot) {
+    return a.excl != nullptr &&
+           ((a.excl[(size_t)bg * excl_tiles(a.NC) + slot / 64] >> (slot % 64)) & 1);
+}
+
+// D_i = dO_i . O_i: 16 lanes per row, 8 elements per lane per step.
+template <typename T>
+__global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o,
+                                                     const T* __restrict__ dout,
+                                                     float* __restrict__ drow, int rows, int D) {
+    const int row = blockIdx.x * 16 + threadIdx.x / 16;
+    const int l = threadIdx.x % 16;
+    float acc = 0.f;
+    if (row < rows) {
+        const T* orow = o + (size_t)row * D;
+        const T* drw = dout + (size_t)row * D;
+        for (int d = l; d < D; d += 16) acc = fmaf(to_f32(orow[d]), to_f32(drw[d]), acc);
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (row < rows && l == 0) drow[row] = acc;
+}
+
+// ------------------------------------------------------------------ f32 path
+// Four lanes per query row (dQ) or per key (dK, dV), a quarter of head_dim each.
+constexpr int kThreads = 256;
+constexpr int kLanes = 4;
+constexpr int kItems = kThreads / kLanes;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_f32_kernel(ChunkArgs a, const float* drow,
+                                                              const float* dout, float* dq) {
+    constexpr int DL = D / kLanes;
+    const int R = a.G * a.S;
+    const int nrb = (R + kItems - 1) / kItems;
+    const int bg = blockIdx.x / nrb, rb = blockIdx.x % nrb;
+    if (bg >= a.B * a.Hkv) return;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int part = threadIdx.x % kLanes;
+    const int row = rb * kItems + threadIdx.x / kLanes;
+    const bool row_ok = row < R;
+    const int i = row_ok ? row / a.G : a.S - 1;
+    const int h = g * a.G + (row_ok ? row % a.G : 0);
+    const int qpos = a.P + i;
+    const size_t qi = (size_t)(b * a.Hq + h) * a.S + i;
+    const float* Q = static_cast<const float*>(a.q) + qi * D;
+    const float* dO = dout + qi * D;
+    const float* Kc = static_cast<const float*>(a.kc) + (size_t)bg * a.NC * D;
+    const float* Vc = static_cast<const float*>(a.vc) + (size_t)bg * a.NC * D;
+    const float* Kn = static_cast<const float*>(a.kn) + (size_t)bg * a.S * D;
+    const float* Vn = static_cast<const float*>(a.vn) + (size_t)bg * a.S * D;
+    const int32_t* posg = a.pos + (size_t)bg * a.NC;
+    const float lse = a.lse[qi], Di = drow[qi];
+    float qv[DL], dov[DL], acc[DL];
+#pragma unroll
+    for (int e = 0; e < DL; ++e) {
+        qv[e] = Q[part * DL + e];
+        dov[e] = dO[part * DL + e];
+        acc[e] = 0.f;
+    }
+    for (int kk = 0; kk < a.n + a.S; ++kk) {
+        const bool cached = kk < a.n;
+        const int kp = cached ? posg[kk] : a.P + (kk - a.n);
+        const float* kr = cached ? Kc + (size_t)kk * D : Kn + (size_t)(kk - a.n) * D;
+        const float* vr = cached ? Vc + (size_t)kk * D : Vn + (size_t)(kk - a.n) * D;
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) {
+            s = fmaf(qv[e], kr[part * DL + e], s);
+            dp = fmaf(dov[e], vr[part * DL + e], dp);
+        }
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        dp += __shfl_xor(dp, 1);
+        dp += __shfl_xor(dp, 2);
+        if (!(kp >= 0 && kp <= qpos) || (cached && excluded(a, bg, kk))) continue;
+        const float ds = expf(s * a.sm_scale - lse) * (dp - Di);
+#pragma unroll
+        for (int e = 0; e < DL; ++e) acc[e] = fmaf(ds, kr[part * DL + e], acc[e]);
+    }
+    if (!row_ok) return;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) dq[qi * D + part * DL + e] = a.sm_scale * acc[e];
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_f32_kernel(ChunkArgs a, const float* drow,
+                                                                const float* dout, float* dk_new,
+                                                                float* dv_new, float* dk_cache,
+                                                                float* dv_cache) {
+    constexpr int DL = D / kLanes;
+    const int nkeys = a.n + a.S;
+    const int nkb = (nkeys + kItems - 1) / kItems;
+    const int bg = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+    if (bg >= a.B * a.Hkv) return;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int part = threadIdx.x % kLanes;
+    const int kk = kb * kItems + threadIdx.x / kLanes;
+    const bool key_ok = kk < nkeys;
+    const int kc = key_ok ? kk : 0;
+    const bool cached = kc < a.n;
+    const int kp = !key_ok ? INT_MAX : (cached ? a.pos[(size_t)bg * a.NC + kc] : a.P + (kc - a.n));
+    const bool ex = key_ok && cached && excluded(a, bg, kc);
+    const float* kr = cached ? static_cast<const float*>(a.kc) + ((size_t)bg * a.NC + kc) * D
+                             : static_cast<const float*>(a.kn) + ((size_t)bg * a.S + (kc - a.n)) * D;
+    const float* vr = cached ? static_cast<const float*>(a.vc) + ((size_t)bg * a.NC + kc) * D
+                             : static_cast<const float*>(a.vn) + ((size_t)bg * a.S + (kc - a.n)) * D;
+    float kv[DL], vv[DL], dk[DL], dv[DL];
+#pragma unroll
+    for (int e = 0; e < DL; ++e) {
+        kv[e] = kr[part * DL + e];
+        vv[e] = vr[part * DL + e];
+        dk[e] = 0.f;
+        dv[e] = 0.f;
+    }
+    const float* Q = static_cast<const float*>(a.q);
+    const int R = a.G * a.S;
+    for (int r = 0; r < R; ++r) {
+        const int h = g * a.G + r % a.G, i = r / a.G;
+        const size_t qi = (size_t)(b * a.Hq + h) * a.S + i;
+        const float* qr = Q + qi * D;
+        const float* dr = dout + qi * D;
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) {
+            s = fmaf(qr[part * DL + e], kv[e], s);
+            dp = fmaf(dr[part * DL + e], vv[e], dp);
+        }
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        dp += __shfl_xor(dp, 1);
+        dp += __shfl_xor(dp, 2);
+        if (!(kp >= 0 && kp <= a.P + i) || ex) continue;
+        const float p = expf(s * a.sm_scale - a.lse[qi]);
+        const float ds = p * (dp - drow[qi]);
+#pragma unroll
+        for (int e = 0; e < DL; ++e) {
+            dv[e] = fmaf(p, dr[part * DL + e], dv[e]);
+            dk[e] = fmaf(ds, qr[part * DL + e], dk[e]);
+        }
+    }
+    if (!key_ok) return;
+    float* dkr = cached ? dk_cache + ((size_t)bg * a.NC + kc) * D : dk_new + ((size_t)bg * a.S + (kc - a.n)) * D;
+    float* dvr = cached ? dv_cache + ((size_t)bg * a.NC + kc) * D : dv_new + ((size_t)bg * a.S + (kc - a.n)) * D;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) {
+        dkr[part * DL + e] = a.sm_scale * dk[e];
+        dvr[part * DL + e] = dv[e];
+    }
+}
+
+// ------------------------------------------------------------------ bf16 path
+// MFMA layout as in the forward kernels (v_mfma_f32_32x32x16_bf16, lane
+// l = 32*hh + lq): A lane holds A[m = lq][k = 8hh..8hh+7], B lane holds
+// B[k = 8hh..8hh+7][n = lq], C lane holds C[8(r/4) + 4hh + r%4][lq].  An A
+// operand whose rows are read through perm_key puts physical row
+// 16(r/8) + 8hh + r%8 in C register r, i.e. eight consecutive rows per lane
+// and 16-row step -- the k order of a following product's A or B operand.
+// Operands read transposed (column lq, eight consecutive rows) use
+// ds_read_b64_tr_b16: a 16-lane group addresses a 4 x 16 block (row 4-group
+// + j16/4, columns 4*(j16%4)..+3 of its 16) and each lane receives one column
+// of the four rows; two reads, four rows apart, give eight rows.
+constexpr int kBwWaves = 4;
+constexpr int kBwThreads = 64 * kBwWaves;
+constexpr int kBwRowsPerTile = 64;            // dK/dV kernel: query rows per LDS tile
+constexpr int kBwKeysPerBlock = 32 * kBwWaves;
+constexpr int kBwKeysPerTile = 64;            // dQ kernel: keys per LDS tile
+constexpr int kBwRowsPerBlock = 32 * kBwWaves;
+constexpr int kWaitVmcnt0 = 0x0F70;           // s_waitcnt vmcnt(0), others at maximum
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Loads that write LDS are this wave's own as far as the compiler knows: each
+// wave waits for its own before the barrier that publishes them.
+__device__ __forceinline__ void publish() {
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+}
+__device__ __forceinline__ void lds16(Rsrc r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds4(Rsrc r, void* lds, int voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 ld_tr(const unsigned char* p0, const unsigned char* p1) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+// Byte offset, in a row-major tile of RB-byte rows whose 16-byte chunks are
+// XOR-swizzled by swz_k, of row r, 16-byte chunk c, 8-byte half h.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c, int h) {
+    return r * (2 * D) + 16 * (c ^ swz_k<D>(r)) + 8 * h;
+}
+// This lane's two transposed-read offsets for rows 8hh..8hh+7 (plus a multiple
+// of 16) and columns 32*dt + lq: XOR 64*dt selects dt, adding 16*RB moves 16 rows.
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int& o0, int& o1) {
+    const int hh = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
+    const int r = 8 * hh + (j16 >> 2);
+    const int c = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    o0 = tile_off<D>(r, c, j16 & 1);
+    o1 = tile_off<D>(r + 4, c, j16 & 1);
+}
+
+// dQ: one workgroup per 128 packed query rows (row r = i*G + head) of a KV
+// head; each wave keeps its 32 rows' Q and dO (the B operands) in registers
+// and walks the key tiles (K, V staged in LDS): S^T = K Q^T, dP^T = V dO^T,
+// dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.
+template <int D>
+__global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, const float* drow,
+                                                                 const u16* dout, float* dq) {
+    constexpr int KS = D / 16, DT = D / 32, RB = 2 * D;
+    constexpr int TB = kBwKeysPerTile * RB;            // bytes per K or V tile
+    constexpr int LOADS = TB / 1024 / kBwWaves;        // 1 KB loads per wave per tile
+    __shared__ __attribute__((aligned(1024))) unsigned char sK[2][TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV[2][TB];
+
+    const int R = a.G * a.S;
+    const int nrb = (R + kBwRowsPerBlock - 1) / kBwRowsPerBlock;
+    const int total = nrb * a.B * a.Hkv;
+    const int t = xcd_tile(blockIdx.x, total);
+    if (t >= total) return;
+    const int bg = t / nrb, rb = t % nrb;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31, hh = lane >> 5;
+    const int row = rb * kBwRowsPerBlock + wave * 32 + lq;
+    const bool row_ok = row < R;
+    const int i = row_ok ? row / a.G : a.S - 1;
+    const int h = g * a.G + (row_ok ? row % a.G : 0);
+    const size_t qi = (size_t)(b * a.Hq + h) * a.S + i;
+
+    bf16x8 qf[KS], df[KS];
+    {
+        const u16* Q = static_cast<const u16*>(a.q) + qi * D;
+        const u16* dO = dout + qi * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u}, w = {0u, 0u, 0u, 0u};
+            if (row_ok) {
+                v = ld16(Q + 16 * ks + 8 * hh);
+                w = ld16(dO + 16 * ks + 8 * hh);
+            }
+            qf[ks] = as_bf16x8(v);
+            df[ks] = as_bf16x8(w);
+        }
+    }
+    const float c = a.sm_scale * kLog2e;
+    // log2-scaled LSE; +inf for rows past the end makes their weights zero
+    const float lse2 = row_ok ? a.lse[qi] * kLog2e : INFINITY;
+    const float Di = row_ok ? drow[qi] : 0.f;
+
+    const int n = a.n, S = a.S;
+    const int cache_tiles = (n + kBwKeysPerTile - 1) / kBwKeysPerTile;
+    const int last_row = min(R - 1, rb * kBwRowsPerBlock + kBwRowsPerBlock - 1);
+    const int ntiles = cache_tiles + (last_row / a.G) / kBwKeysPerTile + 1;
+    const int wave_row0 = min(R - 1, rb * kBwRowsPerBlock + wave * 32);
+    const int i_wave_min = wave_row0 / a.G;
+    const u16* Kc = static_cast<const u16*>(a.kc) + (size_t)bg * a.NC * D;
+    const u16* Vc = static_cast<const u16*>(a.vc) + (size_t)bg * a.NC * D;
+    const u16* Kn = static_cast<const u16*>(a.kn) + (size_t)bg * S * D;
+    const u16* Vn = static_cast<const u16*>(a.vn) + (size_t)bg * S * D;
+    const uint64_t* exrow = a.excl ? a.excl + (size_t)bg * excl_tiles(a.NC) : nullptr;
+
+    // Tile jt: cache slots 64jt.. (jt < cache_tiles) or chunk keys 64(jt - cache_tiles)..
+    auto tile_first = [&](int jt) { return (jt < cache_tiles ? jt : jt - cache_tiles) * kBwKeysPerTile; };
+    auto tile_valid = [&](int jt) {
+        return min(kBwKeysPerTile, (jt < cache_tiles ? n : S) - tile_first(jt));
+    };
+    auto issue = [&](int stage, int jt) {
+        const bool cache = jt < cache_tiles;
+        const int first = tile_first(jt), valid = tile_valid(jt);
+        const Rsrc rk = make_rsrc((cache ? Kc : Kn) + (size_t)first * D, valid * RB);
+        const Rsrc rv = make_rsrc((cache ? Vc : Vn) + (size_t)first * D, valid * RB);
+#pragma unroll
+        for (int it = 0; it < LOADS; ++it) {
+            const int off = (it * kBwWaves + wave) * 1024 + 16 * lane;
+            const int r = off / RB, cp = (off % RB) / 16;
+            const int go = r * RB + 16 * (cp ^ swz_k<D>(r));
+            lds16(rk, &sK[stage][(it * kBwWaves + wave) * 1024], go);
+            lds16(rv, &sV[stage][(it * kBwWaves + wave) * 1024], go);
+        }
+    };
+    // A operand rows: physical key perm_key(lq) (+32 per sub-tile), k-step ks.
+    const int prow = perm_key(lq);
+    const int kb = prow * RB + 16 * (hh ^ swz_k<D>(prow));
+    int t0, t1;
+    tr_offsets<D>(lane, t0, t1);
+
+    f32x16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
+
+    issue(0, 0);
+    publish();
+    for (int jt = 0; jt < ntiles; ++jt) {
+        const int stage = jt & 1;
+        if (jt + 1 < ntiles) issue(stage ^ 1, jt + 1);
+        const unsigned char* tk = sK[stage];
+        const unsigned char* tv = sV[stage];
+        const bool cache = jt < cache_tiles;
+        const int first = tile_first(jt), valid = tile_valid(jt);
+        const uint64_t ex = (cache && exrow != nullptr) ? exrow[jt] : 0ull;
+        // keys k of the tile with k > lim are not visible to this lane's row
+        const int lim = cache ? valid - 1 : min(valid - 1, i - first);
+        const bool all_vis = ex == 0 && valid == kBwKeysPerTile &&
+                             (cache || first + kBwKeysPerTile - 1 <= i_wave_min);
+        const uint32_t lb = __builtin_amdgcn_perm((uint32_t)(ex >> 32), (uint32_t)ex,
+                                                  hh ? 0x07050301u : 0x06040200u);
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ob = (kb ^ (32 * ks)) + sub * 32 * RB;
+                st = mfma32(as_bf16x8(ld16(tk + ob)), qf[ks], st);
+                dpt = mfma32(as_bf16x8(ld16(tv + ob)), df[ks], dpt);
+            }
+            // ds^T for this lane's keys 32*sub + 16*(r/8) + 8*hh + r%8 and its row
+            float dsv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+                float p = fast_exp2(fmaf(st[r], c, -lse2));
+                if (!all_vis && (kk > lim || ((lb >> (16 * sub + r)) & 1u))) p = 0.f;
+                dsv[r] = p * (dpt[r] - Di);
+            }
+            bf16x8 dsb[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                dsb[s2] = as_bf16x8(u32x4{pack2(dsv[8 * s2 + 0], dsv[8 * s2 + 1]),
+                                          pack2(dsv[8 * s2 + 2], dsv[8 * s2 + 3]),
+                                          pack2(dsv[8 * s2 + 4], dsv[8 * s2 + 5]),
+                                          pack2(dsv[8 * s2 + 6], dsv[8 * s2 + 7])});
+            // dQ^T += K^T dS^T: K^T columns d = 32*dt + lq, keys 32*sub + 16*s2 + 8*hh..
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int rows = (sub * 32 + 16 * s2) * RB;
+                    const bf16x8 kt = ld_tr(tk + ((t0 + rows) ^ (64 * dt)), tk + ((t1 + rows) ^ (64 * dt)));
+                    o[dt] = mfma32(kt, dsb[s2], o[dt]);
+                }
+        }
+        publish();
+    }
+    if (!row_ok) return;
+    // o[dt][r] = dQ^T[d = 32dt + 8(r/4) + 4hh + r%4][row lq]
+    float* out = dq + qi * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            float4 w;
+            w.x = a.sm_scale * o[dt][4 * r4 + 0];
+            w.y = a.sm_scale * o[dt][4 * r4 + 1];
+            w.z = a.sm_scale * o[dt][4 * r4 + 2];
+            w.w = a.sm_scale * o[dt][4 * r4 + 3];
+            *reinterpret_cast<float4*>(out + 32 * dt + 8 * r4 + 4 * hh) = w;
+        }
+}
+
+// dK, dV: one workgroup per 128 keys of a KV head (cache slots or chunk keys);
+// each wave keeps its 32 keys' K and V (the B operands) in registers and walks
+// the packed query rows in 64-row tiles (Q, dO, LSE, D staged in LDS):
+// S = Q K^T, dP = dO V^T (rows through perm_key), P, dS = P (dP - D),
+// dV += P^T dO, dK += dS^T Q.
+template <int D>
+__global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint32_t g_magic,
+                          float* dk_new, float* dv_new, float* dk_cache, float* dv_cache) {
+    constexpr int KS = D / 16, DT = D / 32, RB = 2 * D;
+    constexpr int TB = kBwRowsPerTile * RB;
+    constexpr int LOADS = TB / 1024 / kBwWaves;
+    constexpr int ROWS_PER_LOAD = 4096 / RB;
+    __shared__ __attribute__((aligned(1024))) unsigned char sQ[2][TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sD[2][TB];
+    __shared__ __attribute__((aligned(16))) float sL[2][kBwRowsPerTile];
+    __shared__ __attribute__((aligned(16))) float sR[2][kBwRowsPerTile];
+
+    const int n = a.n, S = a.S, G = a.G;
+    const int cache_blocks = (n + kBwKeysPerBlock - 1) / kBwKeysPerBlock;
+    const int nkb = cache_blocks + (S + kBwKeysPerBlock - 1) / kBwKeysPerBlock;
+    const int total = nkb * a.B * a.Hkv;
+    const int t = xcd_tile(blockIdx.x, total);
+    if (t >= total) return;
+    const int bg = t / nkb, kbk = t % nkb;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const bool is_cache = kbk < cache_blocks;
+    const int block_first = (is_cache ? kbk : kbk - cache_blocks) * kBwKeysPerBlock;
+    const int limit = is_cache ? n : S;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lq = lane & 31, hh = lane >> 5;
+    const int first = block_first + wave * 32;
+    const int key = first + lq;                          // this lane's key (B operand column)
+
+    bf16x8 kf[KS], vf[KS];
+    {
+        const u16* Ks = is_cache ? static_cast<const u16*>(a.kc) + (size_t)bg * a.NC * D
+                                 : static_cast<const u16*>(a.kn) + (size_t)bg * S * D;
+        const u16* Vs = is_cache ? static_cast<const u16*>(a.vc) + (size_t)bg * a.NC * D
+                                 : static_cast<const u16*>(a.vn) + (size_t)bg * S * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u}, w = {0u, 0u, 0u, 0u};
+            if (key < limit) {
+                v = ld16(Ks + (size_t)key * D + 16 * ks + 8 * hh);
+                w = ld16(Vs + (size_t)key * D + 16 * ks + 8 * hh);
+            }
+            kf[ks] = as_bf16x8(v);
+            vf[ks] = as_bf16x8(w);
+        }
+    }
+
+    const int R = G * S;
+    const int ntile = (R + kBwRowsPerTile - 1) / kBwRowsPerTile;
+    const int tile0 = is_cache ? 0 : (block_first * G) / kBwRowsPerTile;
+    const u16* Qg = static_cast<const u16*>(a.q) + (size_t)(b * a.Hq + g * G) * S * D;
+    const u16* Dg = dout + (size_t)(b * a.Hq + g * G) * S * D;
+    const float* Lg = a.lse + (size_t)(b * a.Hq + g * G) * S;
+    const float* Rg = drow + (size_t)(b * a.Hq + g * G) * S;
+    const int q_bytes = G * S * D * 2;
+    auto row_split = [&](int r, int& hl, int& ipos) {
+        ipos = G == 1 ? r : (int)__umulhi((uint32_t)r, g_magic);
+        hl = r - ipos * G;
+    };
+    const int rl_base = (wave * 1024 + 16 * lane) / RB;
+    const int cp = (16 * lane % RB) / 16;
+    auto issue = [&](int stage, int rt) {
+        const Rsrc rq = make_rsrc(Qg, q_bytes), rd = make_rsrc(Dg, q_bytes);
+#pragma unroll
+        for (int it = 0; it < LOADS; ++it) {
+            const int rl = rl_base + it * ROWS_PER_LOAD;
+            const int r = rt * kBwRowsPerTile + rl;
+            int hl = 0, ipos = 0;
+            row_split(min(r, R - 1), hl, ipos);
+            const int off = r < R ? ((hl * S + ipos) * D) * 2 + 16 * (cp ^ swz_k<D>(rl)) : q_bytes;
+            lds16(rq, &sQ[stage][(it * kBwWaves + wave) * 1024], off);
+            lds16(rd, &sD[stage][(it * kBwWaves + wave) * 1024], off);
+        }
+        if (wave == 0) {
+            const int r = rt * kBwRowsPerTile + lane;
+            int hl = 0, ipos = 0;
+            row_split(min(r, R - 1), hl, ipos);
+            const int off = r < R ? (hl * S + ipos) * 4 : G * S * 4;
+            lds4(make_rsrc(Lg, G * S * 4), &sL[stage][0], off);
+            lds4(make_rsrc(Rg, G * S * 4), &sR[stage][0], off);
+        }
+    };
+    const float c = a.sm_scale * kLog2e;
+    const int prow = perm_key(lq);
+    const int qb = prow * RB + 16 * (hh ^ swz_k<D>(prow));
+    int t0, t1;
+    tr_offsets<D>(lane, t0, t1);
+
+    f32x16 dk[DT], dv[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        dk[dt] = f32x16{};
+        dv[dt] = f32x16{};
+    }
+    const int kmax = min(first + 31, limit - 1);
+    issue(0, tile0);
+    publish();
+    for (int rt = tile0; rt < ntile; ++rt) {
+        const int stage = (rt - tile0) & 1;
+        if (rt + 1 < ntile) issue(stage ^ 1, rt + 1);
+        const unsigned char* tq = sQ[stage];
+        const unsigned char* td = sD[stage];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            f32x16 st = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ob = (qb ^ (32 * ks)) + sub * 32 * RB;
+                st = mfma32(as_bf16x8(ld16(tq + ob)), kf[ks], st);
+                dp = mfma32(as_bf16x8(ld16(td + ob)), vf[ks], dp);
+            }
+            // rows 32*sub + 16*(r/8) + 8*hh + r%8 of the tile, this lane's key
+            const int r0 = rt * kBwRowsPerTile + 32 * sub;
+            const int i0 = G == 1 ? min(r0, R - 1) : (int)__umulhi((uint32_t)min(r0, R - 1), g_magic);
+            const bool full = is_cache || kmax <= i0;
+            float pv[16], dsv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+                const int rr = rt * kBwRowsPerTile + rl;
+                const float l2 = rr < R ? sL[stage][rl] * kLog2e : INFINITY;
+                float p = fast_exp2(fmaf(st[r], c, -l2));
+                if (!full) {
+                    const int ipos = G == 1 ? rr : (int)__umulhi((uint32_t)rr, g_magic);
+                    if (key > ipos) p = 0.f;
+                }
+                pv[r] = p;
+                dsv[r] = p * (dp[r] - sR[stage][rl]);
+            }
+            bf16x8 pb[2], db[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                pb[s2] = as_bf16x8(u32x4{pack2(pv[8 * s2 + 0], pv[8 * s2 + 1]), pack2(pv[8 * s2 + 2], pv[8 * s2 + 3]),
+                                         pack2(pv[8 * s2 + 4], pv[8 * s2 + 5]), pack2(pv[8 * s2 + 6], pv[8 * s2 + 7])});
+                db[s2] = as_bf16x8(u32x4{pack2(dsv[8 * s2 + 0], dsv[8 * s2 + 1]), pack2(dsv[8 * s2 + 2], dsv[8 * s2 + 3]),
+                                         pack2(dsv[8 * s2 + 4], dsv[8 * s2 + 5]), pack2(dsv[8 * s2 + 6], dsv[8 * s2 + 7])});
+            }
+            // dV += P^T dO, dK += dS^T Q: B operands dO / Q columns 32*dt + lq,
+            // rows 32*sub + 16*s2 + 8*hh.. of the tile, read transposed.
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int rows = (sub * 32 + 16 * s2) * RB;
+                    const int o0 = (t0 + rows) ^ (64 * dt), o1 = (t1 + rows) ^ (64 * dt);
+                    dv[dt] = mfma32(pb[s2], ld_tr(td + o0, td + o1), dv[dt]);
+                    dk[dt] = mfma32(db[s2], ld_tr(tq + o0, tq + o1), dk[dt]);
+                }
+        }
+        publish();
+    }
+    // dk[dt][r] = dK[key first + 8(r/4) + 4hh + r%4][d = 32dt + lq]
+    float* dkb = is_cache ? dk_cache + (size_t)bg * a.NC * D : dk_new + (size_t)bg * S * D;
+    float* dvb = is_cache ? dv_cache + (size_t)bg * a.NC * D : dv_new + (size_t)bg * S * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int kk = first + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (kk >= limit) continue;
+        const bool ex = is_cache && a.excl != nullptr &&
+                        ((a.excl[(size_t)bg * excl_tiles(a.NC) + kk / 64] >> (kk % 64)) & 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            dkb[(size_t)kk * D + 32 * dt + lq] = ex ? 0.f : a.sm_scale * dk[dt][r];
+            dvb[(size_t)kk * D + 32 * dt + lq] = ex ? 0.f : dv[dt][r];
+        }
+    }
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int Hq, int S) {
+    return ((size_t)B * Hq * S * sizeof(float) + 255) / 256 * 256;
+}
+
+hipError_t launch_backward_f32(const ChunkArgs& a, const void* out, const void* dout,
+                               float* drow, float* dq, float* dk_new, float* dv_new,
+                               float* dk_cache, float* dv_cache, hipStream_t s) {
+    const int rows = a.B * a.Hq * a.S;
+    hipLaunchKernelGGL(rowdot_kernel<float>, dim3((rows + 15) / 16), dim3(256), 0, s,
+                       static_cast<const float*>(out), static_cast<const float*>(dout), drow,
+                       rows, a.D);
+    const float* dO = static_cast<const float*>(dout);
+    const int nrb = (a.G * a.S + kItems - 1) / kItems;
+    const int nkb = (a.n + a.S + kItems - 1) / kItems;
+    if (a.D == 128) {
+        hipLaunchKernelGGL(bwd_dq_f32_kernel<128>, dim3(nrb * a.B * a.Hkv), dim3(kThreads), 0, s, a,
+                           drow, dO, dq);
+        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, dim3(nkb * a.B * a.Hkv), dim3(kThreads), 0, s,
+                           a, drow, dO, dk_new, dv_new, dk_cache, dv_cache);
+    } else {
+        hipLaunchKernelGGL(bwd_dq_f32_kernel<64>, dim3(nrb * a.B * a.Hkv), dim3(kThreads), 0, s, a,
+                           drow, dO, dq);
+        hipLaunchKernelGGL(bwd_dkdv_f32_kernel<64>, dim3(nkb * a.B * a.Hkv), dim3(kThreads), 0, s,
+                           a, drow, dO, dk_new, dv_new, dk_cache, dv_cache);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void* dout,
+                                float* drow, float* dq, float* dk_new, float* dv_new,
+                                float* dk_cache, float* dv_cache, hipStream_t s) {
+    const int rows = a.B * a.Hq * a.S;
+    hipLaunchKernelGGL(rowdot_kernel<u16>, dim3((rows + 15) / 16), dim3(256), 0, s,
+                       static_cast<const u16*>(out), static_cast<const u16*>(dout), drow, rows,
+                       a.D);
+    const u16* dO = static_cast<const u16*>(dout);
+    const int nrb = (a.G * a.S + kBwRowsPerBlock - 1) / kBwRowsPerBlock;
+    const int nkb = (a.n + kBwKeysPerBlock - 1) / kBwKeysPerBlock +
+                    (a.S + kBwKeysPerBlock - 1) / kBwKeysPerBlock;
+    const uint32_t magic = a.G > 1 ? (uint32_t)((0x100000000ull + a.G - 1) / a.G) : 0u;
+    const dim3 gq(xcd_grid(nrb * a.B * a.Hkv)), gk(xcd_grid(nkb * a.B * a.Hkv));
+    if (a.D == 128) {
+        hipLaunchKernelGGL(bwd_dq_bf16_kernel<128>, gq, dim3(kBwThreads), 0, s, a, drow, dO, dq);
+        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<128>, gk, dim3(kBwThreads), 0, s, a, drow, dO,
+                           magic, dk_new, dv_new, dk_cache, dv_cache);
+    } else {
+        hipLaunchKernelGGL(bwd_dq_bf16_kernel<64>, gq, dim3(kBwThreads), 0, s, a, drow, dO, dq);
+        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<64>, gk, dim3(kBwThreads), 0, s, a, drow, dO,
+                           magic, dk_new, dv_new, dk_cache, dv_cache);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace h2o

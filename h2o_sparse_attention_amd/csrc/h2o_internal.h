@@ -65,6 +65,15 @@ hipError_t launch_select(const EvictArgs& a, hipStream_t s);
 hipError_t launch_build_excl(const ChunkArgs& a, uint64_t* excl, hipStream_t s);
 hipError_t launch_insert(const EvictArgs& a, hipStream_t s);
 
+// Backward of the chunk attention (fp32 gradients).  drow: B*Hq*S floats.
+size_t backward_workspace_bytes(int B, int Hq, int S);
+hipError_t launch_backward_f32(const ChunkArgs& a, const void* out, const void* dout,
+                               float* drow, float* dq, float* dk_new, float* dv_new,
+                               float* dk_cache, float* dv_cache, hipStream_t s);
+hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void* dout,
+                                float* drow, float* dq, float* dk_new, float* dv_new,
+                                float* dk_cache, float* dv_cache, hipStream_t s);
+
 // Decode (S = 1) specialisation.
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int NC);
 hipError_t launch_decode(const ChunkArgs& a, void* ws, hipStream_t s);

@@ -230,6 +230,35 @@ H2O_API h2o_status_t h2o_evict_and_insert_lastrec(const h2o_dims_t *dims, h2o_ca
                                           const void *v_new, int32_t *freed_slots,
                                           void *stream);
 
+/*
+ * Backward of the chunk attention (pass 1 of h2o_chunk_attn or h2o_buffer_attn)
+ * with the cache decisions fixed: the policy's choices are replayed, not
+ * differentiated ("Gradient Computation Strategy", item 1), so the keys and
+ * the mask are those of the forward call and the gradient is that of masked
+ * softmax attention.  Inputs: the cache as it stood for the forward call (K,
+ * V, pos, n_valid), chunk_start, chunk_len, sm_scale, q, k_new, v_new, that
+ * call's out and lse, dout = dL/dout ([B][Hq][S][d], dtype), and freed_slots
+ * (NULL, or the h2o_buffer_attn targets: those slots are not keys).  With
+ * m = softmax over the visible keys, D_i = sum_d dout[i,d] out[i,d] and
+ * ds_ij = m_ij (dout_i . v_j - D_i), per query head h and KV head g = h / G:
+ *   dq[b,h,i]        = sm_scale sum_j ds_ij k_j               [B][Hq][S][d]
+ *   dk_cache[b,g,j]  = sm_scale sum_{h in g} sum_i ds_ij q_i  [B][Hkv][N_C][d]
+ *   dv_cache[b,g,j]  = sum_{h in g} sum_i m_ij dout_i         [B][Hkv][N_C][d]
+ *   dk_new, dv_new   the same for the chunk's own keys       [B][Hkv][S][d]
+ * All gradients are float32; dk_cache and dv_cache are 0 for j >= n_valid and
+ * at excluded slots.  bf16: MFMA inputs bf16 (the weights and ds rounded to
+ * bf16 for their products), accumulation fp32.  The workspace must hold
+ * h2o_backward_workspace_bytes(dims, chunk_len) bytes.
+ */
+H2O_API size_t h2o_backward_workspace_bytes(const h2o_dims_t *dims, int32_t chunk_len);
+H2O_API h2o_status_t h2o_chunk_attn_backward(const h2o_dims_t *dims, const h2o_cache_t *cache,
+                                     int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                                     const void *q, const void *k_new, const void *v_new,
+                                     const void *out, const float *lse, const void *dout,
+                                     const int32_t *freed_slots, float *dq, float *dk_new,
+                                     float *dv_new, float *dk_cache, float *dv_cache,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 H2O_API const char *h2o_last_error(void);
 
@@ -251,7 +280,8 @@ typedef enum {
     H2O_KERNEL_INSERT = 4,    /* chunk insertion                                */
     H2O_KERNEL_DECODE = 5,    /* S = 1 attention (split over slots)             */
     H2O_KERNEL_DECODE_FINISH = 6, /* S = 1: merge of the splits, summed weights */
-    H2O_KERNEL_COUNT = 7
+    H2O_KERNEL_BACKWARD = 7,  /* backward of the chunk attention (all its launches) */
+    H2O_KERNEL_COUNT = 8
 } h2o_kernel_id_t;
 
 H2O_API h2o_status_t h2o_kernel_timer_start(int32_t kernel, int32_t max_launches);
