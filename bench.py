@@ -276,6 +276,84 @@ def run_decode(args):
     print(json.dumps(line), flush=True)
 
 
+BACKWARD_METRIC = "H2O chunk-attn backward TFLOP/s (chunk 1k, cache 8192, steady chunk), % roofline"
+
+
+def run_backward(args):
+    """Backward of one steady chunk (full cache) repeated: the gradients of the chunk
+    attention w.r.t. q, the chunk's k/v and the cached slots' k/v."""
+    import torch
+
+    import h2o_sparse_attention_amd as h2o
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dims = h2o.H2ODims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity,
+                       wl.recent_window, wl.dtype)
+    dt = dims.torch_dtype
+    c = 16
+    s = W.steady_state(wl, 0, start=c * wl.chunk)
+    x = W.chunk_inputs(wl, 0, c)
+    cache = h2o.H2OCache(dims, dev)
+    cache.load(torch.from_numpy(s["k"]).to(dev, dt), torch.from_numpy(s["v"]).to(dev, dt),
+               torch.from_numpy(s["pos"]).to(dev), torch.from_numpy(s["phi"]).to(dev),
+               s["n"], s["start"])
+    q, k, v = (torch.from_numpy(x[key]).to(dev, dt) for key in ("q", "k", "v"))
+    B, Hq, Hkv, D, NC, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity, wl.chunk
+    P = s["start"]
+    out, lse, _, _ = h2o.chunk_attn(cache, P, q, k, v, wl.sm_scale, summed_weights=False)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    dout = torch.randn(B, Hq, S, D, generator=g).to(dev, dt)
+    grads = {"dq": torch.empty(B, Hq, S, D, device=dev), "dk_new": torch.empty(B, Hkv, S, D, device=dev),
+             "dv_new": torch.empty(B, Hkv, S, D, device=dev),
+             "dk_cache": torch.empty(B, Hkv, NC, D, device=dev),
+             "dv_cache": torch.empty(B, Hkv, NC, D, device=dev)}
+    ws = torch.empty(int(h2o.lib.h2o_backward_workspace_bytes(ctypes_byref(dims), S)),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        h2o.chunk_attn_backward(cache, P, q, k, v, out, lse, dout, wl.sm_scale, grads=grads,
+                                workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = h2o.KernelTimer("backward", args.steps)
+    with timer:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    pairs = pairs_per_head(NC, S)
+    flops = 10.0 * D * Hq * B * pairs         # QK^T recompute, dP, dQ, dK, dV
+    ms = elapsed / args.steps * 1e3
+    tflops = flops / (ms * 1e-3) / 1e12
+    achieved = flops / (timer.mean_ms * 1e-3) / 1e12
+    line = {
+        "metric": BACKWARD_METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name + " steady chunk backward", "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "capacity": NC, "chunk": S,
+                   "parallelism": "single-gpu"},
+        "timing": "eager",
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "h2o_chunk_attn_backward (row-dot, dQ, dK/dV)",
+                     "launches": timer.launches, "mean_launch_us": round(timer.mean_ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def ctypes_byref(dims):
+    import ctypes
+    return ctypes.byref(dims.c())
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,6 +369,8 @@ def main():
     ap.add_argument("--policy", choices=("h2o", "h2o_buffer", "lastrec"), default="h2o",
                     help="h2o: attend, then evict; h2o_buffer: the insert-first buffer form; "
                          "lastrec: keep the first --sink and the most recent tokens")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of a steady chunk instead of the forward sequence")
     ap.add_argument("--sink", type=int, default=64,
                     help="lastrec: leading tokens kept (beta); the pages give no value")
     args = ap.parse_args()
@@ -307,6 +387,8 @@ def main():
     wl = W.WORKLOADS[args.workload]
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
+    if args.backward:
+        return run_backward(args)
     if wl.decode:
         return run_decode(args)
     assert wl.layers == 1, "bench runs a single-layer prefill workload"
