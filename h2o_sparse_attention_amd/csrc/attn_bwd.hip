@@ -344,13 +344,29 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
                                                   hh ? 0x07050301u : 0x06040200u);
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-            f32x16 st = f32x16{}, dpt = f32x16{};
+            bf16x8 ka[KS], va[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ob = (kb ^ (32 * ks)) + sub * 32 * RB;
-                st = mfma32(as_bf16x8(ld16(tk + ob)), qf[ks], st);
-                dpt = mfma32(as_bf16x8(ld16(tv + ob)), df[ks], dpt);
+                ka[ks] = as_bf16x8(ld16(tk + ob));
+                va[ks] = as_bf16x8(ld16(tv + ob));
             }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                st = mfma32(ka[ks], qf[ks], st);
+                dpt = mfma32(va[ks], df[ks], dpt);
+            }
+            bf16x8 ktr[DT][2];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int rows = (sub * 32 + 16 * s2) * RB;
+                    ktr[dt][s2] = ld_tr(tk + ((t0 + rows) ^ (64 * dt)), tk + ((t1 + rows) ^ (64 * dt)));
+                }
+            __builtin_amdgcn_sched_barrier(0);
             // ds^T for this lane's keys 32*sub + 16*(r/8) + 8*hh + r%8 and its row
             float dsv[16];
 #pragma unroll
@@ -371,11 +387,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int rows = (sub * 32 + 16 * s2) * RB;
-                    const bf16x8 kt = ld_tr(tk + ((t0 + rows) ^ (64 * dt)), tk + ((t1 + rows) ^ (64 * dt)));
-                    o[dt] = mfma32(kt, dsb[s2], o[dt]);
-                }
+                for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma32(ktr[dt][s2], dsb[s2], o[dt]);
         }
         publish();
     }
@@ -505,30 +517,61 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
         const unsigned char* td = sD[stage];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-            f32x16 st = f32x16{}, dp = f32x16{};
+            // One wave per SIMD: issue each phase's LDS operand reads together, so
+            // their latency is paid once, not once per MFMA.
+            bf16x8 qa[KS], da[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ob = (qb ^ (32 * ks)) + sub * 32 * RB;
-                st = mfma32(as_bf16x8(ld16(tq + ob)), kf[ks], st);
-                dp = mfma32(as_bf16x8(ld16(td + ob)), vf[ks], dp);
+                qa[ks] = as_bf16x8(ld16(tq + ob));
+                da[ks] = as_bf16x8(ld16(td + ob));
             }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 st = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                st = mfma32(qa[ks], kf[ks], st);
+                dp = mfma32(da[ks], vf[ks], dp);
+            }
+            // The transposed operands of dV and dK, read while the VALU works.
+            bf16x8 dtr[DT][2], qtr[DT][2];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int rows = (sub * 32 + 16 * s2) * RB;
+                    const int o0 = (t0 + rows) ^ (64 * dt), o1 = (t1 + rows) ^ (64 * dt);
+                    dtr[dt][s2] = ld_tr(td + o0, td + o1);
+                    qtr[dt][s2] = ld_tr(tq + o0, tq + o1);
+                }
+            __builtin_amdgcn_sched_barrier(0);
             // rows 32*sub + 16*(r/8) + 8*hh + r%8 of the tile, this lane's key
             const int r0 = rt * kBwRowsPerTile + 32 * sub;
             const int i0 = G == 1 ? min(r0, R - 1) : (int)__umulhi((uint32_t)min(r0, R - 1), g_magic);
             const bool full = is_cache || kmax <= i0;
+            // LSE and D of the lane's rows: two runs of eight consecutive rows, read
+            // unconditionally (in LDS bounds); rows past R get LSE = +inf, weight 0.
+            float lr[16], dr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+                lr[r] = sL[stage][rl];
+                dr[r] = sR[stage][rl];
+            }
+            const bool rows_in = rt * kBwRowsPerTile + kBwRowsPerTile <= R;
             float pv[16], dsv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rl = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
                 const int rr = rt * kBwRowsPerTile + rl;
-                const float l2 = rr < R ? sL[stage][rl] * kLog2e : INFINITY;
+                const float l2 = (rows_in || rr < R) ? lr[r] * kLog2e : INFINITY;
                 float p = fast_exp2(fmaf(st[r], c, -l2));
                 if (!full) {
                     const int ipos = G == 1 ? rr : (int)__umulhi((uint32_t)rr, g_magic);
-                    if (key > ipos) p = 0.f;
+                    p = key > ipos ? 0.f : p;
                 }
                 pv[r] = p;
-                dsv[r] = p * (dp[r] - sR[stage][rl]);
+                dsv[r] = p * (dp[r] - dr[r]);
             }
             bf16x8 pb[2], db[2];
 #pragma unroll
@@ -544,10 +587,8 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    const int rows = (sub * 32 + 16 * s2) * RB;
-                    const int o0 = (t0 + rows) ^ (64 * dt), o1 = (t1 + rows) ^ (64 * dt);
-                    dv[dt] = mfma32(pb[s2], ld_tr(td + o0, td + o1), dv[dt]);
-                    dk[dt] = mfma32(db[s2], ld_tr(tq + o0, tq + o1), dk[dt]);
+                    dv[dt] = mfma32(pb[s2], dtr[dt][s2], dv[dt]);
+                    dk[dt] = mfma32(db[s2], qtr[dt][s2], dk[dt]);
                 }
         }
         publish();
