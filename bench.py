@@ -9,6 +9,11 @@ tokens = 64 chunks).  Inputs are resident in HBM before the timed region.
 Prints one JSON line.  `value` is F6 TFLOP/s: 6*d*Hq*(visible query/key pairs),
 i.e. QK^T and PV for the output plus the QK^T recompute for the summed weights.
 
+`--workload 4` runs the 36-layer stack of the same attention shape (cache 8192,
+chunk 1k, 128k tokens): each step pushes one chunk through all 36 layers, each
+layer from its own full cache with its own seeded inputs; `value` is ms per
+chunk across the layers.
+
 `--policy lastrec` runs the same sequence under the lastrec policy (attention
 without summed weights, eviction by position keeping the first `--sink`
 tokens); its `value` is F4 TFLOP/s, the work that policy does.
@@ -349,6 +354,141 @@ def run_backward(args):
     print(json.dumps(line), flush=True)
 
 
+STACK_METRIC = "H2O 36-layer stack ms per chunk across layers (chunk 1k, cache 8192, 128k ctx)"
+
+
+def run_stack(args):
+    """The layer stack: each timed step pushes one chunk through every layer (chunk-major,
+    as a model runs it), each layer with its own full cache and its own seeded inputs.
+    The caches start as steady full caches before the middle chunk of the sequence."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import torch
+
+    import h2o_sparse_attention_amd as h2o
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    dims = h2o.H2ODims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity,
+                       wl.recent_window, wl.dtype)
+    dt = dims.torch_dtype
+    L = wl.layers
+    B, Hq, Hkv, D, NC, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity, wl.chunk
+    c0 = wl.n_chunks // 2
+    n_chunk = args.warmup + args.steps
+    assert c0 + n_chunk <= wl.n_chunks
+    t_gen = time.perf_counter()
+
+    def gen_layer(layer):
+        s = W.steady_state(wl, layer, start=c0 * S, seed=layer)
+        xs = [W.chunk_inputs(wl, layer, c0 + i) for i in range(n_chunk)]
+        return s, xs
+
+    caches, inputs = [], [[None] * L for _ in range(n_chunk)]
+    with ThreadPoolExecutor(8) as pool:
+        for layer, (s, xs) in enumerate(pool.map(gen_layer, range(L))):
+            cache = h2o.H2OCache(dims, dev)
+            cache.load(torch.from_numpy(s["k"]).to(dev, dt), torch.from_numpy(s["v"]).to(dev, dt),
+                       torch.from_numpy(s["pos"]).to(dev), torch.from_numpy(s["phi"]).to(dev),
+                       s["n"], s["start"])
+            caches.append(cache)
+            for i, x in enumerate(xs):
+                inputs[i][layer] = tuple(torch.from_numpy(x[k]).to(dev, dt) for k in ("q", "k", "v"))
+    print(f"[bench] {L} layer caches + {n_chunk} chunks per layer generated in "
+          f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    bufs = {"out": torch.empty(B, Hq, S, D, dtype=dt, device=dev),
+            "lse": torch.empty(B, Hq, S, dtype=torch.float32, device=dev),
+            "colsum_cache": torch.empty(B, Hkv, NC, dtype=torch.float32, device=dev),
+            "colsum_new": torch.empty(B, Hkv, S, dtype=torch.float32, device=dev),
+            "freed_slots": torch.empty(B, Hkv, S, dtype=torch.int32, device=dev),
+            "workspace": torch.empty(max(1, h2o.workspace_bytes(dims, S)), dtype=torch.uint8,
+                                     device=dev)}
+
+    def chunk_through_stack(i):
+        for layer in range(L):
+            q, k, v = inputs[i][layer]
+            h2o.step(caches[layer], q, k, v, wl.sm_scale, bufs=bufs)
+
+    for i in range(args.warmup):
+        chunk_through_stack(i)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    snap = [(c.k.clone(), c.v.clone(), c.pos.clone(), c.score.clone(), c.n_valid, c.next_pos)
+            for c in caches]
+    # Per-kernel means: the timed chunks run eagerly once with the library's kernel timers.
+    kernels = ("attn", "colsum", "update", "select", "insert")
+    timers = {k: h2o.KernelTimer(k, args.steps * L) for k in kernels}
+    for t_ in timers.values():
+        t_.__enter__()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_chunk):
+        chunk_through_stack(i)
+    torch.cuda.synchronize()
+    eager_s = time.perf_counter() - t0
+    for t_ in timers.values():
+        t_.__exit__(None, None, None)
+    elapsed = eager_s
+    if not args.no_graph:
+        # Timed region: the same chunks again from the same cache states, each chunk's
+        # pass through the stack replayed from a HIP graph captured beforehand.
+        ref = [bufs["out"].clone()] + [t for c in caches for t in (c.score.clone(), c.pos.clone())]
+        for c, sn in zip(caches, snap):
+            c.load(*sn)
+        graphs = []
+        for i in range(args.warmup, n_chunk):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                chunk_through_stack(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        got = [bufs["out"]] + [t for c in caches for t in (c.score, c.pos)]
+        check_replay("layer stack", zip(got, ref))
+    ms_chunk = elapsed / args.steps * 1e3
+    pairs = pairs_per_head(NC, S)
+    f6 = 6.0 * D * Hq * B * pairs * L
+    attn = timers["attn"]
+    attn_flops = 4.0 * D * Hq * B * pairs
+    achieved = attn_flops / (attn.mean_ms * 1e-3) / 1e12
+    kernel_us = {k: round(t_.mean_ms * 1e3, 2) for k, t_ in timers.items()}
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
+        c = cpu_baseline(wl, args.cpu_budget)
+        cpu = {"value": round(c["ms_per_chunk"] * L, 1), "unit": "ms per chunk across layers",
+               "cores": c["cores"], "kind": "oracle",
+               "sample": c["sample"] + f"; per-chunk time x {L} layers",
+               "tflops": c["value"]}
+    line = {
+        "metric": STACK_METRIC, "value": round(ms_chunk, 3), "unit": "ms",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_chunk, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "capacity": NC,
+                   "recent_window": wl.recent_window, "chunk": S, "seq_len": wl.seq_len,
+                   "timed_chunks": f"{c0 + args.warmup}..{c0 + n_chunk - 1} (full caches)",
+                   "policy": "h2o", "parallelism": "single-gpu"},
+        "timing": "hip_graph" if not args.no_graph else "eager",
+        "ms_per_step_eager": round(eager_s / args.steps * 1e3, 3),
+        "tokens_per_s": round(B * S / (ms_chunk * 1e-3), 1),
+        "tflops_f6": round(f6 / (ms_chunk * 1e-3) / 1e12, 3),
+        "kernel_mean_us": kernel_us,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_bf16_kernel<128>",
+                     "launches": attn.launches, "mean_launch_us": round(attn.mean_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def ctypes_byref(dims):
     import ctypes
     return ctypes.byref(dims.c())
@@ -391,6 +531,8 @@ def main():
         return run_backward(args)
     if wl.decode:
         return run_decode(args)
+    if wl.layers > 1:
+        return run_stack(args)
     assert wl.layers == 1, "bench runs a single-layer prefill workload"
     dev = torch.device("cuda:0")
     dims = h2o.H2ODims(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity,

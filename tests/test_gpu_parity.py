@@ -184,3 +184,61 @@ def test_decode_steps_full_cache():
     H.load_oracle_state(cache, st, wl.dtype)
     del s
     H.run_chain(wl, range(3), lambda t: W.decode_step_inputs(wl, t), cache=cache, st=st)
+
+
+def test_layer_stack_first_chunks():
+    """36-layer stack workload: the first two chunks (n = 0, 1024) of the last layer,
+    whose inputs come from that layer's own seed."""
+    wl = W.WORKLOADS[4]
+    H.run_chain(wl, range(2), _chunk_getter(wl, layer=wl.layers - 1))
+
+
+def test_layer_stack_interleaved_steady():
+    """36-layer stack workload, chunk-major as a model runs it: layers 0, 17 and 35,
+    each from its own full cache (its own seed), take chunks 64 and 65 in turn through
+    one shared set of output and workspace buffers; each layer is compared with its
+    own oracle state after every chunk."""
+    wl = W.WORKLOADS[4]
+    layers = (0, 17, wl.layers - 1)
+    dt = H.TORCH_DT[wl.dtype]
+    c0 = 64
+    caches, states = {}, {}
+    for layer in layers:
+        s = W.steady_state(wl, layer, start=c0 * wl.chunk, seed=layer)
+        states[layer] = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"],
+                                                    s["n"], s["start"])
+        caches[layer] = h2o.H2OCache(H.dims_of(wl), H.DEV)
+        H.load_oracle_state(caches[layer], states[layer], wl.dtype)
+    B, Hq, Hkv, D, NC, S = (wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.capacity,
+                            wl.chunk)
+    bufs = {"out": torch.empty(B, Hq, S, D, dtype=dt, device=H.DEV),
+            "lse": torch.empty(B, Hq, S, dtype=torch.float32, device=H.DEV),
+            "colsum_cache": torch.empty(B, Hkv, NC, dtype=torch.float32, device=H.DEV),
+            "colsum_new": torch.empty(B, Hkv, S, dtype=torch.float32, device=H.DEV),
+            "freed_slots": torch.empty(B, Hkv, S, dtype=torch.int32, device=H.DEV),
+            "workspace": torch.empty(max(1, h2o.workspace_bytes(H.dims_of(wl), S)),
+                                     dtype=torch.uint8, device=H.DEV)}
+    for c in (c0, c0 + 1):
+        for layer in layers:
+            cache, st = caches[layer], states[layer]
+            where = f"layer {layer} chunk {c}:"
+            x = W.chunk_inputs(wl, layer, c)
+            n_before, pos_before, P = st.n, st.pos.copy(), st.P
+            assert cache.next_pos == P == c * S
+            got = h2o.step(cache, H.dev(x["q"], dt), H.dev(x["k"], dt), H.dev(x["v"], dt),
+                           wl.sm_scale, bufs=bufs)
+            torch.cuda.synchronize()
+            g = {key: H.host(t) for key, t in got.items()}
+            r = oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window)
+            H.compare_attention(g, r, n_before, wl.dtype, where)
+            swaps = H.compare_victims(g["freed_slots"].astype(np.int64), r["freed_slots"],
+                                      r["phi_updated"], pos_before, n_before, P,
+                                      wl.recent_window, where)
+            if swaps:
+                H.load_oracle_state(cache, st, wl.dtype)
+                continue
+            assert (g["freed_slots"] == r["freed_slots"]).all(), f"{where} freed slots"
+            assert (H.host(cache.pos) == st.pos).all(), f"{where} positions"
+            assert torch.equal(cache.k, H.dev(st.K, dt)) and torch.equal(cache.v, H.dev(st.V, dt))
+            e = H.rel_err(H.host(cache.score), st.phi).max()
+            assert e <= H.TOL[wl.dtype]["cs_rel"], f"{where} scores rel {e:.3e}"

@@ -71,3 +71,17 @@ def test_decode_initial_state():
     assert abs(jitter.mean()) < 0.02 and abs(jitter.std() - 0.25) < 0.02
     x = W.decode_step_inputs(wl, 3)
     assert x["q"].shape == (2, 32, 1, 128) and x["start"] == 515
+
+
+def test_layer_stack_layers_draw_independently():
+    """The 36-layer stack: each layer has its own inputs, heavy positions and cache state."""
+    wl = W.workload(4, seq_len=8192, capacity=1024, chunk=256, heavy_count=82)
+    assert W.WORKLOADS[4].layers == 36
+    a, b = W.chunk_inputs(wl, 0, 2), W.chunk_inputs(wl, 35, 2)
+    for key in ("q", "k", "v"):
+        assert a[key].shape == b[key].shape
+        assert np.corrcoef(a[key].ravel(), b[key].ravel())[0, 1] < 0.05
+    ha, hb = W.heavy_boost(wl, 0)[0], W.heavy_boost(wl, 35)[0]
+    assert not np.array_equal(ha, hb)
+    sa, sb = W.steady_state(wl, 0, start=2048), W.steady_state(wl, 35, start=2048)
+    assert not np.array_equal(sa["pos"], sb["pos"]) and not np.array_equal(sa["k"], sb["k"])
