@@ -664,8 +664,9 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
 
     // One stage: 8 MFMAs of (sQm, subm) into the result, interleaved with the
     // exponentials of sv (fully visible) or followed by the masked form.
-    auto stage = [&](const unsigned char* sQm, int subm, const f32x16& sv, float lse2,
-                     bool full, int rt_e, int sub_e, bool do_mfma) {
+    auto stage = [&](auto mfma_c, const unsigned char* sQm, int subm, const f32x16& sv,
+                     float lse2, bool full, int rt_e, int sub_e) {
+        constexpr bool do_mfma = decltype(mfma_c)::value;
         f32x16 r = f32x16{};
         if (full) {
             bf16x8 qr[2];
@@ -710,12 +711,15 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
         const bool has_next = rt + 1 < t_hi;
         const float l0 = lse2_of(lc, rt, 0), l1 = lse2_of(lc, rt, 1);
         // A: MFMAs of (rt, 1) with the exponentials of (rt, 0).
-        const f32x16 s1 = stage(qc, 1, s0, l0, full_tile(rt, 0), rt, 0, true);
+        const f32x16 s1 = stage(std::true_type{}, qc, 1, s0, l0, full_tile(rt, 0), rt, 0);
         publish_lds_loads();
         // B: loads of tile rt+2 into tile rt's buffer; MFMAs of (rt+1, 0) with
         // the exponentials of (rt, 1).
         if (rt + 2 < t_hi) issue(qc, lc, rt + 2);
-        s0 = stage(qn, 0, s1, l1, full_tile(rt, 1), rt, 1, has_next);
+        // (the MFMA flag is a template argument: as a runtime flag it split the
+        // MFMAs into conditional blocks ahead of all the exponentials)
+        if (has_next) s0 = stage(std::true_type{}, qn, 0, s1, l1, full_tile(rt, 1), rt, 1);
+        else stage(std::false_type{}, qn, 0, s1, l1, full_tile(rt, 1), rt, 1);
         (void)ln;
     };
     for (int rt = t_lo; rt < t_hi; rt += 2) {
