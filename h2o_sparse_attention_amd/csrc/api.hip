@@ -181,6 +181,15 @@ h2o_status_t evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_
     a.score_mode = mode;
     a.sink = sink;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (do_select && do_insert && k == 1 && S == 1) {
+        // one victim and one token: one launch, timed as the selection
+        timer_begin(H2O_KERNEL_SELECT, s);
+        hipError_t e = launch_select1_insert(a, s);
+        timer_end(H2O_KERNEL_SELECT, s);
+        if ((st = check_hip(e, "select/insert launch")) != H2O_OK) return st;
+        cache->n_valid = NC;
+        return ok();
+    }
     if (do_select) {
         timer_begin(H2O_KERNEL_SELECT, s);
         hipError_t e = launch_select(a, s);

@@ -330,6 +330,84 @@ __global__ __launch_bounds__(256) void insert_kernel(EvictArgs a) {
     }
 }
 
+// --------------------------------------------------- one victim, one token
+// k = 1 and S = 1 (a decode step on a full cache): the victim is the smallest
+// (key, slot) pair under the same order keys as select_kernel, found in one
+// pass of 16-byte loads and a reduction, and the same workgroup writes the new
+// token into it.  Same victims and cache contents as select_kernel followed by
+// insert_kernel, in one launch instead of two.
+constexpr int kOneThreads = 1024;
+constexpr int kOneLoads = 4;                     // 16-byte loads in flight per array
+
+__global__ __launch_bounds__(kOneThreads) void select1_insert_kernel(EvictArgs a) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    __shared__ uint64_t sBest[kOneThreads / 64];
+    const int bg = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = a.n, NC = a.NC;
+    const float* sc = a.score + (size_t)bg * NC;
+    const int32_t* ps = a.pos + (size_t)bg * NC;
+    const int thr = a.P - a.W;                   // eligible iff t(j) < P - W
+    const int t_now = a.P + 1;
+    const bool need_score = a.score_mode != kModeLastrec;
+    const dev::Rsrc rs = dev::make_rsrc(sc, n * 4), rp = dev::make_rsrc(ps, n * 4);
+    uint64_t best = ~0ull;
+    for (int base = 0; base < n; base += 4 * kOneThreads * kOneLoads) {
+        u32x4 s4[kOneLoads], p4[kOneLoads];
+#pragma unroll
+        for (int u = 0; u < kOneLoads; ++u) {
+            const int j = base + 4 * (u * kOneThreads + tid);
+            s4[u] = need_score ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              rs, j * 4, 0, 0))
+                               : u32x4{0u, 0u, 0u, 0u};
+            p4[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, j * 4, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < kOneLoads; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = base + 4 * (u * kOneThreads + tid) + e;
+                const int pj = (int)p4[u][e];
+                uint32_t kv;
+                if (a.score_mode == kModeLastrec) {
+                    kv = j >= n ? kAbsent : (pj >= a.sink ? (uint32_t)pj : kIneligible);
+                } else {
+                    float v = __uint_as_float(s4[u][e]);
+                    if (a.score_mode == H2O_SCORE_H2O_NORM) v = v / (float)(t_now - pj);
+                    kv = j >= n ? kAbsent : (pj < thr ? order_key(v) : kIneligible);
+                }
+                const uint64_t key = ((uint64_t)kv << 32) | (uint32_t)j;
+                best = key < best ? key : best;
+            }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t o = __shfl_xor(best, off);
+        best = o < best ? o : best;
+    }
+    if (lane == 0) sBest[wave] = best;
+    __syncthreads();
+    uint64_t m = sBest[0];
+#pragma unroll
+    for (int w = 1; w < kOneThreads / 64; ++w) m = sBest[w] < m ? sBest[w] : m;
+    const int victim = (int)(uint32_t)m;
+    // The new token into the victim's slot.
+    const int units = a.D * a.elem_bytes / 16;    // 16-byte units per row
+    u32x4* kc = static_cast<u32x4*>(a.kc) + ((size_t)bg * NC + victim) * units;
+    u32x4* vc = static_cast<u32x4*>(a.vc) + ((size_t)bg * NC + victim) * units;
+    const u32x4* kn = static_cast<const u32x4*>(a.kn) + (size_t)bg * units;
+    const u32x4* vn = static_cast<const u32x4*>(a.vn) + (size_t)bg * units;
+    for (int u = tid; u < units; u += kOneThreads) {
+        kc[u] = kn[u];
+        vc[u] = vn[u];
+    }
+    if (tid == 0) {
+        a.freed[bg] = victim;
+        a.pos[(size_t)bg * NC + victim] = a.P;
+        a.score[(size_t)bg * NC + victim] = a.cs_new ? a.cs_new[bg] : 0.f;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_update_scores(float* score, const float* cs, int rows, int NC, int n,
@@ -392,6 +470,11 @@ hipError_t launch_build_excl(const ChunkArgs& a, uint64_t* excl, hipStream_t s) 
 hipError_t launch_insert(const EvictArgs& a, hipStream_t s) {
     const dim3 grid((a.S + kInsTokens - 1) / kInsTokens, a.B * a.Hkv), block(256);
     hipLaunchKernelGGL(insert_kernel, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_select1_insert(const EvictArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(select1_insert_kernel, dim3(a.B * a.Hkv), dim3(kOneThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -64,6 +64,8 @@ hipError_t launch_select(const EvictArgs& a, hipStream_t s);
 // excl[bg][t] = bits of the victims (freed slots below n) among slots 64t .. 64t+63.
 hipError_t launch_build_excl(const ChunkArgs& a, uint64_t* excl, hipStream_t s);
 hipError_t launch_insert(const EvictArgs& a, hipStream_t s);
+// k = 1 and S = 1 (decode on a full cache): selection and insertion in one launch.
+hipError_t launch_select1_insert(const EvictArgs& a, hipStream_t s);
 
 // Backward of the chunk attention (fp32 gradients).  drow: B*Hq*S floats.
 size_t backward_workspace_bytes(int B, int Hq, int S);

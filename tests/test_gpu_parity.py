@@ -242,3 +242,38 @@ def test_layer_stack_interleaved_steady():
             assert torch.equal(cache.k, H.dev(st.K, dt)) and torch.equal(cache.v, H.dev(st.V, dt))
             e = H.rel_err(H.host(cache.score), st.phi).max()
             assert e <= H.TOL[wl.dtype]["cs_rel"], f"{where} scores rel {e:.3e}"
+
+
+@pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
+def test_decode_one_victim_fused_matches_separate(score_mode):
+    """A decode step on a full cache takes one launch for selection and insertion; it
+    gives bit for bit what the separate selection and insertion calls give, and the
+    oracle's victim, with 20% of the scores set to three shared values (ties)."""
+    wl = W.workload(5, batch=4)
+    s = W.decode_initial_state(wl)
+    phi = s["phi"].copy()
+    r = np.random.default_rng(11)
+    levels = np.sort(phi.reshape(-1))[[100, 1000, 4000]]
+    mask = r.random(phi.shape) < 0.2
+    phi[mask] = levels[r.integers(0, 3, mask.sum())]
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], phi, s["n"], s["start"])
+    fused, sep = (h2o.H2OCache(H.dims_of(wl), H.DEV) for _ in range(2))
+    for c in (fused, sep):
+        H.load_oracle_state(c, st, wl.dtype)
+    for t in range(3):
+        x = W.decode_step_inputs(wl, t)
+        P = fused.next_pos
+        k, v = H.dev(x["k"], torch.bfloat16), H.dev(x["v"], torch.bfloat16)
+        cs_new = H.dev(r.random((wl.batch, wl.n_kv_heads, 1)).astype(np.float32), torch.float32)
+        f1 = h2o.evict_and_insert(fused, P, k, v, cs_new, score_mode=score_mode)
+        f2 = h2o.select_slots(sep, P, 1, score_mode=score_mode)
+        h2o.insert(sep, P, k, v, f2, cs_new)
+        torch.cuda.synchronize()
+        victims = oracle.select_victims(st, 1, wl.recent_window, score_mode)
+        oracle.evict_and_insert(st, victims, x["k"], x["v"], H.host(cs_new))
+        assert (H.host(f1) == victims).all(), f"step {t}: fused victim"
+        assert torch.equal(f1, f2), f"step {t}: victims"
+        for name in ("k", "v", "pos", "score"):
+            assert torch.equal(getattr(fused, name), getattr(sep, name)), f"step {t}: {name}"
+        assert (H.host(fused.pos) == st.pos).all()
+        assert fused.n_valid == sep.n_valid == st.n
