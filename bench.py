@@ -163,6 +163,79 @@ def check_replay(name, pairs):
             sys.exit(3)
 
 
+def steady_chunk(wl, dims, step_kw, bufs, reps: int = 10):
+    """One chunk of the path (all its calls) on a full cache, replayed from a captured HIP
+    graph and timed alone with HIP events on the replay stream: the cache is reloaded from
+    a snapshot before each repetition, outside the events.  Returns the median in
+    microseconds."""
+    import torch
+
+    import h2o_sparse_attention_amd as h2o
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    dt = dims.torch_dtype
+    c = wl.n_chunks // 2
+    s = W.steady_state(wl, 0, start=c * wl.chunk)
+    x = W.chunk_inputs(wl, 0, c)
+    snap = [torch.from_numpy(s[k]).to(dev, dt if k in ("k", "v") else None)
+            for k in ("k", "v", "pos", "phi")]
+    q, k, v = (torch.from_numpy(x[key]).to(dev, dt) for key in ("q", "k", "v"))
+    cache = h2o.H2OCache(dims, dev)
+
+    def reset():
+        cache.load(*snap, s["n"], s["start"])
+
+    graph = capture(lambda: h2o.step(cache, q, k, v, wl.sm_scale, bufs=bufs, **step_kw), reset)
+    times = []
+    for r in range(reps + 2):
+        reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            times.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(times))
+
+
+def measured_peaks():
+    """Achievable rates on this GPU for comparison with the datasheet peaks: a large bf16
+    GEMM through torch (hipBLASLt) and a 1 GiB device copy."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy = 2.0 * src.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return {"gemm_bf16_8192_tflops": round(gemm, 1), "copy_1gib_gbs": round(copy, 1)}
+
+
 def run_decode(args):
     import torch
 
@@ -632,6 +705,19 @@ def main():
                 "launches": attn.launches, "mean_launch_us": round(attn_ms * 1e3, 2)}
     kernel_us = {k: round(t.mean_ms * 1e3, 2) for k, t in timers.items()}
     steady_n = [i for i, n in enumerate(sched) if n == NC]
+    # One full-cache chunk alone, and the rates this GPU reaches on a GEMM and a copy.
+    steady_us = steady_chunk(wl, dims, step_kw, bufs)
+    if args.policy == "h2o_buffer":
+        steady_pairs = pairs_per_head(NC - S, S)
+    else:
+        steady_pairs = pairs_per_head(NC, S)
+    steady_f = (4.0 if lastrec else 6.0) * D * Hq * B * steady_pairs
+    steady = {"us": round(steady_us, 1),
+              "tflops": round(steady_f / (steady_us * 1e-6) / 1e12, 1),
+              "frac_bf16_peak": round(steady_f / (steady_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+              "flops": "F4" if lastrec else "F6"}
+    peaks = measured_peaks()
+    roofline["frac_of_measured_gemm"] = round(achieved / peaks["gemm_bf16_8192_tflops"], 4)
 
     cpu = None
     if args.cpu_budget > 0 and args.policy == "h2o":
@@ -658,6 +744,8 @@ def main():
         "frac_bf16_peak_f6": None if lastrec else round(tflops / PEAK_BF16_TFLOPS, 4),
         "kernel_mean_us": kernel_us,
         "steady_chunks": len(steady_n),
+        "steady_chunk": steady,
+        "measured_peaks": peaks,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
