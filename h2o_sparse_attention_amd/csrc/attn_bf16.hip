@@ -38,7 +38,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 32 * kWaves;   // attention pass: 32 query rows per wave
 constexpr int kKeysPerTile = 64;             // attention pass: keys staged per step
-constexpr int kKeysPerBlock = 32 * kWaves;   // colsum pass: 32 keys per wave
+constexpr int kColsumKB = 1;                 // colsum pass: 32-key blocks per wave
+constexpr int kKeysPerBlock = 32 * kColsumKB * kWaves;   // colsum pass: keys per workgroup
 constexpr int kRowsPerTile = 64;             // colsum pass: query rows staged per step
 constexpr int kColsumMaxParts = 4;           // colsum pass: row ranges per key block
 
@@ -479,7 +480,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Colsum pass: for 128 keys of one (b, kv head), sum exp(s - lse) over every
-// query row of the group (G heads x S positions).  K stays in registers; Q and
+// query row of the group (G heads x S positions).  Each wave holds kColsumKB
+// blocks of 32 keys (one: at two, each Q fragment read from LDS feeds two
+// MFMAs, but the 2 waves per SIMD that the registers then allow ran slower
+// than 3 waves with one block).  K stays in registers; Q and
 // LSE tiles of 64 packed rows (row r = i*G + head) go from global memory
 // straight into double-buffered LDS, Q rows XOR-swizzled like the attention
 // pass's K.  Each lane accumulates its 16 keys over its query column, and the
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 //      exponentials of sub-tile 1 of tile rt.
 // ---------------------------------------------------------------------------
 template <int D, bool EVEN_ROWS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kColsumKB == 1 ? 3 : 2)))
 void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restrict__ part_ws) {
     constexpr int KS = D / 16;
     constexpr int RB = 2 * D;                          // bytes per Q row
@@ -514,7 +518,8 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     __shared__ __attribute__((aligned(1024))) unsigned char sQ1[QT];
     __shared__ __attribute__((aligned(16))) float sL0[kRowsPerTile];
     __shared__ __attribute__((aligned(16))) float sL1[kRowsPerTile];
-    __shared__ float sRed[kWaves][32][33];
+    constexpr int KB = kColsumKB;
+    __shared__ float sRed[kWaves][32 * KB][33];
 
     const int n = a.n, S = a.S, G = a.G;
     const int cache_blocks = (n + kKeysPerBlock - 1) / kKeysPerBlock;
@@ -533,18 +538,19 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lq = lane & 31, hh = lane >> 5;
-    const int first = block_first + wave * 32;         // this wave's first key in its source
+    const int first = block_first + wave * 32 * KB;    // this wave's first key in its source
 
     const u16* Ksrc = is_cache ? static_cast<const u16*>(a.kc) + (size_t)bg * a.NC * D
                                : static_cast<const u16*>(a.kn) + (size_t)bg * S * D;
-    bf16x8 kf[KS];
-    {
-        const int idx = first + lq;
+    bf16x8 kf[KB][KS];
+#pragma unroll
+    for (int kbl = 0; kbl < KB; ++kbl) {
+        const int idx = first + 32 * kbl + lq;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (idx < limit) v = ld16(Ksrc + (size_t)idx * D + 16 * ks + 8 * hh);
-            kf[ks] = as_bf16x8(v);
+            kf[kbl][ks] = as_bf16x8(v);
         }
     }
 
@@ -560,7 +566,7 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
         ? (is_cache ? a.cs_cache + (size_t)bg * a.NC : a.cs_new + (size_t)bg * S)
         : part_ws + ((size_t)part * a.B * a.Hkv + bg) * (a.NC + S) + (is_cache ? 0 : a.NC);
     if (t_lo >= t_hi) {                    // no visible row in this range
-        if (lane < 32 && first + lane < limit) dst[first + lane] = 0.f;
+        if (lane < 32 * KB && first + lane < limit) dst[first + lane] = 0.f;
         return;
     }
 
@@ -624,9 +630,11 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     };
 
     const float c = a.sm_scale * kLog2e;
-    float acc[16];
+    float acc[KB][16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int kbl = 0; kbl < KB; ++kbl)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[kbl][r] = 0.f;
 
     // Q operand of query row lq of sub-tile `sub`, k-step ks: chunk 2*ks + hh
     // of that row, swizzled.
@@ -638,11 +646,12 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     // makes its weights zero).
     auto lse2_of = [&](const float* sLt, int rt, int sub) {
         const int r = rt * kRowsPerTile + sub * 32 + lq;
-        return r < R ? sLt[sub * 32 + lq] * kLog2e : INFINITY;
+        const float v = sLt[sub * 32 + lq];            // in bounds for every lane
+        return r < R ? v * kLog2e : INFINITY;
     };
     // Chunk key blocks near the diagonal: is every key of this wave visible
     // to every row of sub-tile (rt, sub)?
-    const int kmax = min(first + 31, limit - 1);       // largest key index of the wave
+    const int kmax = min(first + 32 * KB - 1, limit - 1);   // largest key index of the wave
     auto full_tile = [&](int rt, int sub) {
         if (is_cache) return true;
         const int r0 = min(rt * kRowsPerTile + sub * 32, R - 1);
@@ -651,23 +660,31 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     };
     // Exponentials of sub-tile values sv (lse2 of this lane's row) into acc,
     // with the causal test when the tile is not fully visible.
-    auto exp_masked = [&](const f32x16& sv, float lse2, int rt, int sub) {
+    auto exp_masked = [&](const f32x16 (&sv)[KB], float lse2, int rt, int sub)
+        __attribute__((always_inline)) {
         const int r = min(rt * kRowsPerTile + sub * 32 + lq, R - 1);
         const int ipos = G == 1 ? r : (int)__umulhi((uint32_t)r, g_magic);
+        // key first + 4*hh + off is visible iff off <= dlim
+        const int dlim = ipos - first - 4 * hh;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int key = first + 8 * (e >> 2) + 4 * hh + (e & 3);
-            const float p = fast_exp2(fmaf(sv[e], c, -lse2));
-            acc[e] += key <= ipos ? p : 0.f;
-        }
+        for (int kbl = 0; kbl < KB; ++kbl)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = fast_exp2(fmaf(sv[kbl][e], c, -lse2));
+                acc[kbl][e] += 32 * kbl + 8 * (e >> 2) + (e & 3) <= dlim ? p : 0.f;
+            }
     };
 
     // One stage: 8 MFMAs of (sQm, subm) into the result, interleaved with the
     // exponentials of sv (fully visible) or followed by the masked form.
-    auto stage = [&](auto mfma_c, const unsigned char* sQm, int subm, const f32x16& sv,
-                     float lse2, bool full, int rt_e, int sub_e) {
+    // Each Q fragment read from LDS feeds KB MFMAs, one per 32-key block.
+    auto stage = [&](auto mfma_c, const unsigned char* sQm, int subm, const f32x16 (&sv)[KB],
+                     float lse2, bool full, int rt_e, int sub_e, f32x16 (&r)[KB])
+        __attribute__((always_inline)) {
         constexpr bool do_mfma = decltype(mfma_c)::value;
-        f32x16 r = f32x16{};
+        constexpr int PER = 16 * KB / KS;                 // exponentials per k-step
+#pragma unroll
+        for (int kbl = 0; kbl < KB; ++kbl) r[kbl] = f32x16{};
         if (full) {
             bf16x8 qr[2];
             if (do_mfma) qr[0] = qread(sQm, subm, 0);
@@ -675,34 +692,45 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
             for (int ks = 0; ks < KS; ++ks) {
                 if (do_mfma) {
                     if (ks + 1 < KS) qr[(ks + 1) & 1] = qread(sQm, subm, ks + 1);
-                    r = mfma32(kf[ks], qr[ks & 1], r);
+#pragma unroll
+                    for (int kbl = 0; kbl < KB; ++kbl)
+                        r[kbl] = mfma32(kf[kbl][ks], qr[ks & 1], r[kbl]);
                 }
 #pragma unroll
-                for (int e = 0; e < 16 / KS; ++e) {
-                    const int x = ks * (16 / KS) + e;
-                    acc[x] += fast_exp2(fmaf(sv[x], c, -lse2));
+                for (int e = 0; e < PER; ++e) {
+                    const int x = ks * PER + e;
+                    acc[x >> 4][x & 15] += fast_exp2(fmaf(sv[x >> 4][x & 15], c, -lse2));
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
             if (do_mfma) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) r = mfma32(kf[ks], qread(sQm, subm, ks), r);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 q = qread(sQm, subm, ks);
+#pragma unroll
+                    for (int kbl = 0; kbl < KB; ++kbl) r[kbl] = mfma32(kf[kbl][ks], q, r[kbl]);
+                }
             }
             exp_masked(sv, lse2, rt_e, sub_e);
         }
-        return r;
     };
 
     // Prologue: tiles t_lo and t_lo+1; S of (t_lo, sub 0).
     issue(sQ0, sL0, t_lo);
     if (t_lo + 1 < t_hi) issue(sQ1, sL1, t_lo + 1);
     publish_lds_loads();
-    f32x16 s0 = f32x16{};
+    f32x16 s0[KB], s1[KB];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) s0 = mfma32(kf[ks], qread(sQ0, 0, ks), s0);
+    for (int kbl = 0; kbl < KB; ++kbl) s0[kbl] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 q = qread(sQ0, 0, ks);
+#pragma unroll
+        for (int kbl = 0; kbl < KB; ++kbl) s0[kbl] = mfma32(kf[kbl][ks], q, s0[kbl]);
+    }
 
-    auto step = [&](auto odd_c, int rt) {
+    auto step = [&](auto odd_c, int rt) __attribute__((always_inline)) {
         constexpr bool odd = decltype(odd_c)::value;      // (rt - t_lo) & 1
         unsigned char* qc = odd ? sQ1 : sQ0;              // tile rt
         unsigned char* qn = odd ? sQ0 : sQ1;              // tile rt+1
@@ -711,15 +739,15 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
         const bool has_next = rt + 1 < t_hi;
         const float l0 = lse2_of(lc, rt, 0), l1 = lse2_of(lc, rt, 1);
         // A: MFMAs of (rt, 1) with the exponentials of (rt, 0).
-        const f32x16 s1 = stage(std::true_type{}, qc, 1, s0, l0, full_tile(rt, 0), rt, 0);
+        stage(std::true_type{}, qc, 1, s0, l0, full_tile(rt, 0), rt, 0, s1);
         publish_lds_loads();
         // B: loads of tile rt+2 into tile rt's buffer; MFMAs of (rt+1, 0) with
         // the exponentials of (rt, 1).
         if (rt + 2 < t_hi) issue(qc, lc, rt + 2);
         // (the MFMA flag is a template argument: as a runtime flag it split the
         // MFMAs into conditional blocks ahead of all the exponentials)
-        if (has_next) s0 = stage(std::true_type{}, qn, 0, s1, l1, full_tile(rt, 1), rt, 1);
-        else stage(std::false_type{}, qn, 0, s1, l1, full_tile(rt, 1), rt, 1);
+        if (has_next) stage(std::true_type{}, qn, 0, s1, l1, full_tile(rt, 1), rt, 1, s0);
+        else stage(std::false_type{}, qn, 0, s1, l1, full_tile(rt, 1), rt, 1, s0);
         (void)ln;
     };
     for (int rt = t_lo; rt < t_hi; rt += 2) {
@@ -729,9 +757,12 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     publish_lds_loads();
 
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sRed[wave][8 * (r >> 2) + 4 * hh + (r & 3)][lq] = acc[r];
+    for (int kbl = 0; kbl < KB; ++kbl)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            sRed[wave][32 * kbl + 8 * (r >> 2) + 4 * hh + (r & 3)][lq] = acc[kbl][r];
     __syncthreads();
-    if (lane < 32) {
+    if (lane < 32 * KB) {
         float sum = 0.f;
 #pragma unroll 8
         for (int j = 0; j < 32; ++j) sum += sRed[wave][lane][j];
@@ -784,12 +815,13 @@ size_t colsum_workspace_bytes(int B, int Hkv, int NC, int S) {
 }
 
 int colsum_parts(const ChunkArgs& a, int cus) {
-    // Key blocks as whole units of work; 3 workgroups fit on a CU.  Take the
+    // Key blocks as whole units of work; 3 workgroups fit on a CU (2 with two key
+    // blocks per wave).  Take the
     // split that needs the fewest rounds of resident workgroups, counted in
     // whole-block units (ties: the smaller split).
     const long long units = (long long)((a.n + kKeysPerBlock - 1) / kKeysPerBlock +
                                         (a.S + kKeysPerBlock - 1) / kKeysPerBlock) * a.B * a.Hkv;
-    const long long slots = 3LL * cus;
+    const long long slots = (kColsumKB == 1 ? 3LL : 2LL) * cus;
     int best = 1;
     double best_t = 1e30;
     for (int p = 1; p <= kColsumMaxParts; p *= 2) {
