@@ -418,18 +418,37 @@ h2o_status_t h2o_chunk_attn_backward(const h2o_dims_t* dims, const h2o_cache_t* 
         a.excl = excl;
     }
     const int rows = a.B * a.Hkv;
-    if (a.n < a.NC) {
-        const size_t per = (size_t)(a.NC - a.n) * a.D, stride = (size_t)a.NC * a.D;
-        if ((st = check_hip(launch_zero_f32(dk_cache, per, stride, rows, (size_t)a.n * a.D, s),
+    // bf16: key blocks may be split into two row halves that add into zeroed
+    // dK/dV buffers; otherwise only the empty slots' rows are zeroed here.
+    int parts = 1;
+    if (dims->dtype == H2O_BF16) {
+        int cus = 0;
+        if ((st = check_hip(cu_count(&cus), "device attributes")) != H2O_OK) return st;
+        parts = backward_dkdv_parts(a, cus);
+    }
+    timer_begin(H2O_KERNEL_BACKWARD, s);
+    const size_t cstride = (size_t)a.NC * a.D, nstride = (size_t)a.S * a.D;
+    if (parts == 2) {
+        if ((st = check_hip(launch_zero_f32(dk_cache, cstride, cstride, rows, 0, s),
+                            "zero dk")) != H2O_OK ||
+            (st = check_hip(launch_zero_f32(dv_cache, cstride, cstride, rows, 0, s),
+                            "zero dv")) != H2O_OK ||
+            (st = check_hip(launch_zero_f32(dk_new, nstride, nstride, rows, 0, s),
+                            "zero dk_new")) != H2O_OK ||
+            (st = check_hip(launch_zero_f32(dv_new, nstride, nstride, rows, 0, s),
+                            "zero dv_new")) != H2O_OK)
+            return st;
+    } else if (a.n < a.NC) {
+        const size_t per = (size_t)(a.NC - a.n) * a.D;
+        if ((st = check_hip(launch_zero_f32(dk_cache, per, cstride, rows, (size_t)a.n * a.D, s),
                             "zero dk tail")) != H2O_OK ||
-            (st = check_hip(launch_zero_f32(dv_cache, per, stride, rows, (size_t)a.n * a.D, s),
+            (st = check_hip(launch_zero_f32(dv_cache, per, cstride, rows, (size_t)a.n * a.D, s),
                             "zero dv tail")) != H2O_OK)
             return st;
     }
-    timer_begin(H2O_KERNEL_BACKWARD, s);
     hipError_t e = dims->dtype == H2O_BF16
                        ? launch_backward_bf16(a, out, dout, drow, dq, dk_new, dv_new, dk_cache,
-                                              dv_cache, s)
+                                              dv_cache, parts, s)
                        : launch_backward_f32(a, out, dout, drow, dq, dk_new, dv_new, dk_cache,
                                              dv_cache, s);
     timer_end(H2O_KERNEL_BACKWARD, s);

@@ -407,15 +407,22 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
         }
 }
 
-// dK, dV: one workgroup per 128 keys of a KV head (cache slots or chunk keys);
-// each wave keeps its 32 keys' K and V (the B operands) in registers and walks
-// the packed query rows in 64-row tiles (Q, dO, LSE, D staged in LDS):
+// dK, dV: one workgroup per 128 keys of a KV head (cache slots or chunk keys)
+// and per part of the query rows; each wave keeps its 32 keys' K and V (the B
+// operands) in registers and walks its part's packed query rows in 64-row
+// tiles (Q, dO, LSE, D staged in LDS):
 // S = Q K^T, dP = dO V^T (rows through perm_key), P, dS = P (dP - D),
 // dV += P^T dO, dK += dS^T Q.
+// With parts == 2 the two row halves of a key block add their sums into
+// gradient buffers zeroed beforehand: two additions to zero give the same bits
+// in either order, so the result stays deterministic.  (At one wave per SIMD,
+// 576 whole blocks at chunk 1k / 8192 slots take three rounds of 256 CUs for
+// 2.25 rounds of work; halves take 2.5.)
 template <int D>
 __global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint32_t g_magic,
-                          float* dk_new, float* dv_new, float* dk_cache, float* dv_cache) {
+                          int parts, float* dk_new, float* dv_new, float* dk_cache,
+                          float* dv_cache) {
     constexpr int KS = D / 16, DT = D / 32, RB = 2 * D;
     constexpr int TB = kBwRowsPerTile * RB;
     constexpr int LOADS = TB / 1024 / kBwWaves;
@@ -428,10 +435,10 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
     const int n = a.n, S = a.S, G = a.G;
     const int cache_blocks = (n + kBwKeysPerBlock - 1) / kBwKeysPerBlock;
     const int nkb = cache_blocks + (S + kBwKeysPerBlock - 1) / kBwKeysPerBlock;
-    const int total = nkb * a.B * a.Hkv;
+    const int total = nkb * a.B * a.Hkv * parts;
     const int t = xcd_tile(blockIdx.x, total);
     if (t >= total) return;
-    const int bg = t / nkb, kbk = t % nkb;
+    const int kbk = t % nkb, part = (t / nkb) % parts, bg = t / nkb / parts;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const bool is_cache = kbk < cache_blocks;
     const int block_first = (is_cache ? kbk : kbk - cache_blocks) * kBwKeysPerBlock;
@@ -463,6 +470,10 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
     const int R = G * S;
     const int ntile = (R + kBwRowsPerTile - 1) / kBwRowsPerTile;
     const int tile0 = is_cache ? 0 : (block_first * G) / kBwRowsPerTile;
+    // This workgroup's row tiles [t_lo, t_hi).
+    const int per_part = (ntile - tile0 + parts - 1) / parts;
+    const int t_lo = tile0 + part * per_part, t_hi = min(ntile, t_lo + per_part);
+    if (t_lo >= t_hi) return;                 // nothing to add (parts > 1 only)
     const u16* Qg = static_cast<const u16*>(a.q) + (size_t)(b * a.Hq + g * G) * S * D;
     const u16* Dg = dout + (size_t)(b * a.Hq + g * G) * S * D;
     const float* Lg = a.lse + (size_t)(b * a.Hq + g * G) * S;
@@ -508,11 +519,11 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
         dv[dt] = f32x16{};
     }
     const int kmax = min(first + 31, limit - 1);
-    issue(0, tile0);
+    issue(0, t_lo);
     publish();
-    for (int rt = tile0; rt < ntile; ++rt) {
-        const int stage = (rt - tile0) & 1;
-        if (rt + 1 < ntile) issue(stage ^ 1, rt + 1);
+    for (int rt = t_lo; rt < t_hi; ++rt) {
+        const int stage = (rt - t_lo) & 1;
+        if (rt + 1 < t_hi) issue(stage ^ 1, rt + 1);
         const unsigned char* tq = sQ[stage];
         const unsigned char* td = sD[stage];
 #pragma unroll
@@ -602,10 +613,18 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
         if (kk >= limit) continue;
         const bool ex = is_cache && a.excl != nullptr &&
                         ((a.excl[(size_t)bg * excl_tiles(a.NC) + kk / 64] >> (kk % 64)) & 1);
+        if (parts == 1) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            dkb[(size_t)kk * D + 32 * dt + lq] = ex ? 0.f : a.sm_scale * dk[dt][r];
-            dvb[(size_t)kk * D + 32 * dt + lq] = ex ? 0.f : dv[dt][r];
+            for (int dt = 0; dt < DT; ++dt) {
+                dkb[(size_t)kk * D + 32 * dt + lq] = ex ? 0.f : a.sm_scale * dk[dt][r];
+                dvb[(size_t)kk * D + 32 * dt + lq] = ex ? 0.f : dv[dt][r];
+            }
+        } else if (!ex) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                atomicAdd(&dkb[(size_t)kk * D + 32 * dt + lq], a.sm_scale * dk[dt][r]);
+                atomicAdd(&dvb[(size_t)kk * D + 32 * dt + lq], dv[dt][r]);
+            }
         }
     }
 }
@@ -640,9 +659,20 @@ hipError_t launch_backward_f32(const ChunkArgs& a, const void* out, const void* 
     return hipGetLastError();
 }
 
+int backward_dkdv_parts(const ChunkArgs& a, int cus) {
+    // Whole key blocks or row halves, whichever needs fewer rounds of one
+    // workgroup per CU, counted in whole-block units (ties: whole blocks).
+    const long long blocks = (long long)((a.n + kBwKeysPerBlock - 1) / kBwKeysPerBlock +
+                                         (a.S + kBwKeysPerBlock - 1) / kBwKeysPerBlock) *
+                             a.B * a.Hkv;
+    const double r1 = (double)((blocks + cus - 1) / cus);
+    const double r2 = (double)((2 * blocks + cus - 1) / cus) / 2.0;
+    return r2 < r1 - 1e-9 ? 2 : 1;
+}
+
 hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void* dout,
                                 float* drow, float* dq, float* dk_new, float* dv_new,
-                                float* dk_cache, float* dv_cache, hipStream_t s) {
+                                float* dk_cache, float* dv_cache, int parts, hipStream_t s) {
     const int rows = a.B * a.Hq * a.S;
     hipLaunchKernelGGL(rowdot_kernel<u16>, dim3((rows + 15) / 16), dim3(256), 0, s,
                        static_cast<const u16*>(out), static_cast<const u16*>(dout), drow, rows,
@@ -652,15 +682,15 @@ hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void*
     const int nkb = (a.n + kBwKeysPerBlock - 1) / kBwKeysPerBlock +
                     (a.S + kBwKeysPerBlock - 1) / kBwKeysPerBlock;
     const uint32_t magic = a.G > 1 ? (uint32_t)((0x100000000ull + a.G - 1) / a.G) : 0u;
-    const dim3 gq(xcd_grid(nrb * a.B * a.Hkv)), gk(xcd_grid(nkb * a.B * a.Hkv));
+    const dim3 gq(xcd_grid(nrb * a.B * a.Hkv)), gk(xcd_grid(nkb * a.B * a.Hkv * parts));
     if (a.D == 128) {
         hipLaunchKernelGGL(bwd_dq_bf16_kernel<128>, gq, dim3(kBwThreads), 0, s, a, drow, dO, dq);
         hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<128>, gk, dim3(kBwThreads), 0, s, a, drow, dO,
-                           magic, dk_new, dv_new, dk_cache, dv_cache);
+                           magic, parts, dk_new, dv_new, dk_cache, dv_cache);
     } else {
         hipLaunchKernelGGL(bwd_dq_bf16_kernel<64>, gq, dim3(kBwThreads), 0, s, a, drow, dO, dq);
         hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<64>, gk, dim3(kBwThreads), 0, s, a, drow, dO,
-                           magic, dk_new, dv_new, dk_cache, dv_cache);
+                           magic, parts, dk_new, dv_new, dk_cache, dv_cache);
     }
     return hipGetLastError();
 }

@@ -40,8 +40,17 @@ __global__ __launch_bounds__(256) void update_scores_kernel(float* __restrict__ 
 __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int per_row,
                                                    size_t stride, size_t offset) {
     float* row = p + (size_t)blockIdx.y * stride + offset;
-    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < per_row; j += gridDim.x * blockDim.x)
-        row[j] = 0.f;
+    const int step = gridDim.x * blockDim.x;
+    if (((reinterpret_cast<uintptr_t>(row) & 15u) | (uintptr_t)(per_row & 3)) == 0) {
+        // 16-byte stores when the row start is 16-byte aligned and the length a
+        // multiple of 4 floats
+        float4* row4 = reinterpret_cast<float4*>(row);
+        const float4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < per_row / 4; j += step)
+            row4[j] = z;
+        return;
+    }
+    for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < per_row; j += step) row[j] = 0.f;
 }
 
 // ------------------------------------------------------------------ select
@@ -428,7 +437,7 @@ hipError_t launch_zero_f32(float* p, size_t per_row, size_t stride, int rows, si
                            hipStream_t s) {
     if (rows == 0 || per_row == 0) return hipSuccess;
     int bx = (int)((per_row + 1023) / 1024);
-    if (bx > 64) bx = 64;
+    if (bx > 256) bx = 256;
     hipLaunchKernelGGL(zero_kernel, dim3(bx, rows), dim3(256), 0, s, p, (int)per_row, stride,
                        offset);
     return hipGetLastError();

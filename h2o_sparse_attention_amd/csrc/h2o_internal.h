@@ -72,9 +72,12 @@ size_t backward_workspace_bytes(int B, int Hq, int S);
 hipError_t launch_backward_f32(const ChunkArgs& a, const void* out, const void* dout,
                                float* drow, float* dq, float* dk_new, float* dv_new,
                                float* dk_cache, float* dv_cache, hipStream_t s);
+// Row parts (1 or 2) of the bf16 dK/dV kernel for `cus` compute units; with 2
+// the dK/dV outputs must be zero before the launch.
+int backward_dkdv_parts(const ChunkArgs& a, int cus);
 hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void* dout,
                                 float* drow, float* dq, float* dk_new, float* dv_new,
-                                float* dk_cache, float* dv_cache, hipStream_t s);
+                                float* dk_cache, float* dv_cache, int parts, hipStream_t s);
 
 // Decode (S = 1) specialisation.
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int NC);
