@@ -141,3 +141,23 @@ def test_backward_full_size_steady():
     s = W.steady_state(wl, 0, start=16 * wl.chunk)
     st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
     check_backward(wl, st, W.chunk_inputs(wl, 0, 16), seed=16)
+
+
+def test_backward_full_size_deterministic():
+    """At the full chunk-1k shape the dK/dV rows of each key block go in two halves that
+    add into zeroed buffers; two runs give the same bits (two additions to zero commute)."""
+    wl = W.WORKLOADS[2]
+    s = W.steady_state(wl, 0, start=16 * wl.chunk)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    dt = H.TORCH_DT[wl.dtype]
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    x = W.chunk_inputs(wl, 0, 16)
+    q, k, v = H.dev(x["q"], dt), H.dev(x["k"], dt), H.dev(x["v"], dt)
+    out, lse, _, _ = h2o.chunk_attn(cache, st.P, q, k, v, wl.sm_scale, summed_weights=False)
+    dout = H.dev(_dout(wl, wl.chunk, 3), dt)
+    runs = [h2o.chunk_attn_backward(cache, st.P, q, k, v, out, lse, dout, wl.sm_scale)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, *runs):
+        assert torch.equal(a, b), name
