@@ -327,19 +327,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
     // depend on the merged LSE: start their loads before computing it.
     // Slots past n read zeros and are never stored.
     const int j0 = kc * kFinishKeys, j1 = min(n, j0 + kFinishKeys);
-    constexpr int U = kFinishKeys / kDecThreads;           // slots per thread
-    static_assert(kFinishKeys % kDecThreads == 0, "finish tiling");
+    // Slots j0 + 4*tid + 4*kDecThreads*u + e (e < 4): 16-byte loads and stores.
+    constexpr int U = kFinishKeys / (4 * kDecThreads);     // 4-slot groups per thread
+    static_assert(kFinishKeys % (4 * kDecThreads) == 0, "finish tiling");
     constexpr int kPre = 4;
     const Rsrc rlog = make_rsrc(ws.logits + (size_t)bg * G * ws.ncp, G * ws.ncp * 4);
     auto lload = [&](int hh, int u) {
-        return __uint_as_float(bload4_stream(rlog, (hh * ws.ncp + j0 + tid + u * kDecThreads) * 4));
+        return __builtin_bit_cast(float4, bload16_stream(
+            rlog, (hh * ws.ncp + j0 + 4 * tid + 4 * kDecThreads * u) * 4));
     };
     const bool want_cs = a.cs_cache != nullptr;
-    float vpre[kPre][U];
+    float4 vpre[kPre][U];
 #pragma unroll
     for (int hh = 0; hh < kPre; ++hh)
 #pragma unroll
-        for (int u = 0; u < U; ++u) vpre[hh][u] = (want_cs && hh < G) ? lload(hh, u) : 0.f;
+        for (int u = 0; u < U; ++u)
+            vpre[hh][u] = (want_cs && hh < G) ? lload(hh, u) : float4{0.f, 0.f, 0.f, 0.f};
 
     // Per head: the new token's logit and the merged log-sum-exp (log2 units).
     for (int hh = wave; hh < G; hh += kDecWaves) {
@@ -403,29 +406,40 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
         }
     }
     if (!want_cs) return;
-    float cs[U];
+    float4 cs[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) cs[u] = 0.f;
+    for (int u = 0; u < U; ++u) cs[u] = float4{0.f, 0.f, 0.f, 0.f};
+    auto add_head = [&](const float4 (&v)[U], float l2) {
 #pragma unroll
-    for (int hh = 0; hh < kPre; ++hh) {
-        if (hh < G) {
-            const float l2 = sLse2[hh];
-#pragma unroll
-            for (int u = 0; u < U; ++u) cs[u] += fast_exp2(vpre[hh][u] - l2);
+        for (int u = 0; u < U; ++u) {
+            cs[u].x += fast_exp2(v[u].x - l2);
+            cs[u].y += fast_exp2(v[u].y - l2);
+            cs[u].z += fast_exp2(v[u].z - l2);
+            cs[u].w += fast_exp2(v[u].w - l2);
         }
-    }
+    };
+#pragma unroll
+    for (int hh = 0; hh < kPre; ++hh)
+        if (hh < G) add_head(vpre[hh], sLse2[hh]);
     for (int hh = kPre; hh < G; ++hh) {
-        const float l2 = sLse2[hh];
-        float v[U];
+        float4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = lload(hh, u);
-#pragma unroll
-        for (int u = 0; u < U; ++u) cs[u] += fast_exp2(v[u] - l2);
+        add_head(v, sLse2[hh]);
     }
+    float* csr = a.cs_cache + (size_t)bg * a.NC;
+    const bool vec = ((reinterpret_cast<uintptr_t>(csr) & 15u) | (uintptr_t)(a.NC & 3)) == 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int j = j0 + tid + u * kDecThreads;
-        if (j < j1) a.cs_cache[(size_t)bg * a.NC + j] = cs[u];
+        const int j = j0 + 4 * tid + 4 * kDecThreads * u;
+        if (vec && j + 3 < j1) {
+            *reinterpret_cast<float4*>(csr + j) = cs[u];
+        } else {
+            const float w[4] = {cs[u].x, cs[u].y, cs[u].z, cs[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e < j1) csr[j + e] = w[e];
+        }
     }
 }
 
