@@ -170,6 +170,32 @@ def evict_and_insert(cache: H2OCache, chunk_start: int, k_new, v_new, colsum_new
     return freed_slots
 
 
+def update_evict_and_insert(cache: H2OCache, chunk_start: int, colsum_cache, k_new, v_new,
+                            colsum_new, freed_slots=None, score_mode="h2o", stream=None):
+    """h2o_update_evict_and_insert: update_scores then evict_and_insert in one call (the
+    update runs inside the selection when slots are evicted); returns freed_slots."""
+    d = cache.dims
+    B, Hkv, D = d.batch, d.n_kv_heads, d.head_dim
+    S = k_new.shape[2]
+    dev = cache.k.device
+    _need(colsum_cache, (B, Hkv, d.capacity), torch.float32, "colsum_cache")
+    _need(k_new, (B, Hkv, S, D), d.torch_dtype, "k_new")
+    _need(v_new, (B, Hkv, S, D), d.torch_dtype, "v_new")
+    _need(colsum_new, (B, Hkv, S), torch.float32, "colsum_new")
+    if freed_slots is None:
+        freed_slots = torch.empty(B, Hkv, S, dtype=torch.int32, device=dev)
+    _need(freed_slots, (B, Hkv, S), torch.int32, "freed_slots")
+    cs = cache.c()
+    check(lib.h2o_update_evict_and_insert(ctypes.byref(d.c()), ctypes.byref(cs),
+                                          colsum_cache.data_ptr(), int(chunk_start), S,
+                                          SCORE_MODES[score_mode], k_new.data_ptr(),
+                                          v_new.data_ptr(), colsum_new.data_ptr(),
+                                          freed_slots.data_ptr(), _stream_ptr(stream, dev)))
+    cache.n_valid = cs.n_valid
+    cache.next_pos = int(chunk_start) + S
+    return freed_slots
+
+
 def select_slots(cache: H2OCache, chunk_start: int, chunk_len: int, freed_slots=None,
                  score_mode="h2o", stream=None):
     """h2o_select_slots: the chunk's targets [B,Hkv,S] from the current scores; the cache
@@ -343,9 +369,8 @@ def step(cache: H2OCache, q, k_new, v_new, sm_scale: float, score_mode="h2o", bu
     out, lse, cs_cache, cs_new = chunk_attn(cache, P, q, k_new, v_new, sm_scale,
                                             b.get("out"), b.get("lse"), b.get("colsum_cache"),
                                             b.get("colsum_new"), b.get("workspace"), stream)
-    update_scores(cache, cs_cache, stream)
-    freed = evict_and_insert(cache, P, k_new, v_new, cs_new, b.get("freed_slots"), score_mode,
-                             stream)
+    freed = update_evict_and_insert(cache, P, cs_cache, k_new, v_new, cs_new,
+                                    b.get("freed_slots"), score_mode, stream)
     return {"out": out, "lse": lse, "colsum_cache": cs_cache, "colsum_new": cs_new,
             "freed_slots": freed}
 

@@ -50,6 +50,9 @@ _SIGNATURES = {
     "h2o_evict_and_insert": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32,
                                        c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
+    "h2o_update_evict_and_insert": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_void_p,
+                                              c_int64, c_int32, c_int32, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_void_p]),
     "h2o_evict_and_insert_lastrec": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64,
                                                c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                                c_void_p]),

@@ -146,7 +146,8 @@ size_t excl_bytes(const h2o_dims_t* dims) {
 h2o_status_t evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_t chunk_start,
                               int32_t chunk_len, int mode, int sink, const void* k_new,
                               const void* v_new, const float* colsum_new, int32_t* freed_slots,
-                              void* stream, bool do_select = true, bool do_insert = true) {
+                              void* stream, bool do_select = true, bool do_insert = true,
+                              const float* cs_upd = nullptr) {
     h2o_status_t st;
     if ((st = validate_dims(dims)) != H2O_OK) return st;
     if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
@@ -181,6 +182,18 @@ h2o_status_t evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_
     a.score_mode = mode;
     a.sink = sink;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cs_upd != nullptr) {
+        // The score update of h2o_update_scores: inside the selection when there is
+        // one (it reads every score anyway), else on its own.
+        if (k > 0 && do_select) {
+            a.cs_upd = cs_upd;
+        } else {
+            timer_begin(H2O_KERNEL_UPDATE, s);
+            hipError_t e = launch_update_scores(cache->score, cs_upd, a.B * a.Hkv, NC, n, s);
+            timer_end(H2O_KERNEL_UPDATE, s);
+            if ((st = check_hip(e, "update launch")) != H2O_OK) return st;
+        }
+    }
     if (do_select && do_insert && k == 1 && S == 1) {
         // one victim and one token: one launch, timed as the selection
         timer_begin(H2O_KERNEL_SELECT, s);
@@ -470,6 +483,20 @@ h2o_status_t h2o_update_scores(const h2o_dims_t* dims, const h2o_cache_t* cache,
     timer_end(H2O_KERNEL_UPDATE, s);
     if ((st = check_hip(e, "update launch")) != H2O_OK) return st;
     return ok();
+}
+
+h2o_status_t h2o_update_evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache,
+                                         const float* colsum_cache, int64_t chunk_start,
+                                         int32_t chunk_len, int32_t score_mode,
+                                         const void* k_new, const void* v_new,
+                                         const float* colsum_new, int32_t* freed_slots,
+                                         void* stream) {
+    if (!colsum_cache) return fail(H2O_ERR_INVALID_ARG, "colsum_cache is NULL");
+    if (!colsum_new) return fail(H2O_ERR_INVALID_ARG, "colsum_new is NULL");
+    if (score_mode != H2O_SCORE_H2O && score_mode != H2O_SCORE_H2O_NORM)
+        return fail(H2O_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
+    return evict_and_insert(dims, cache, chunk_start, chunk_len, score_mode, 0, k_new, v_new,
+                            colsum_new, freed_slots, stream, true, true, colsum_cache);
 }
 
 h2o_status_t h2o_evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache,

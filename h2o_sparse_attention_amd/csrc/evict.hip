@@ -133,6 +133,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
             sraw[e] = need_score ? dev::bload4(rs, (e * kSelThreads + tid) * 4) : 0u;
             praw[e] = dev::bload4(rp, (e * kSelThreads + tid) * 4);
         }
+        if (a.cs_upd != nullptr) {
+            // The score update first: phi += colsum for the filled slots, written back.
+            const dev::Rsrc rc = dev::make_rsrc(a.cs_upd + (size_t)bg * NC, n * 4);
+            uint32_t craw[KPT];
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) craw[e] = dev::bload4(rc, (e * kSelThreads + tid) * 4);
+            float* scw = a.score + (size_t)bg * NC;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const int j = e * kSelThreads + tid;
+                const float v = __uint_as_float(sraw[e]) + __uint_as_float(craw[e]);
+                if (j < n) scw[j] = v;
+                sraw[e] = __float_as_uint(v);
+            }
+        }
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             const int j = e * kSelThreads + tid;
@@ -370,6 +385,34 @@ __global__ __launch_bounds__(kOneThreads) void select1_insert_kernel(EvictArgs a
                                                               rs, j * 4, 0, 0))
                                : u32x4{0u, 0u, 0u, 0u};
             p4[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, j * 4, 0, 0));
+        }
+        if (a.cs_upd != nullptr) {
+            // The score update first: phi += colsum for the filled slots, written back.
+            const dev::Rsrc rc = dev::make_rsrc(a.cs_upd + (size_t)bg * NC, n * 4);
+            u32x4 c4[kOneLoads];
+#pragma unroll
+            for (int u = 0; u < kOneLoads; ++u)
+                c4[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      rc, (base + 4 * (u * kOneThreads + tid)) * 4,
+                                                      0, 0));
+            float* scw = a.score + (size_t)bg * NC;
+#pragma unroll
+            for (int u = 0; u < kOneLoads; ++u) {
+                const int j = base + 4 * (u * kOneThreads + tid);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[e] = __uint_as_float(s4[u][e]) + __uint_as_float(c4[u][e]);
+                    s4[u][e] = __float_as_uint(v[e]);
+                }
+                if (j + 3 < n && (((reinterpret_cast<uintptr_t>(scw) & 15u) | (NC & 3)) == 0)) {
+                    *reinterpret_cast<float4*>(scw + j) = float4{v[0], v[1], v[2], v[3]};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (j + e < n) scw[j + e] = v[e];
+                }
+            }
         }
 #pragma unroll
         for (int u = 0; u < kOneLoads; ++u)

@@ -42,6 +42,9 @@ struct EvictArgs {
     int32_t* freed;
     int B, Hkv, D, S, NC, n, W, P, elem_bytes, score_mode;
     int sink;               // lastrec: slots at positions < sink are never evicted
+    // If set, the selection first adds these summed weights to the scores of the
+    // filled slots (and writes the sums back), as h2o_update_scores would.
+    const float* cs_upd = nullptr;
 };
 
 // Internal ranking mode of the select kernel, beside h2o_score_mode_t.

@@ -161,6 +161,24 @@ H2O_API h2o_status_t h2o_evict_and_insert(const h2o_dims_t *dims, h2o_cache_t *c
                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * h2o_update_scores followed by h2o_evict_and_insert, in one call with the
+ * same results bit for bit ("Improvements to H2O", item 2: accumulate, then
+ * overwrite the smallest).  When slots are evicted (n + S > N_C) the score
+ * update runs inside the selection, which reads every score anyway, so the
+ * step takes one launch fewer; otherwise it runs on its own first.
+ *   colsum_cache: [B][Hkv][N_C] fp32 device buffer, as for h2o_update_scores;
+ *   the other arguments, the layouts, the errors (all returned before any
+ *   launch) and the update of cache->n_valid are those of h2o_evict_and_insert.
+ * score_mode is H2O_SCORE_H2O or H2O_SCORE_H2O_NORM.
+ */
+H2O_API h2o_status_t h2o_update_evict_and_insert(const h2o_dims_t *dims, h2o_cache_t *cache,
+                                         const float *colsum_cache, int64_t chunk_start,
+                                         int32_t chunk_len, int32_t score_mode,
+                                         const void *k_new, const void *v_new,
+                                         const float *colsum_new, int32_t *freed_slots,
+                                         void *stream);
+
+/*
  * Insert-first buffer form ("Kernel Support Needs": attention over the fixed
  * N_C-slot buffer under the positional mask -inf * 1[P+i < t(b,h,j)]).  The
  * victims are chosen on the scores before the chunk and the chunk is written

@@ -126,6 +126,26 @@ def test_evict_rejects_bad_args():
     assert _evict(_dims(head_dim=32), 10, 8)[0] == _native.H2O_ERR_UNSUPPORTED
 
 
+def _update_evict(dims, n_valid, S, P=1000, mode=0, cs=FAKE, freed=FAKE):
+    cache = _native.CacheStruct(FAKE, FAKE, FAKE, FAKE, n_valid)
+    st = h2o.lib.h2o_update_evict_and_insert(ctypes.byref(dims), ctypes.byref(cache), cs, P, S,
+                                             mode, FAKE, FAKE, FAKE, freed, None)
+    return st, cache.n_valid
+
+
+def test_update_evict_rejects_before_launching():
+    """The fused update + eviction call validates exactly like the two calls: every error is
+    returned before any launch, the cache count untouched."""
+    st, n = _update_evict(_dims(capacity=256, recent_window=200), n_valid=256, S=64)
+    assert st == _native.H2O_ERR_CAPACITY and n == 256
+    assert _update_evict(_dims(), 10, 8, cs=None)[0] == _native.H2O_ERR_INVALID_ARG
+    assert "colsum_cache" in h2o.lib.h2o_last_error().decode()
+    assert _update_evict(_dims(), 10, 8, mode=5)[0] == _native.H2O_ERR_INVALID_ARG
+    assert _update_evict(_dims(), 10, 8, freed=None)[0] == _native.H2O_ERR_INVALID_ARG
+    assert _update_evict(_dims(), 10, 0)[0] == _native.H2O_ERR_INVALID_ARG
+    assert _update_evict(_dims(head_dim=32), 10, 8)[0] == _native.H2O_ERR_UNSUPPORTED
+
+
 def _lastrec(dims, n_valid, S, sink, P=1000, freed=FAKE):
     cache = _native.CacheStruct(FAKE, FAKE, FAKE, FAKE, n_valid)
     st = h2o.lib.h2o_evict_and_insert_lastrec(ctypes.byref(dims), ctypes.byref(cache), P, S,

@@ -277,3 +277,57 @@ def test_decode_one_victim_fused_matches_separate(score_mode):
             assert torch.equal(getattr(fused, name), getattr(sep, name)), f"step {t}: {name}"
         assert (H.host(fused.pos) == st.pos).all()
         assert fused.n_valid == sep.n_valid == st.n
+
+
+@pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
+@pytest.mark.parametrize("case", ["steady_chunk", "decode", "filling"])
+def test_update_evict_fused_matches_separate(case, score_mode):
+    """h2o_update_evict_and_insert gives bit for bit what h2o_update_scores followed by
+    h2o_evict_and_insert gives: a full-size evicting chunk (k = 1024), a decode step (k = 1)
+    and a filling chunk (k = 0, the update on its own)."""
+    r = np.random.default_rng(21)
+    if case == "decode":
+        wl = W.workload(5, batch=4)
+        s = W.decode_initial_state(wl)
+        x = W.decode_step_inputs(wl, 0)
+    elif case == "steady_chunk":
+        wl = W.WORKLOADS[2]
+        s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=2, tie_fraction=0.2)
+        x = W.chunk_inputs(wl, 0, 20)
+    else:
+        wl = W.workload(2, batch=2, n_q_heads=8, n_kv_heads=2, capacity=512, recent_window=64,
+                        chunk=128, seq_len=2048, heavy_count=20)
+        st0 = oracle.H2OState.empty(wl.batch, wl.n_kv_heads, wl.capacity, wl.head_dim)
+        for c in range(2):
+            xc = W.chunk_inputs(wl, 0, c)
+            oracle.h2o_step(st0, xc["q"], xc["k"], xc["v"], wl.sm_scale, wl.recent_window)
+        s = {"k": st0.K, "v": st0.V, "pos": st0.pos, "phi": st0.phi, "n": st0.n, "start": st0.P}
+        x = W.chunk_inputs(wl, 0, 2)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    fused, sep = (h2o.H2OCache(H.dims_of(wl), H.DEV) for _ in range(2))
+    for c in (fused, sep):
+        H.load_oracle_state(c, st, wl.dtype)
+    S = x["k"].shape[2]
+    dt = H.TORCH_DT[wl.dtype]
+    k, v = H.dev(x["k"], dt), H.dev(x["v"], dt)
+    cs_cache = H.dev(r.random((wl.batch, wl.n_kv_heads, wl.capacity)).astype(np.float32),
+                     torch.float32)
+    cs_new = H.dev(r.random((wl.batch, wl.n_kv_heads, S)).astype(np.float32), torch.float32)
+    P = st.P
+    f1 = h2o.update_evict_and_insert(fused, P, cs_cache, k, v, cs_new, score_mode=score_mode)
+    h2o.update_scores(sep, cs_cache)
+    f2 = h2o.evict_and_insert(sep, P, k, v, cs_new, score_mode=score_mode)
+    torch.cuda.synchronize()
+    assert torch.equal(f1, f2), "targets"
+    for name in ("k", "v", "pos", "score"):
+        assert torch.equal(getattr(fused, name), getattr(sep, name)), name
+    assert fused.n_valid == sep.n_valid and fused.next_pos == sep.next_pos
+    # and the oracle's targets on the updated scores (fp64 sums there: near ties at the
+    # cut may swap, under the usual rule)
+    oracle.update_scores(st, H.host(cs_cache))
+    n_before, pos_before = st.n, st.pos.copy()
+    rank = oracle.selection_scores(st.copy(), S, score_mode).copy()
+    victims = oracle.select_victims(st, S, wl.recent_window, score_mode)
+    want = oracle.evict_and_insert(st, victims, x["k"], x["v"], H.host(cs_new))
+    H.compare_victims(H.host(f1).astype(np.int64), want, rank, pos_before, n_before, P,
+                      wl.recent_window, case)
