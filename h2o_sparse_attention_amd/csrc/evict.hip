@@ -104,7 +104,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sWave, int& tota
 // (score, slot index) order exactly.
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
-    __shared__ int sHist[256];
+    __shared__ int sHist[2][256];
     __shared__ int sSel[2];
     __shared__ int sWave[kSelWaves];
     const int bg = blockIdx.x;
@@ -235,18 +235,27 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
         uint32_t mask = top >= 24 ? 0u : ~0u << (top + 8);
         uint32_t prefix = lo & mask;
         int k_rem = k;                        // rank of T among the keys matching prefix
-        for (int shift = top; shift >= 0; shift -= 8) {
-            if (tid < 256) sHist[tid] = 0;
-            __syncthreads();
+        // Two histograms: while wave 0 scans one, the other waves clear the other
+        // for the next pass (its last reader, the scan before, ended at a barrier).
+        if (tid < 256) {
+            sHist[0][tid] = 0;
+            sHist[1][tid] = 0;
+        }
+        __syncthreads();
+        int hb = 0;
+        for (int shift = top; shift >= 0; shift -= 8, hb ^= 1) {
+            int* hist = sHist[hb];
 #pragma unroll
             for (int e = 0; e < KPT; ++e)
-                if ((key[e] & mask) == prefix) atomicAdd(&sHist[(key[e] >> shift) & 255u], 1);
+                if ((key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1);
             __syncthreads();
-            if (wave == 0) {
+            if (wave != 0) {
+                if (tid < 256 + 64) sHist[hb ^ 1][tid - 64] = 0;
+            } else {
                 int c4[4], sum = 0;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    c4[q] = sHist[4 * lane + q];
+                    c4[q] = hist[4 * lane + q];
                     sum += c4[q];
                 }
                 int incl = sum;
@@ -271,31 +280,29 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
             k_rem -= sSel[1];
         }
         const uint32_t T = prefix;
-        // T is the k-th smallest key: count(< T) < k <= count(<= T).
+        // T is the k-th smallest key: count(< T) < k <= count(<= T).  One scan of
+        // the packed counts (less in the low 16 bits, equal in the high: at most
+        // N_C <= 32768 each) gives, in slot order, the keys below T and the keys
+        // equal to T before each thread; a victim's output index is the number of
+        // victims before it: the keys below T plus the first need_eq equal keys.
         int my_less = 0, my_eq = 0;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
             my_less += key[e] < T;
             my_eq += (key[e] == T) && (j0 + e < n);
         }
-        int less_total, eq_total;
-        block_exclusive_scan(my_less, sWave, less_total);
-        int eq_before = block_exclusive_scan(my_eq, sWave, eq_total);
-        const int need_eq = k - less_total;
-        int my_v = 0;
-        bool vic[KPT];
+        int total;
+        const int before = block_exclusive_scan(my_less | (my_eq << 16), sWave, total);
+        const int need_eq = k - (total & 0xFFFF);
+        int less_run = before & 0xFFFF, eq_run = before >> 16;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
+            const bool lt = key[e] < T;
             const bool eq = (key[e] == T) && (j0 + e < n);
-            vic[e] = key[e] < T || (eq && eq_before < need_eq);
-            eq_before += eq;
-            my_v += vic[e];
+            if (lt || (eq && eq_run < need_eq)) freed[less_run + min(eq_run, need_eq)] = j0 + e;
+            less_run += lt;
+            eq_run += eq;
         }
-        int v_total;
-        int out_idx = block_exclusive_scan(my_v, sWave, v_total);
-#pragma unroll
-        for (int e = 0; e < KPT; ++e)
-            if (vic[e]) freed[out_idx++] = j0 + e;
     }
     for (int e = tid; e < n_new - n; e += kSelThreads) freed[k + e] = n + e;
 }
