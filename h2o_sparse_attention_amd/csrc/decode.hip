@@ -344,22 +344,47 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
         for (int u = 0; u < U; ++u)
             vpre[hh][u] = (want_cs && hh < G) ? lload(hh, u) : float4{0.f, 0.f, 0.f, 0.f};
 
+    // The output merge's loads (workgroup kc == 0) go out now too, so that every
+    // global read of this kernel is in flight at once: each thread's (head, d)
+    // pairs idx = tid, tid + 256 (G*D <= 512, at most kMaxSplits splits).
+    constexpr int kMaxSplits = 8;
+    const size_t stride = (size_t)G * (D + 2);
+    const bool pre_out = kc == 0 && G * D <= 2 * kDecThreads && nsplit_rt <= kMaxSplits;
+    float pm[2][kMaxSplits], po[2][kMaxSplits];
+    if (pre_out) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = min(tid + i * kDecThreads, G * D - 1);
+            const float* rec0 = ws.partial + ((size_t)bg * ws.nsplit * G + idx / D) * (D + 2);
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplits; ++sp) {
+                const int spc = min(sp, nsplit_rt - 1);
+                pm[i][sp] = rec0[spc * stride];
+                po[i][sp] = rec0[spc * stride + 2 + idx % D];
+            }
+        }
+    }
+
     // Per head: the new token's logit and the merged log-sum-exp (log2 units).
     for (int hh = wave; hh < G; hh += kDecWaves) {
         const u16* q = Q + (size_t)(b * a.Hq + g * G + hh) * D;
+        const float* rec0 = ws.partial + ((size_t)bg * ws.nsplit * G + hh) * (D + 2);
+        // the split records first (one per lane), then the dot product
+        const bool has_rec = lane < nsplit_rt;
+        const float mrec = has_rec ? rec0[lane * stride] : -INFINITY;
+        const float lrec = has_rec ? rec0[lane * stride + 1] : 0.f;
         float dot = 0.f;
         for (int d = lane; d < D; d += 64) dot = fmaf(bf(q[d]), bf(Kn[d]), dot);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
         const float s_new = dot * c;
-        float m = s_new;
-        const float* rec0 = ws.partial + ((size_t)bg * ws.nsplit * G + hh) * (D + 2);
-        const size_t stride = (size_t)G * (D + 2);
-        for (int sp = lane; sp < nsplit_rt; sp += 64) m = fmaxf(m, rec0[sp * stride]);
+        float m = fmaxf(s_new, mrec);
+        for (int sp = lane + 64; sp < nsplit_rt; sp += 64) m = fmaxf(m, rec0[sp * stride]);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
         float l = lane == 0 ? fast_exp2(s_new - m) : 0.f;
-        for (int sp = lane; sp < nsplit_rt; sp += 64) {
+        if (mrec != -INFINITY) l += lrec * fast_exp2(mrec - m);
+        for (int sp = lane + 64; sp < nsplit_rt; sp += 64) {
             const float ms = rec0[sp * stride];
             if (ms != -INFINITY) l += rec0[sp * stride + 1] * fast_exp2(ms - m);
         }
@@ -373,7 +398,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
     }
     __syncthreads();
 
-    if (kc == 0) {
+    if (pre_out) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + i * kDecThreads;
+            if (idx >= G * D) break;
+            const int hh = idx / D, d = idx % D;
+            const float m = sM[hh];
+            float acc = bf(Vn[d]) * fast_exp2(sNew[hh] - m);
+#pragma unroll
+            for (int sp = 0; sp < kMaxSplits; ++sp)
+                if (sp < nsplit_rt && pm[i][sp] != -INFINITY)
+                    acc += po[i][sp] * fast_exp2(pm[i][sp] - m);
+            const float inv = fast_exp2(m - sLse2[hh]);       // 1 / l
+            const size_t oi = (size_t)(b * a.Hq + g * G + hh) * D + d;
+            static_cast<__hip_bfloat16*>(a.out)[oi] = __float2bfloat16(acc * inv);
+            if (d == 0) a.lse[(size_t)(b * a.Hq + g * G + hh)] = sLse2[hh] * 0.6931471805599453f;
+        }
+        if (want_cs && tid == 0) {
+            float cs = 0.f;
+            for (int hh = 0; hh < G; ++hh) cs += fast_exp2(sNew[hh] - sLse2[hh]);
+            a.cs_new[bg] = cs;
+        }
+    } else if (kc == 0) {
         for (int idx = tid; idx < G * D; idx += kDecThreads) {
             const int hh = idx / D, d = idx % D;
             const float m = sM[hh];
