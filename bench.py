@@ -96,10 +96,25 @@ def cpu_baseline(wl, budget_s: float):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{chunks} steady chunk(s) of {wl.name} (full cache, "
-                      f"{wl.capacity}+{wl.chunk} keys, fp64 NumPy), {dt:.1f} s",
-            "tokens_per_s": chunks * wl.chunk / dt, "ms_per_chunk": dt / chunks * 1e3}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{chunks} steady chunk(s) of {wl.name} (full cache, "
+                     f"{wl.capacity}+{wl.chunk} keys, fp64 NumPy), {dt:.1f} s",
+           "tokens_per_s": chunks * wl.chunk / dt, "ms_per_chunk": dt / chunks * 1e3}
+    # The same oracle on one thread, one chunk.
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"],
+                                             s["start"])
+            t1 = time.perf_counter()
+            oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window)
+            d1 = time.perf_counter() - t1
+        f1 = 6.0 * wl.head_dim * wl.n_q_heads * pairs_per_head(wl.capacity, wl.chunk)
+        out["one_thread"] = {"value": f1 / d1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                             "ms_per_chunk": d1 * 1e3, "sample": "1 steady chunk"}
+    except ImportError:  # pragma: no cover
+        out["one_thread"] = None
+    return out
 
 
 def copy_probe(mib: int) -> None:
