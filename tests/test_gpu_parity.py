@@ -280,7 +280,7 @@ def test_decode_one_victim_fused_matches_separate(score_mode):
 
 
 @pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
-@pytest.mark.parametrize("case", ["steady_chunk", "decode", "filling"])
+@pytest.mark.parametrize("case", ["steady_chunk", "decode", "filling", "f32_plumbing"])
 def test_update_evict_fused_matches_separate(case, score_mode):
     """h2o_update_evict_and_insert gives bit for bit what h2o_update_scores followed by
     h2o_evict_and_insert gives: a full-size evicting chunk (k = 1024), a decode step (k = 1)
@@ -294,6 +294,10 @@ def test_update_evict_fused_matches_separate(case, score_mode):
         wl = W.WORKLOADS[2]
         s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=2, tie_fraction=0.2)
         x = W.chunk_inputs(wl, 0, 20)
+    elif case == "f32_plumbing":
+        wl = W.WORKLOADS[1]
+        s = W.steady_state(wl, 0, start=10 * wl.chunk, seed=4, tie_fraction=0.2)
+        x = W.chunk_inputs(wl, 0, 10)
     else:
         wl = W.workload(2, batch=2, n_q_heads=8, n_kv_heads=2, capacity=512, recent_window=64,
                         chunk=128, seq_len=2048, heavy_count=20)
