@@ -303,16 +303,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 
     // O^T += V^T P^T for the tile in sVt, operands read two MFMAs ahead,
     // interleaved with the running max of the next tile's scores (sn).
-    auto pv_max = [&](const u16* sVt, const bf16x8 (&pb)[2][2], const f32x16 (&sn)[2]) {
+    // The MFMAs of the first 32 keys (sub-tile 0, whose P is complete) also carry
+    // the last 8 exponentials of each lane (keys 48..63 of this tile), the ones
+    // of sub-tile 1 the maxima of the next tile, so both phases of an iteration
+    // hold VALU work under their MFMAs.
+    auto pv_max = [&](const u16* sVt, bf16x8 (&pb)[2][2], const f32x16 (&sc)[2],
+                      const f32x16 (&sn)[2], float mcv, float& lsum) {
         const unsigned char* base = reinterpret_cast<const unsigned char*>(sVt);
         auto vread = [&](int x) {
             const int dt = x % DT, s2 = (x / DT) & 1, sub = x / (2 * DT);
             return ld_vt(base + (vb ^ (64 * dt)) + (sub * 32 + 16 * s2) * RB, 4 * RB);
         };
         constexpr int NX = 4 * DT;
+        constexpr int HX = 2 * DT;                // MFMAs of one sub-tile
         constexpr int AHEAD = 2;
-        constexpr int MPER = 32 / NX;             // maxima per MFMA
         float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        float p[8];
         bf16x8 va[AHEAD + 1];
 #pragma unroll
         for (int x = 0; x < AHEAD; ++x) va[x] = vread(x);
@@ -321,10 +327,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
             if (x + AHEAD < NX) va[(x + AHEAD) % (AHEAD + 1)] = vread(x + AHEAD);
             const int dt = x % DT, s2 = (x / DT) & 1, sub = x / (2 * DT);
             o[dt] = mfma32(va[x % (AHEAD + 1)], pb[sub][s2], o[dt]);
+            if (x < HX) {
 #pragma unroll
-            for (int e = 0; e < MPER; ++e) {
-                const int idx = x * MPER + e;
-                m4[idx & 3] = fmaxf(m4[idx & 3], sn[idx >> 4][idx & 15]);
+                for (int e = 8 * x / HX; e < 8 * (x + 1) / HX; ++e) {
+                    p[e] = fast_exp2(fmaf(sc[1][8 + e], c, -mcv));
+                    lsum += p[e];
+                }
+                if (x == HX - 1)
+                    pb[1][1] = as_bf16x8(u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]),
+                                               pack2(p[4], p[5]), pack2(p[6], p[7])});
+            } else {
+#pragma unroll
+                for (int idx = 32 * (x - HX) / HX; idx < 32 * (x - HX + 1) / HX; ++idx)
+                    m4[idx & 3] = fmaxf(m4[idx & 3], sn[idx >> 4][idx & 15]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
             auto kread = [&](int ks, int sub) {
                 return as_bf16x8(ld16(kbase + ((kb ^ (32 * ks)) + sub * 32 * RB)));
             };
-            constexpr int PER = 32 / KS;          // exponentials per k-step
+            constexpr int NEA = 24;               // exponentials in this phase (of 32)
             bf16x8 kr[2][2];
             kr[0][0] = kread(0, 0);
             kr[0][1] = kread(0, 1);
@@ -393,34 +408,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
                 snext[0] = mfma32(kr[ks & 1][0], qf[ks], snext[0]);
                 snext[1] = mfma32(kr[ks & 1][1], qf[ks], snext[1]);
 #pragma unroll
-                for (int e = 0; e < PER; ++e) {
-                    const int idx = ks * PER + e, q4 = idx >> 3, ee = idx & 7;
+                for (int idx = ks * NEA / KS; idx < (ks + 1) * NEA / KS; ++idx) {
+                    const int q4 = idx >> 3, ee = idx & 7;
                     p[ee] = fast_exp2(fmaf(scur[q4 >> 1][8 * (q4 & 1) + ee], c, -mc));
                     lsum += p[ee];
-                }
-                if (((ks + 1) * PER) % 8 == 0) {
-                    const int q4 = (ks * PER) >> 3;
-                    pb[q4 >> 1][q4 & 1] =
-                        as_bf16x8(u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]),
-                                        pack2(p[4], p[5]), pack2(p[6], p[7])});
+                    if (ee == 7)
+                        pb[q4 >> 1][q4 & 1] =
+                            as_bf16x8(u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]),
+                                            pack2(p[4], p[5]), pack2(p[6], p[7])});
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
             // Keep the exponentials here: their only uses come after a branch
             // and would otherwise be sunk past it, out of the MFMA stream.
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
+            for (int q4 = 0; q4 < 3; ++q4)
                 asm volatile("" : : "v"(__builtin_bit_cast(u32x4, pb[q4 >> 1][q4 & 1])));
             asm volatile("" : : "v"(lsum));
-            l_run += lsum;
             // The next tile's mask (rare: partial or diagonal tiles).
             if (has_next) {
                 const uint64_t exn = tile_excl(jt + 1);
                 if (!tile_all_visible(jt + 1) || exn != 0) apply_mask(snext, tile_lim(jt + 1), exn);
             }
             // Phase B: P V of this tile with the next tile's row max.
-            const float mt = pv_max(vcur, pb, snext);
+            const float mt = pv_max(vcur, pb, scur, snext, mc, lsum);
             asm volatile("" : : "v"(mt));         // keep the maxima under the MFMAs
+            l_run += lsum;
             if (has_next) mc = rescale_for(mt);
         }
         publish_lds_loads();
