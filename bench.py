@@ -1,8 +1,9 @@
 """Throughput of the H2O chunk path: attention + summed weights + score update +
 eviction/insert, over a whole synthetic sequence, on one MI355X.
 
-A step is one full sequence of the workload pushed through the three C-ABI calls
-chunk by chunk from an empty cache (default: Qwen3-4B attention shape, 32 query /
+A step is one full sequence of the workload pushed through the path chunk by chunk
+(h2o_chunk_attn, then h2o_update_evict_and_insert: the score update, selection and
+insertion, with the update inside the selection kernel) from an empty cache (default: Qwen3-4B attention shape, 32 query /
 8 KV heads, head_dim 128, bf16, chunk 1024, cache 8192, recent window 256, 64k
 tokens = 64 chunks).  Inputs are resident in HBM before the timed region.
 
