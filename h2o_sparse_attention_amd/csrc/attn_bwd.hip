@@ -526,26 +526,19 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
         if (rt + 1 < t_hi) issue(stage ^ 1, rt + 1);
         const unsigned char* tq = sQ[stage];
         const unsigned char* td = sD[stage];
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            // One wave per SIMD: issue each phase's LDS operand reads together, so
-            // their latency is paid once, not once per MFMA.
-            bf16x8 qa[KS], da[KS];
+        // The two 32-row sub-tiles are pipelined inside the wave (one wave per
+        // SIMD): sub-tile 0's exponentials and dS run under sub-tile 1's S and dP
+        // MFMAs, sub-tile 1's under sub-tile 0's dV and dK MFMAs.
+        auto read_qd = [&](int sub, bf16x8 (&qa)[KS], bf16x8 (&da)[KS]) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ob = (qb ^ (32 * ks)) + sub * 32 * RB;
                 qa[ks] = as_bf16x8(ld16(tq + ob));
                 da[ks] = as_bf16x8(ld16(td + ob));
             }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 st = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                st = mfma32(qa[ks], kf[ks], st);
-                dp = mfma32(da[ks], vf[ks], dp);
-            }
-            // The transposed operands of dV and dK, read while the VALU works.
-            bf16x8 dtr[DT][2], qtr[DT][2];
+        };
+        // The transposed operands of dV and dK for one sub-tile.
+        auto read_tr = [&](int sub, bf16x8 (&dtr)[DT][2], bf16x8 (&qtr)[DT][2]) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -555,53 +548,108 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
                     dtr[dt][s2] = ld_tr(td + o0, td + o1);
                     qtr[dt][s2] = ld_tr(tq + o0, tq + o1);
                 }
-            __builtin_amdgcn_sched_barrier(0);
-            // rows 32*sub + 16*(r/8) + 8*hh + r%8 of the tile, this lane's key
+        };
+        const bool rows_in = rt * kBwRowsPerTile + kBwRowsPerTile <= R;
+        // log2-scaled LSE (+inf past the last row: weight 0) and D of the lane's
+        // rows 32*sub + 16*(r/8) + 8*hh + r%8; read unconditionally (in LDS bounds).
+        float l2v[16], drv[16];
+        auto read_ld = [&](int sub) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
+                const float lr = sL[stage][rl];
+                drv[r] = sR[stage][rl];
+                l2v[r] = (rows_in || rt * kBwRowsPerTile + rl < R) ? lr * kLog2e : INFINITY;
+            }
+        };
+        // Chunk keys near the diagonal: -inf for this lane's key at rows before it.
+        auto mask_sub = [&](int sub, f32x16& stv) {
             const int r0 = rt * kBwRowsPerTile + 32 * sub;
             const int i0 = G == 1 ? min(r0, R - 1) : (int)__umulhi((uint32_t)min(r0, R - 1), g_magic);
-            const bool full = is_cache || kmax <= i0;
-            // LSE and D of the lane's rows: two runs of eight consecutive rows, read
-            // unconditionally (in LDS bounds); rows past R get LSE = +inf, weight 0.
-            float lr[16], dr[16];
+            if (is_cache || kmax <= i0) return;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int rl = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-                lr[r] = sL[stage][rl];
-                dr[r] = sR[stage][rl];
+                const int rr = r0 + 16 * (r >> 3) + 8 * hh + (r & 7);
+                const int ipos = G == 1 ? rr : (int)__umulhi((uint32_t)rr, g_magic);
+                if (key > ipos) stv[r] = -INFINITY;
             }
-            const bool rows_in = rt * kBwRowsPerTile + kBwRowsPerTile <= R;
-            float pv[16], dsv[16];
+        };
+        // P and dS = P (dP - D) of value r of a sub-tile.
+        auto pds = [&](const f32x16& stv, const f32x16& dpv, int r, float& pr, float& dsr) {
+            pr = fast_exp2(fmaf(stv[r], c, -l2v[r]));
+            dsr = pr * (dpv[r] - drv[r]);
+        };
+        auto pack = [&](const float (&v)[16], bf16x8 (&b)[2]) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rl = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-                const int rr = rt * kBwRowsPerTile + rl;
-                const float l2 = (rows_in || rr < R) ? lr[r] * kLog2e : INFINITY;
-                float p = fast_exp2(fmaf(st[r], c, -l2));
-                if (!full) {
-                    const int ipos = G == 1 ? rr : (int)__umulhi((uint32_t)rr, g_magic);
-                    p = key > ipos ? 0.f : p;
-                }
-                pv[r] = p;
-                dsv[r] = p * (dp[r] - dr[r]);
+            for (int s2 = 0; s2 < 2; ++s2)
+                b[s2] = as_bf16x8(u32x4{pack2(v[8 * s2 + 0], v[8 * s2 + 1]), pack2(v[8 * s2 + 2], v[8 * s2 + 3]),
+                                        pack2(v[8 * s2 + 4], v[8 * s2 + 5]), pack2(v[8 * s2 + 6], v[8 * s2 + 7])});
+        };
+
+        // A: sub-tile 0's S and dP.
+        bf16x8 qa0[KS], da0[KS];
+        read_qd(0, qa0, da0);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 st0 = f32x16{}, dp0 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            st0 = mfma32(qa0[ks], kf[ks], st0);
+            dp0 = mfma32(da0[ks], vf[ks], dp0);
+        }
+        bf16x8 qa1[KS], da1[KS], dtr[DT][2], qtr[DT][2];
+        read_qd(1, qa1, da1);
+        read_tr(0, dtr, qtr);
+        read_ld(0);
+        __builtin_amdgcn_sched_barrier(0);
+        mask_sub(0, st0);
+        // B: sub-tile 1's S and dP with sub-tile 0's P and dS.
+        float pv[16], dsv[16];
+        f32x16 st1 = f32x16{}, dp1 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            st1 = mfma32(qa1[ks], kf[ks], st1);
+            dp1 = mfma32(da1[ks], vf[ks], dp1);
+#pragma unroll
+            for (int r = 16 * ks / KS; r < 16 * (ks + 1) / KS; ++r) pds(st0, dp0, r, pv[r], dsv[r]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 pb0[2], db0[2];
+        pack(pv, pb0);
+        pack(dsv, db0);
+        read_ld(1);
+        __builtin_amdgcn_sched_barrier(0);
+        mask_sub(1, st1);
+        // C: sub-tile 0's dV and dK (B operands dO / Q columns 32*dt + lq, rows
+        // 16*s2 + 8*hh.. of the sub-tile, read transposed) with sub-tile 1's P and dS.
+        // (each transposed operand of sub-tile 1 is read into the registers the
+        // MFMAs of sub-tile 0 have just taken theirs from)
+#pragma unroll
+        for (int x = 0; x < 2 * DT; ++x) {
+            const int dt = x >> 1, s2 = x & 1;
+            dv[dt] = mfma32(pb0[s2], dtr[dt][s2], dv[dt]);
+            dk[dt] = mfma32(db0[s2], qtr[dt][s2], dk[dt]);
+            {
+                const int rows = (32 + 16 * s2) * RB;
+                const int o0 = (t0 + rows) ^ (64 * dt), o1 = (t1 + rows) ^ (64 * dt);
+                dtr[dt][s2] = ld_tr(td + o0, td + o1);
+                qtr[dt][s2] = ld_tr(tq + o0, tq + o1);
             }
-            bf16x8 pb[2], db[2];
+#pragma unroll
+            for (int r = 16 * x / (2 * DT); r < 16 * (x + 1) / (2 * DT); ++r)
+                pds(st1, dp1, r, pv[r], dsv[r]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 pb1[2], db1[2];
+        pack(pv, pb1);
+        pack(dsv, db1);
+        // E: sub-tile 1's dV and dK.
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                pb[s2] = as_bf16x8(u32x4{pack2(pv[8 * s2 + 0], pv[8 * s2 + 1]), pack2(pv[8 * s2 + 2], pv[8 * s2 + 3]),
-                                         pack2(pv[8 * s2 + 4], pv[8 * s2 + 5]), pack2(pv[8 * s2 + 6], pv[8 * s2 + 7])});
-                db[s2] = as_bf16x8(u32x4{pack2(dsv[8 * s2 + 0], dsv[8 * s2 + 1]), pack2(dsv[8 * s2 + 2], dsv[8 * s2 + 3]),
-                                         pack2(dsv[8 * s2 + 4], dsv[8 * s2 + 5]), pack2(dsv[8 * s2 + 6], dsv[8 * s2 + 7])});
+                dv[dt] = mfma32(pb1[s2], dtr[dt][s2], dv[dt]);
+                dk[dt] = mfma32(db1[s2], qtr[dt][s2], dk[dt]);
             }
-            // dV += P^T dO, dK += dS^T Q: B operands dO / Q columns 32*dt + lq,
-            // rows 32*sub + 16*s2 + 8*hh.. of the tile, read transposed.
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    dv[dt] = mfma32(pb[s2], dtr[dt][s2], dv[dt]);
-                    dk[dt] = mfma32(db[s2], qtr[dt][s2], dk[dt]);
-                }
-        }
         publish();
     }
     // dk[dt][r] = dK[key first + 8(r/4) + 4hh + r%4][d = 32dt + lq]
