@@ -342,53 +342,90 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
                              (cache || first + kBwKeysPerTile - 1 <= i_wave_min);
         const uint32_t lb = __builtin_amdgcn_perm((uint32_t)(ex >> 32), (uint32_t)ex,
                                                   hh ? 0x07050301u : 0x06040200u);
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            bf16x8 ka[KS], va[KS];
+        // The two 32-key sub-tiles are pipelined inside the wave (one wave per SIMD):
+        // sub-tile 0's dS runs under sub-tile 1's S and dP MFMAs, sub-tile 1's under
+        // sub-tile 0's dQ MFMAs.  Invisible keys get score -inf (weight 0) first.
+        auto read_kv = [&](int sub, bf16x8 (&ka)[KS], bf16x8 (&va)[KS]) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int ob = (kb ^ (32 * ks)) + sub * 32 * RB;
                 ka[ks] = as_bf16x8(ld16(tk + ob));
                 va[ks] = as_bf16x8(ld16(tv + ob));
             }
-            __builtin_amdgcn_sched_barrier(0);
-            f32x16 st = f32x16{}, dpt = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                st = mfma32(ka[ks], qf[ks], st);
-                dpt = mfma32(va[ks], df[ks], dpt);
-            }
-            bf16x8 ktr[DT][2];
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int rows = (sub * 32 + 16 * s2) * RB;
-                    ktr[dt][s2] = ld_tr(tk + ((t0 + rows) ^ (64 * dt)), tk + ((t1 + rows) ^ (64 * dt)));
-                }
-            __builtin_amdgcn_sched_barrier(0);
-            // ds^T for this lane's keys 32*sub + 16*(r/8) + 8*hh + r%8 and its row
-            float dsv[16];
+        };
+        auto ktr_of = [&](int sub, int dt, int s2) {
+            const int rows = (sub * 32 + 16 * s2) * RB;
+            return ld_tr(tk + ((t0 + rows) ^ (64 * dt)), tk + ((t1 + rows) ^ (64 * dt)));
+        };
+        // this lane's keys 32*sub + 16*(r/8) + 8*hh + r%8 and its row
+        auto mask_sub = [&](int sub, f32x16& stv) {
+            if (all_vis) return;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int kk = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-                float p = fast_exp2(fmaf(st[r], c, -lse2));
-                if (!all_vis && (kk > lim || ((lb >> (16 * sub + r)) & 1u))) p = 0.f;
-                dsv[r] = p * (dpt[r] - Di);
+                if (kk > lim || ((lb >> (16 * sub + r)) & 1u)) stv[r] = -INFINITY;
             }
-            bf16x8 dsb[2];
+        };
+        auto pack = [&](const float (&v)[16], bf16x8 (&b)[2]) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-                dsb[s2] = as_bf16x8(u32x4{pack2(dsv[8 * s2 + 0], dsv[8 * s2 + 1]),
-                                          pack2(dsv[8 * s2 + 2], dsv[8 * s2 + 3]),
-                                          pack2(dsv[8 * s2 + 4], dsv[8 * s2 + 5]),
-                                          pack2(dsv[8 * s2 + 6], dsv[8 * s2 + 7])});
-            // dQ^T += K^T dS^T: K^T columns d = 32*dt + lq, keys 32*sub + 16*s2 + 8*hh..
+                b[s2] = as_bf16x8(u32x4{pack2(v[8 * s2 + 0], v[8 * s2 + 1]), pack2(v[8 * s2 + 2], v[8 * s2 + 3]),
+                                        pack2(v[8 * s2 + 4], v[8 * s2 + 5]), pack2(v[8 * s2 + 6], v[8 * s2 + 7])});
+        };
+        // A: sub-tile 0's S and dP.
+        bf16x8 ka0[KS], va0[KS];
+        read_kv(0, ka0, va0);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 st0 = f32x16{}, dp0 = f32x16{};
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma32(ktr[dt][s2], dsb[s2], o[dt]);
+        for (int ks = 0; ks < KS; ++ks) {
+            st0 = mfma32(ka0[ks], qf[ks], st0);
+            dp0 = mfma32(va0[ks], df[ks], dp0);
         }
+        bf16x8 ka1[KS], va1[KS], ktr[DT][2];
+        read_kv(1, ka1, va1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) ktr[dt][s2] = ktr_of(0, dt, s2);
+        __builtin_amdgcn_sched_barrier(0);
+        mask_sub(0, st0);
+        // B: sub-tile 1's S and dP with sub-tile 0's dS.
+        float dsv[16];
+        f32x16 st1 = f32x16{}, dp1 = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            st1 = mfma32(ka1[ks], qf[ks], st1);
+            dp1 = mfma32(va1[ks], df[ks], dp1);
+#pragma unroll
+            for (int r = 16 * ks / KS; r < 16 * (ks + 1) / KS; ++r)
+                dsv[r] = fast_exp2(fmaf(st0[r], c, -lse2)) * (dp0[r] - Di);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 dsb0[2];
+        pack(dsv, dsb0);
+        __builtin_amdgcn_sched_barrier(0);
+        mask_sub(1, st1);
+        // C: sub-tile 0's dQ^T += K^T dS^T (K^T columns d = 32*dt + lq, keys
+        // 16*s2 + 8*hh.. of the sub-tile) with sub-tile 1's dS; each of sub-tile 1's
+        // K^T operands is read into the registers the MFMA has just taken its own from.
+#pragma unroll
+        for (int x = 0; x < 2 * DT; ++x) {
+            const int dt = x >> 1, s2 = x & 1;
+            o[dt] = mfma32(ktr[dt][s2], dsb0[s2], o[dt]);
+            ktr[dt][s2] = ktr_of(1, dt, s2);
+#pragma unroll
+            for (int r = 16 * x / (2 * DT); r < 16 * (x + 1) / (2 * DT); ++r)
+                dsv[r] = fast_exp2(fmaf(st1[r], c, -lse2)) * (dp1[r] - Di);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 dsb1[2];
+        pack(dsv, dsb1);
+        // E: sub-tile 1's dQ.
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma32(ktr[dt][s2], dsb1[s2], o[dt]);
         publish();
     }
     if (!row_ok) return;
