@@ -219,7 +219,7 @@ def steady_chunk(wl, dims, step_kw, bufs, reps: int = 10):
 
 def measured_peaks():
     """Achievable rates on this GPU for comparison with the datasheet peaks: a large bf16
-    GEMM through torch (hipBLASLt) and a 1 GiB device copy."""
+    GEMM through torch (hipBLASLt), a 1 GiB device copy and a 1 GiB read (torch's sum)."""
     import torch
     dev = torch.device("cuda:0")
     n = 8192
@@ -248,8 +248,19 @@ def measured_peaks():
     e1.record()
     torch.cuda.synchronize()
     copy = 2.0 * src.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
-    return {"gemm_bf16_8192_tflops": round(gemm, 1), "copy_1gib_gbs": round(copy, 1)}
+    del dst
+    for _ in range(3):
+        src.sum()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        src.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read = src.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src
+    return {"gemm_bf16_8192_tflops": round(gemm, 1), "copy_1gib_gbs": round(copy, 1),
+            "read_1gib_gbs": round(read, 1)}
 
 
 def run_decode(args):
@@ -342,6 +353,7 @@ def run_decode(args):
     dec = timers["decode"]
     kv_bytes = B * Hkv * NC * 2 * D * 2            # K and V rows read by the attention launch
     achieved = kv_bytes / (dec.mean_ms * 1e-3) / 1e9
+    peaks = measured_peaks()
     line = {
         "metric": {"h2o": DECODE_METRIC, "h2o_buffer": BUFFER_DECODE_METRIC,
                    "lastrec": LASTREC_DECODE_METRIC}[args.policy],
@@ -365,6 +377,7 @@ def run_decode(args):
                      "traffic": read_traffic(DECODE_TRAFFIC_FILE),
                      "kernel": "decode_attn_kernel<128>", "launches": dec.launches,
                      "mean_launch_us": round(dec.mean_ms * 1e3, 2)},
+        "measured_peaks": peaks,
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

@@ -699,15 +699,21 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
 #pragma unroll
         for (int kbl = 0; kbl < KB; ++kbl) r[kbl] = f32x16{};
         if (full) {
-            bf16x8 qr[2];
-            if (do_mfma) qr[0] = qread(sQm, subm, 0);
+            // Q fragments are read two k-steps ahead of their MFMA (one ahead
+            // left the LDS latency exposed: 89 us against 87 us per chunk).
+            constexpr int QA = 2;
+            bf16x8 qr[QA + 1];
+            if (do_mfma) {
+#pragma unroll
+                for (int j = 0; j < QA; ++j) qr[j] = qread(sQm, subm, j);
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if (do_mfma) {
-                    if (ks + 1 < KS) qr[(ks + 1) & 1] = qread(sQm, subm, ks + 1);
+                    if (ks + QA < KS) qr[(ks + QA) % (QA + 1)] = qread(sQm, subm, ks + QA);
 #pragma unroll
                     for (int kbl = 0; kbl < KB; ++kbl)
-                        r[kbl] = mfma32(kf[kbl][ks], qr[ks & 1], r[kbl]);
+                        r[kbl] = mfma32(kf[kbl][ks], qr[ks % (QA + 1)], r[kbl]);
                 }
 #pragma unroll
                 for (int e = 0; e < PER; ++e) {
