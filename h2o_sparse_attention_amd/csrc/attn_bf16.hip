@@ -871,8 +871,8 @@ hipError_t launch_colsum_bf16(const ChunkArgs& a, int parts, float* part_ws, hip
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || parts == 1) return e;
     const int row = a.NC + a.S;
-    int bx = (row + 1023) / 1024;
-    if (bx > 64) bx = 64;
+    int bx = (row + 255) / 256;
+    if (bx > 256) bx = 256;
     hipLaunchKernelGGL(colsum_reduce_kernel, dim3(bx, a.B * a.Hkv), dim3(256), 0, s, a, parts,
                        part_ws);
     return hipGetLastError();

@@ -56,6 +56,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int pe
 // ------------------------------------------------------------------ select
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kHistCopies = 4;
 constexpr uint32_t kIneligible = 0xFFFFFFFEu;   // filled slot inside the recent window
 constexpr uint32_t kAbsent = 0xFFFFFFFFu;       // slot >= n: never a victim
 constexpr uint32_t kMaxEligible = 0xFF800001u;  // just above +inf: NaN scores rank here
@@ -104,7 +105,10 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sWave, int& tota
 // (score, slot index) order exactly.
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
-    __shared__ int sHist[2][256];
+    // kHistCopies copies of every bin, lane l adding to copy l % kHistCopies:
+    // scores cluster in a few exponent bins, and lanes of one instruction that
+    // hit the same LDS word serialize.
+    __shared__ int sHist[2][256 * kHistCopies];
     __shared__ int sSel[2];
     __shared__ int sWave[kSelWaves];
     const int bg = blockIdx.x;
@@ -237,9 +241,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
         int k_rem = k;                        // rank of T among the keys matching prefix
         // Two histograms: while wave 0 scans one, the other waves clear the other
         // for the next pass (its last reader, the scan before, ended at a barrier).
-        if (tid < 256) {
-            sHist[0][tid] = 0;
-            sHist[1][tid] = 0;
+        for (int x = tid; x < 256 * kHistCopies; x += kSelThreads) {
+            sHist[0][x] = 0;
+            sHist[1][x] = 0;
         }
         __syncthreads();
         int hb = 0;
@@ -247,15 +251,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
             int* hist = sHist[hb];
 #pragma unroll
             for (int e = 0; e < KPT; ++e)
-                if ((key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1);
+                if ((key[e] & mask) == prefix)
+                    atomicAdd(&hist[((key[e] >> shift) & 255u) * kHistCopies +
+                                    (lane & (kHistCopies - 1))], 1);
             __syncthreads();
             if (wave != 0) {
-                if (tid < 256 + 64) sHist[hb ^ 1][tid - 64] = 0;
+                for (int x = tid - 64; x < 256 * kHistCopies; x += kSelThreads - 64)
+                    sHist[hb ^ 1][x] = 0;
             } else {
                 int c4[4], sum = 0;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    c4[q] = hist[4 * lane + q];
+                    c4[q] = 0;
+#pragma unroll
+                    for (int cp = 0; cp < kHistCopies; ++cp)
+                        c4[q] += hist[(4 * lane + q) * kHistCopies + cp];
                     sum += c4[q];
                 }
                 int incl = sum;
