@@ -81,10 +81,16 @@ def test_steady_chunk_full_size(key):
          recent_window=7, seq_len=520),
     dict(dtype="f32", head_dim=64, n_q_heads=2, n_kv_heads=2, capacity=40, chunk=1,
          recent_window=2, seq_len=60),
-], ids=["bf16_d64_g3_S100", "bf16_mha_S33", "bf16_S1", "f32_d128_S65", "f32_S1"])
+    dict(dtype="bf16", head_dim=128, n_q_heads=6, n_kv_heads=2, capacity=70, chunk=1,
+         recent_window=4, seq_len=90),
+    dict(dtype="bf16", head_dim=128, n_q_heads=16, n_kv_heads=2, capacity=70, chunk=1,
+         recent_window=4, seq_len=90),
+], ids=["bf16_d64_g3_S100", "bf16_mha_S33", "bf16_S1", "f32_d128_S65", "f32_S1", "bf16_S1_g3",
+        "bf16_S1_g8"])
 def test_ragged_shapes(case):
-    """Chunk lengths and capacities that are not tile multiples, MHA and GQA 3/4,
-    single-token chunks, and capacities that are not multiples of the chunk."""
+    """Chunk lengths and capacities that are not tile multiples, MHA and GQA 3/4/8,
+    single-token chunks (decode) at GQA 3, 4 and 8, and capacities that are not multiples
+    of the chunk."""
     wl = W.workload(2, batch=2, heavy_count=4, sm_scale=case["head_dim"] ** -0.5, **case)
     H.run_chain(wl, range(wl.n_chunks), _chunk_getter(wl))
 
