@@ -391,6 +391,17 @@ __global__ __launch_bounds__(kOneThreads) void select1_insert_kernel(EvictArgs a
     const int thr = a.P - a.W;                   // eligible iff t(j) < P - W
     const int t_now = a.P + 1;
     const bool need_score = a.score_mode != kModeLastrec;
+    // The new token's K / V row and summed weight do not depend on the victim:
+    // load them with the scores so the insertion at the end only stores.
+    const int units = a.D * a.elem_bytes / 16;    // 16-byte units per row (<= 32)
+    const u32x4* kn = static_cast<const u32x4*>(a.kn) + (size_t)bg * units;
+    const u32x4* vn = static_cast<const u32x4*>(a.vn) + (size_t)bg * units;
+    u32x4 knv = {0u, 0u, 0u, 0u}, vnv = {0u, 0u, 0u, 0u};
+    if (tid < units) {
+        knv = kn[tid];
+        vnv = vn[tid];
+    }
+    const float cs_tok = (tid == 0 && a.cs_new) ? a.cs_new[bg] : 0.f;
     const dev::Rsrc rs = dev::make_rsrc(sc, n * 4), rp = dev::make_rsrc(ps, n * 4);
     uint64_t best = ~0ull;
     for (int base = 0; base < n; base += 4 * kOneThreads * kOneLoads) {
@@ -461,19 +472,16 @@ __global__ __launch_bounds__(kOneThreads) void select1_insert_kernel(EvictArgs a
     for (int w = 1; w < kOneThreads / 64; ++w) m = sBest[w] < m ? sBest[w] : m;
     const int victim = (int)(uint32_t)m;
     // The new token into the victim's slot.
-    const int units = a.D * a.elem_bytes / 16;    // 16-byte units per row
     u32x4* kc = static_cast<u32x4*>(a.kc) + ((size_t)bg * NC + victim) * units;
     u32x4* vc = static_cast<u32x4*>(a.vc) + ((size_t)bg * NC + victim) * units;
-    const u32x4* kn = static_cast<const u32x4*>(a.kn) + (size_t)bg * units;
-    const u32x4* vn = static_cast<const u32x4*>(a.vn) + (size_t)bg * units;
-    for (int u = tid; u < units; u += kOneThreads) {
-        kc[u] = kn[u];
-        vc[u] = vn[u];
+    if (tid < units) {
+        kc[tid] = knv;
+        vc[tid] = vnv;
     }
     if (tid == 0) {
         a.freed[bg] = victim;
         a.pos[(size_t)bg * NC + victim] = a.P;
-        a.score[(size_t)bg * NC + victim] = a.cs_new ? a.cs_new[bg] : 0.f;
+        a.score[(size_t)bg * NC + victim] = cs_tok;
     }
 }
 
