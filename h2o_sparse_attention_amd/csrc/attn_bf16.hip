@@ -399,6 +399,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
             snext[0] = f32x16{};
             snext[1] = f32x16{};
             float p[8];
+            // Raised wave priority in this phase: the two waves of a SIMD run in
+            // lockstep, and favouring the one in its QK^T phase keeps the MFMA
+            // pipe fed (140 -> 138 us; the same in the P V phase: no change).
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if (ks + 1 < KS) {
@@ -419,6 +423,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
             // Keep the exponentials here: their only uses come after a branch
             // and would otherwise be sunk past it, out of the MFMA stream.
 #pragma unroll
@@ -757,8 +762,11 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
         float* ln = odd ? sL0 : sL1;
         const bool has_next = rt + 1 < t_hi;
         const float l0 = lse2_of(lc, rt, 0), l1 = lse2_of(lc, rt, 1);
-        // A: MFMAs of (rt, 1) with the exponentials of (rt, 0).
+        // A: MFMAs of (rt, 1) with the exponentials of (rt, 0), at raised wave
+        // priority (81.7 -> 81.1 us).
+        __builtin_amdgcn_s_setprio(1);
         stage(std::true_type{}, qc, 1, s0, l0, full_tile(rt, 0), rt, 0, s1);
+        __builtin_amdgcn_s_setprio(0);
         publish_lds_loads();
         // B: loads of tile rt+2 into tile rt's buffer; MFMAs of (rt+1, 0) with
         // the exponentials of (rt, 1).
