@@ -176,7 +176,12 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
     }
     for (; sub < nsub; sub += kDecWaves) {
         const int next = sub + kDecWaves;
+        // The next tile's loads go out at raised wave priority: waves that are
+        // issuing loads win the arbitration against waves in their MFMA / softmax
+        // work, which keeps more of the cache stream in flight (199 -> 193 us).
+        __builtin_amdgcn_s_setprio(1);
         if (next < nsub) gload(next);
+        __builtin_amdgcn_s_setprio(0);
         f32x16 s = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
