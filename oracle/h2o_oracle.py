@@ -27,7 +27,7 @@ Readings taken where the pages are silent or garbled:
   whose position is older than P - W; victims are the k smallest by
   (score, slot index); chunk token i goes to the i-th smallest freed slot;
 * a newly inserted token starts with its own in-chunk summed weight as score;
-* h2o-norm divides the score by the age t - t(j) with t = P + S, in float32;
+* h2o-norm divides the score by the age t - t(j) with t = P + S;
 * lastrec ("Experimental Validation", the lr policy: the first beta and the
   last N_C - beta tokens stay) evicts the k oldest filled slots whose position
   is at least beta, and refuses a chunk when fewer are eligible;
@@ -138,12 +138,10 @@ def selection_scores(state: H2OState, S: int, score_mode: str = "h2o"):
     if score_mode == "h2o":
         return state.phi
     if score_mode == "h2o_norm":
-        # The ratio decides which slot is evicted, so it is formed in float32, the
-        # precision the kernel forms it in (IEEE division of the float32 score by the
-        # exact float32 age).
+        # phi / (t - t(j)) with t = P + S: the age counts the chunk being processed,
+        # so it is at least 1 for every cached token.
         t_now = state.P + S
-        age = (t_now - state.pos).astype(np.float32)
-        return (state.phi.astype(np.float32) / age).astype(np.float64)
+        return state.phi / (t_now - state.pos).astype(np.float64)
     raise ValueError(score_mode)
 
 
@@ -205,13 +203,14 @@ def h2o_step(state: H2OState, q, k_new, v_new, sm_scale: float, W: int,
     out, lse, cs_cache, cs_new = attend_chunk(state, q, k_new, v_new, sm_scale)
     update_scores(state, cs_cache)
     phi_after_update = state.phi.copy()
+    rank = selection_scores(state, S, score_mode).copy()
     victims = select_victims(state, S, W, score_mode)
     evicted_phi = np.take_along_axis(state.phi, victims, axis=2) if victims.size else \
         np.zeros(victims.shape)
     freed = evict_and_insert(state, victims, np.asarray(k_new, np.float64),
                              np.asarray(v_new, np.float64), cs_new)
     return {"out": out, "lse": lse, "colsum_cache": cs_cache, "colsum_new": cs_new,
-            "phi_updated": phi_after_update, "victims": victims,
+            "phi_updated": phi_after_update, "rank": rank, "victims": victims,
             "evicted_phi": evicted_phi, "freed_slots": freed}
 
 
