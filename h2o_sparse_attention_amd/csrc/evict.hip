@@ -172,7 +172,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
         for (int e = 0; e < KPT; ++e) key[e] = sKeys[j0 + e + (j0 + e) / 16];
 
         if (k == 1) {
-            // Single victim (decode): argmin of (key, slot), one reduction.
+            // Single victim: argmin of (key, slot), one reduction.  The empty-slot
+            // targets (S > 1) follow below like those of the radix path.
             uint64_t best = ~0ull;
 #pragma unroll
             for (int e = 0; e < KPT; ++e) {
@@ -192,126 +193,126 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
                 for (int w = 1; w < kSelWaves; ++w) m = sBest[w] < m ? sBest[w] : m;
                 freed[0] = (int)(uint32_t)m;
             }
-            return;
-        }
-        // Skip the leading digits that every candidate for T shares: T lies in
-        // [lo, hi] with lo the smallest key and hi the largest eligible key when
-        // at least k are eligible (else the largest possible key), so digits
-        // where lo and hi agree are T's digits too, and no key lies below them.
-        // Positions (lastrec) share their high bytes: their passes would pile
-        // every key into one histogram bin.
-        uint32_t lo = ~0u, hi = 0u;
-        int elig = 0;
+        } else {
+            // Skip the leading digits that every candidate for T shares: T lies in
+            // [lo, hi] with lo the smallest key and hi the largest eligible key when
+            // at least k are eligible (else the largest possible key), so digits
+            // where lo and hi agree are T's digits too, and no key lies below them.
+            // Positions (lastrec) share their high bytes: their passes would pile
+            // every key into one histogram bin.
+            uint32_t lo = ~0u, hi = 0u;
+            int elig = 0;
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            lo = min(lo, key[e]);
-            const bool is_e = key[e] < kIneligible;
-            hi = is_e ? max(hi, key[e]) : hi;
-            elig += is_e;
-        }
+            for (int e = 0; e < KPT; ++e) {
+                lo = min(lo, key[e]);
+                const bool is_e = key[e] < kIneligible;
+                hi = is_e ? max(hi, key[e]) : hi;
+                elig += is_e;
+            }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
-            hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
-            elig += __shfl_xor(elig, off);
-        }
-        __shared__ uint32_t sLo[kSelWaves], sHi[kSelWaves];
-        __shared__ int sElig[kSelWaves];
-        if (lane == 0) {
-            sLo[wave] = lo;
-            sHi[wave] = hi;
-            sElig[wave] = elig;
-        }
-        __syncthreads();
-        lo = ~0u;
-        hi = 0u;
-        elig = 0;
-#pragma unroll
-        for (int w = 0; w < kSelWaves; ++w) {
-            lo = min(lo, sLo[w]);
-            hi = max(hi, sHi[w]);
-            elig += sElig[w];
-        }
-        if (elig < k) hi = ~0u;
-        const uint32_t diff = lo ^ hi;
-        // Highest digit where lo and hi differ (-8: none, T == lo).
-        const int top = diff ? ((31 - __clz((int)diff)) & ~7) : -8;
-        uint32_t mask = top >= 24 ? 0u : ~0u << (top + 8);
-        uint32_t prefix = lo & mask;
-        int k_rem = k;                        // rank of T among the keys matching prefix
-        // Two histograms: while wave 0 scans one, the other waves clear the other
-        // for the next pass (its last reader, the scan before, ended at a barrier).
-        for (int x = tid; x < 256 * kHistCopies; x += kSelThreads) {
-            sHist[0][x] = 0;
-            sHist[1][x] = 0;
-        }
-        __syncthreads();
-        int hb = 0;
-        for (int shift = top; shift >= 0; shift -= 8, hb ^= 1) {
-            int* hist = sHist[hb];
-#pragma unroll
-            for (int e = 0; e < KPT; ++e)
-                if ((key[e] & mask) == prefix)
-                    atomicAdd(&hist[((key[e] >> shift) & 255u) * kHistCopies +
-                                    (lane & (kHistCopies - 1))], 1);
-            __syncthreads();
-            if (wave != 0) {
-                for (int x = tid - 64; x < 256 * kHistCopies; x += kSelThreads - 64)
-                    sHist[hb ^ 1][x] = 0;
-            } else {
-                int c4[4], sum = 0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    c4[q] = 0;
-#pragma unroll
-                    for (int cp = 0; cp < kHistCopies; ++cp)
-                        c4[q] += hist[(4 * lane + q) * kHistCopies + cp];
-                    sum += c4[q];
-                }
-                int incl = sum;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const int y = __shfl_up(incl, off);
-                    if (lane >= off) incl += y;
-                }
-                int before = incl - sum;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    if (before < k_rem && before + c4[q] >= k_rem) {
-                        sSel[0] = 4 * lane + q;
-                        sSel[1] = before;
-                    }
-                    before += c4[q];
-                }
+            for (int off = 32; off >= 1; off >>= 1) {
+                lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+                hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+                elig += __shfl_xor(elig, off);
+            }
+            __shared__ uint32_t sLo[kSelWaves], sHi[kSelWaves];
+            __shared__ int sElig[kSelWaves];
+            if (lane == 0) {
+                sLo[wave] = lo;
+                sHi[wave] = hi;
+                sElig[wave] = elig;
             }
             __syncthreads();
-            prefix |= (uint32_t)sSel[0] << shift;
-            mask |= 255u << shift;
-            k_rem -= sSel[1];
-        }
-        const uint32_t T = prefix;
-        // T is the k-th smallest key: count(< T) < k <= count(<= T).  One scan of
-        // the packed counts (less in the low 16 bits, equal in the high: at most
-        // N_C <= 32768 each) gives, in slot order, the keys below T and the keys
-        // equal to T before each thread; a victim's output index is the number of
-        // victims before it: the keys below T plus the first need_eq equal keys.
-        int my_less = 0, my_eq = 0;
+            lo = ~0u;
+            hi = 0u;
+            elig = 0;
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            my_less += key[e] < T;
-            my_eq += (key[e] == T) && (j0 + e < n);
-        }
-        int total;
-        const int before = block_exclusive_scan(my_less | (my_eq << 16), sWave, total);
-        const int need_eq = k - (total & 0xFFFF);
-        int less_run = before & 0xFFFF, eq_run = before >> 16;
+            for (int w = 0; w < kSelWaves; ++w) {
+                lo = min(lo, sLo[w]);
+                hi = max(hi, sHi[w]);
+                elig += sElig[w];
+            }
+            if (elig < k) hi = ~0u;
+            const uint32_t diff = lo ^ hi;
+            // Highest digit where lo and hi differ (-8: none, T == lo).
+            const int top = diff ? ((31 - __clz((int)diff)) & ~7) : -8;
+            uint32_t mask = top >= 24 ? 0u : ~0u << (top + 8);
+            uint32_t prefix = lo & mask;
+            int k_rem = k;                        // rank of T among the keys matching prefix
+            // Two histograms: while wave 0 scans one, the other waves clear the other
+            // for the next pass (its last reader, the scan before, ended at a barrier).
+            for (int x = tid; x < 256 * kHistCopies; x += kSelThreads) {
+                sHist[0][x] = 0;
+                sHist[1][x] = 0;
+            }
+            __syncthreads();
+            int hb = 0;
+            for (int shift = top; shift >= 0; shift -= 8, hb ^= 1) {
+                int* hist = sHist[hb];
 #pragma unroll
-        for (int e = 0; e < KPT; ++e) {
-            const bool lt = key[e] < T;
-            const bool eq = (key[e] == T) && (j0 + e < n);
-            if (lt || (eq && eq_run < need_eq)) freed[less_run + min(eq_run, need_eq)] = j0 + e;
-            less_run += lt;
-            eq_run += eq;
+                for (int e = 0; e < KPT; ++e)
+                    if ((key[e] & mask) == prefix)
+                        atomicAdd(&hist[((key[e] >> shift) & 255u) * kHistCopies +
+                                        (lane & (kHistCopies - 1))], 1);
+                __syncthreads();
+                if (wave != 0) {
+                    for (int x = tid - 64; x < 256 * kHistCopies; x += kSelThreads - 64)
+                        sHist[hb ^ 1][x] = 0;
+                } else {
+                    int c4[4], sum = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        c4[q] = 0;
+#pragma unroll
+                        for (int cp = 0; cp < kHistCopies; ++cp)
+                            c4[q] += hist[(4 * lane + q) * kHistCopies + cp];
+                        sum += c4[q];
+                    }
+                    int incl = sum;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const int y = __shfl_up(incl, off);
+                        if (lane >= off) incl += y;
+                    }
+                    int before = incl - sum;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (before < k_rem && before + c4[q] >= k_rem) {
+                            sSel[0] = 4 * lane + q;
+                            sSel[1] = before;
+                        }
+                        before += c4[q];
+                    }
+                }
+                __syncthreads();
+                prefix |= (uint32_t)sSel[0] << shift;
+                mask |= 255u << shift;
+                k_rem -= sSel[1];
+            }
+            const uint32_t T = prefix;
+            // T is the k-th smallest key: count(< T) < k <= count(<= T).  One scan of
+            // the packed counts (less in the low 16 bits, equal in the high: at most
+            // N_C <= 32768 each) gives, in slot order, the keys below T and the keys
+            // equal to T before each thread; a victim's output index is the number of
+            // victims before it: the keys below T plus the first need_eq equal keys.
+            int my_less = 0, my_eq = 0;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                my_less += key[e] < T;
+                my_eq += (key[e] == T) && (j0 + e < n);
+            }
+            int total;
+            const int before = block_exclusive_scan(my_less | (my_eq << 16), sWave, total);
+            const int need_eq = k - (total & 0xFFFF);
+            int less_run = before & 0xFFFF, eq_run = before >> 16;
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const bool lt = key[e] < T;
+                const bool eq = (key[e] == T) && (j0 + e < n);
+                if (lt || (eq && eq_run < need_eq)) freed[less_run + min(eq_run, need_eq)] = j0 + e;
+                less_run += lt;
+                eq_run += eq;
+            }
         }
     }
     for (int e = tid; e < n_new - n; e += kSelThreads) freed[k + e] = n + e;

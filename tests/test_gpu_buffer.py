@@ -53,11 +53,7 @@ def buffer_chunk(cache, st, x, wl, score_mode="h2o", where=""):
 
     # attention
     g = {"out": H.host(out), "lse": H.host(lse)}
-    diff = np.abs(g["out"] - r["out"])
-    assert (diff <= tol["out_abs"] + tol["out_rel"] * np.abs(r["out"])).all(), \
-        f"{where} out max-abs {diff.max():.3e}"
-    l2 = np.linalg.norm(g["out"] - r["out"]) / np.linalg.norm(r["out"])
-    assert l2 <= tol["out_rel_l2"], f"{where} out rel-L2 {l2:.3e}"
+    H.check_out(g["out"], r["out"], wl.dtype, where)
     assert np.abs(g["lse"] - r["lse"]).max() <= tol["lse_abs"], f"{where} lse"
     # summed weights: survivors keep their slot; chunk token i' is the slot it went to
     csc, csn = H.host(cs_cache), H.host(cs_new)
@@ -133,6 +129,35 @@ def test_buffer_ragged(case):
     split decode kernels with the overwritten slot excluded)."""
     wl = W.workload(2, batch=2, heavy_count=4, sm_scale=case["head_dim"] ** -0.5, **case)
     run_buffer_chain(wl, range(wl.n_chunks), _chunks(wl))
+
+
+@pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
+def test_buffer_one_victim_with_empty_targets(score_mode):
+    """N_C = 11, S = 3, W = 5: the fourth chunk's targets are one victim and the two
+    empty slots (k = 1 with S > 1), later chunks evict 3 each."""
+    wl = W.workload(2, batch=2, n_q_heads=4, n_kv_heads=2, capacity=11, recent_window=5,
+                    chunk=3, seq_len=30, heavy_count=3)
+    run_buffer_chain(wl, range(wl.n_chunks), _chunks(wl), score_mode=score_mode)
+
+
+def test_buffer_select_one_victim_full_size():
+    """h2o_select_slots on an 8192-slot cache holding 7169 tokens, chunk 1024: the
+    targets are the one oracle victim and the 1023 empty slots."""
+    wl = W.WORKLOADS[2]
+    s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=9, tie_fraction=0.2)
+    n = wl.capacity - wl.chunk + 1
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], n, s["start"])
+    st.pos[:, :, n:] = -1
+    st.phi[:, :, n:] = 0.0
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    freed = h2o.select_slots(cache, st.P, wl.chunk)
+    torch.cuda.synchronize()
+    victims = oracle.select_victims(st, wl.chunk, wl.recent_window)
+    want = np.concatenate([victims, np.broadcast_to(np.arange(n, wl.capacity),
+                                                    victims.shape[:2] + (wl.chunk - 1,))],
+                          axis=2)
+    assert (H.host(freed) == want).all()
 
 
 @pytest.mark.parametrize("key", [2, 3])

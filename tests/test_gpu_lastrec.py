@@ -23,11 +23,7 @@ import h2o_sparse_attention_amd as h2o  # noqa: E402
 
 def _compare_out(g_out, g_lse, r, dtype, where):
     tol = H.TOL[dtype]
-    diff = np.abs(g_out - r["out"])
-    bound = tol["out_abs"] + tol["out_rel"] * np.abs(r["out"])
-    assert (diff <= bound).all(), f"{where} out max-abs {diff.max():.3e}"
-    l2 = np.linalg.norm(g_out - r["out"]) / np.linalg.norm(r["out"])
-    assert l2 <= tol["out_rel_l2"], f"{where} out rel-L2 {l2:.3e}"
+    H.check_out(g_out, r["out"], dtype, where)
     d_lse = np.abs(g_lse - r["lse"]).max()
     assert d_lse <= tol["lse_abs"], f"{where} lse abs {d_lse:.3e}"
 
@@ -92,6 +88,18 @@ def test_lastrec_ragged(case):
     wl = W.workload(2, batch=2, heavy_count=4, recent_window=0,
                     sm_scale=case["head_dim"] ** -0.5, **case)
     run_lastrec_chain(wl, range(wl.n_chunks), lambda c: W.chunk_inputs(wl, 0, c), sink)
+
+
+def test_lastrec_one_victim_with_empty_targets():
+    """N_C = 11, S = 3, beta = 2: the fourth chunk's targets are one victim (the oldest
+    non-sink token) and the two empty slots; later chunks evict 3 each."""
+    wl = W.workload(2, batch=2, n_q_heads=4, n_kv_heads=2, capacity=11, recent_window=0,
+                    chunk=3, seq_len=30, heavy_count=3)
+    cache, st = run_lastrec_chain(wl, range(wl.n_chunks), lambda c: W.chunk_inputs(wl, 0, c), 2)
+    want = {0, 1} | set(range(30 - 9, 30))
+    for b in range(2):
+        for g in range(2):
+            assert set(H.host(cache.pos)[b, g].tolist()) == want
 
 
 @pytest.mark.parametrize("key,sink", [(2, 64), (3, 1000)])

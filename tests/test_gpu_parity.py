@@ -95,12 +95,35 @@ def test_ragged_shapes(case):
     H.run_chain(wl, range(wl.n_chunks), _chunk_getter(wl))
 
 
-def _isolated_evict(wl, score_mode, seed):
-    s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=seed, tie_fraction=0.2)
-    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+def one_victim_workload(dtype="bf16", head_dim=128):
+    """N_C = 11, S = 3, W = 5: after three filling chunks n = 9, so the fourth chunk has
+    n + S = N_C + 1 (one victim and two empty slots as targets); later chunks evict 3."""
+    return W.workload(2, batch=2, n_q_heads=4, n_kv_heads=2, head_dim=head_dim, capacity=11,
+                      recent_window=5, chunk=3, seq_len=30, heavy_count=3, dtype=dtype,
+                      sm_scale=head_dim ** -0.5)
+
+
+@pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_chain_one_victim_with_empty_targets(score_mode, dtype, head_dim):
+    """Free-running chain through the chunk whose targets are one victim plus empty
+    slots (k = 1 with S = 3), then chunks evicting 3 each."""
+    wl = one_victim_workload(dtype, head_dim)
+    assert [max(0, min(wl.capacity, c * wl.chunk) + wl.chunk - wl.capacity)
+            for c in range(5)] == [0, 0, 0, 1, 3]
+    H.run_chain(wl, range(wl.n_chunks), _chunk_getter(wl), score_mode=score_mode)
+
+
+def _isolated_evict(wl, score_mode, seed, state=None):
+    if state is None:
+        s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=seed, tie_fraction=0.2)
+        state = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"],
+                                            s["start"])
+    st = state
+    before = st.copy()
     cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
     H.load_oracle_state(cache, st, wl.dtype)
-    x = W.chunk_inputs(wl, 0, 20)
+    x = W.chunk_inputs(wl, 0, st.P // wl.chunk)
     cs_new = np.random.default_rng(seed).random((wl.batch, wl.n_kv_heads, wl.chunk)).astype(
         np.float32)
     k, v = H.dev(x["k"], torch.bfloat16), H.dev(x["v"], torch.bfloat16)
@@ -109,7 +132,30 @@ def _isolated_evict(wl, score_mode, seed):
     torch.cuda.synchronize()
     victims = oracle.select_victims(st, wl.chunk, wl.recent_window, score_mode)
     want = oracle.evict_and_insert(st, victims, x["k"], x["v"], cs_new)
-    return freed, cache, st, want
+    return freed, cache, st, want, before, x, cs_new
+
+
+def _check_isolated(wl, score_mode, freed, cache, st, want, before, x, cs_new):
+    """h2o: the targets and the cache bit-exact.  h2o-norm: the GPU forms score / age in
+    float32, the oracle in fp64, so a swap across the cut is accepted when the two
+    ratios are within 1e-5 of the cut; the cache must then be exactly what the oracle's
+    insertion gives for the GPU's own targets."""
+    g = H.host(freed).astype(np.int64)
+    if score_mode == "h2o":
+        assert (g == want).all()
+    else:
+        rank = oracle.selection_scores(before, wl.chunk, score_mode)
+        swaps = H.compare_victims(g, want, rank, before.pos, before.n, before.P,
+                                  wl.recent_window, "isolated")
+        print("h2o-norm near-tie swaps:", swaps)
+        if swaps:
+            st = before.copy()
+            victims = np.stack([np.stack([row[row < before.n] for row in gb]) for gb in g])
+            oracle.evict_and_insert(st, victims, x["k"], x["v"], cs_new)
+    assert (H.host(cache.pos) == st.pos).all()
+    assert (H.host(cache.k) == st.K).all() and (H.host(cache.v) == st.V).all()
+    assert (H.host(cache.score) == st.phi).all()
+    assert cache.n_valid == st.n
 
 
 @pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
@@ -118,12 +164,33 @@ def test_evict_isolated_bit_exact(score_mode, seed):
     """Same scores in, same victims out: selection and insertion are bit-exact at the
     full chunk-1k size, with 20% of the scores set to three shared values (ties)."""
     wl = W.WORKLOADS[2]
-    freed, cache, st, want = _isolated_evict(wl, score_mode, seed)
-    assert (H.host(freed) == want).all()
-    assert (H.host(cache.pos) == st.pos).all()
-    assert (H.host(cache.k) == st.K).all() and (H.host(cache.v) == st.V).all()
-    assert (H.host(cache.score) == st.phi).all()
-    assert cache.n_valid == st.n
+    res = _isolated_evict(wl, score_mode, seed)
+    _check_isolated(wl, score_mode, *res)
+
+
+def _partly_filled_state(wl, n, seed):
+    """A cache holding n < N_C tokens (slots [n, N_C) empty), positions below P in
+    random slot order, LogNormal scores with shared values (ties)."""
+    s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=seed, tie_fraction=0.2)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], n, s["start"])
+    st.pos[:, :, n:] = -1
+    st.phi[:, :, n:] = 0.0
+    st.K[:, :, n:] = 0.0
+    st.V[:, :, n:] = 0.0
+    return st
+
+
+@pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
+def test_evict_one_victim_with_empty_targets_full_size(score_mode):
+    """n + S = N_C + 1 with S > 1 (an 8192-slot cache holding 7169 tokens, then a 1024-token
+    chunk): one victim and 1023 empty slots are the targets, ascending."""
+    wl = W.WORKLOADS[2]
+    st = _partly_filled_state(wl, wl.capacity - wl.chunk + 1, seed=7)
+    res = _isolated_evict(wl, score_mode, 7, state=st)
+    _check_isolated(wl, score_mode, *res)
+    g = H.host(res[0])
+    assert (g[..., 0] < wl.capacity - wl.chunk + 1).all()
+    assert (g[..., 1:] == np.arange(wl.capacity - wl.chunk + 1, wl.capacity)).all()
 
 
 @pytest.mark.parametrize("fill", ["all_equal", "two_levels"])
@@ -151,7 +218,7 @@ def test_evict_degenerate_scores(fill):
 
 def test_evict_isolated_large_capacity():
     wl = W.workload(3, capacity=32768, chunk=2048, recent_window=512)
-    freed, cache, st, want = _isolated_evict(wl, "h2o", 3)
+    freed, cache, st, want = _isolated_evict(wl, "h2o", 3)[:4]
     assert (H.host(freed) == want).all()
     assert (H.host(cache.pos) == st.pos).all()
 
@@ -238,7 +305,7 @@ def test_layer_stack_interleaved_steady():
             r = oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window)
             H.compare_attention(g, r, n_before, wl.dtype, where)
             swaps = H.compare_victims(g["freed_slots"].astype(np.int64), r["freed_slots"],
-                                      r["phi_updated"], pos_before, n_before, P,
+                                      r["rank"], pos_before, n_before, P,
                                       wl.recent_window, where)
             if swaps:
                 H.load_oracle_state(cache, st, wl.dtype)
@@ -286,13 +353,20 @@ def test_decode_one_victim_fused_matches_separate(score_mode):
 
 
 @pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
-@pytest.mark.parametrize("case", ["steady_chunk", "decode", "filling", "f32_plumbing"])
+@pytest.mark.parametrize("case", ["steady_chunk", "decode", "filling", "f32_plumbing",
+                                  "one_victim_chunk"])
 def test_update_evict_fused_matches_separate(case, score_mode):
     """h2o_update_evict_and_insert gives bit for bit what h2o_update_scores followed by
     h2o_evict_and_insert gives: a full-size evicting chunk (k = 1024), a decode step (k = 1)
     and a filling chunk (k = 0, the update on its own)."""
     r = np.random.default_rng(21)
-    if case == "decode":
+    if case == "one_victim_chunk":
+        wl = W.WORKLOADS[2]
+        st1 = _partly_filled_state(wl, wl.capacity - wl.chunk + 1, seed=8)
+        s = {"k": st1.K, "v": st1.V, "pos": st1.pos, "phi": st1.phi, "n": st1.n,
+             "start": st1.P}
+        x = W.chunk_inputs(wl, 0, st1.P // wl.chunk)
+    elif case == "decode":
         wl = W.workload(5, batch=4)
         s = W.decode_initial_state(wl)
         x = W.decode_step_inputs(wl, 0)
