@@ -144,6 +144,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(1024))) u16 sK1[2][T::U16];
     __shared__ __attribute__((aligned(1024))) u16 sV0[2][T::U16];
     __shared__ __attribute__((aligned(1024))) u16 sV1[2][T::U16];
+    // Positions t(j) of the cache tile in each K stage, [stage][half][key].
+    __shared__ __attribute__((aligned(256))) int sPos[2][2][kKeysPerTile];
 
     const int R = a.G * a.S;
     const int nrb = (R + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -196,12 +198,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
         const int r = off / RB, cp = (off % RB) / 16;
         return r * RB + 16 * (cp ^ (is_v ? swz_v<D>(r) : swz_k<D>(r)));
     };
-    auto issue_k = [&](u16* dst, int jt) {
+    // K tile jt of this half into stage st; a cache tile's positions go with it
+    // (one 4-byte load per lane of the half's first wave).
+    const int32_t* posg = a.pos + (size_t)bg * a.NC;
+    auto issue_k = [&](int st, int jt) {
         const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
         const Rsrc rk = make_rsrc(tr.k, tr.valid * RB);
-        unsigned char* d = reinterpret_cast<unsigned char*>(dst) + rw * 1024;
+        unsigned char* d = reinterpret_cast<unsigned char*>(st ? sK1[kh] : sK0[kh]) + rw * 1024;
 #pragma unroll
         for (int it = 0; it < T::LOADS; ++it) load_lds16(rk, d + it * 4096, goff(it, false), 0);
+        if (tr.cache && rw == 0) load_lds4(make_rsrc(posg + tr.first, tr.valid * 4),
+                                           &sPos[st][kh][0], 4 * lane);
     };
     auto issue_v = [&](u16* dst, int jt) {
         const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
@@ -239,11 +246,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
                 sd[sub] = mfma32(as_bf16x8(ld16(base + ((kb ^ (32 * ks)) + sub * 32 * RB))),
                                  qf[ks], sd[sub]);
     };
-    // Visibility.  Filled cache slots hold positions below P (the cache only
-    // ever receives earlier tokens), so a cache key is visible to every row of
-    // the chunk and chunk key i' to row i iff i' <= i: within tile jt, key k is
-    // visible to this lane's row iff k <= lim(jt).  Tiles whose keys are all
-    // visible to every row of the wave skip the mask.
+    // Visibility: key j is visible to row i iff 0 <= t(j) <= P + i.  Chunk key
+    // i' sits at P + i', so it is visible iff i' <= i.  A filled cache slot
+    // normally holds an earlier token, 0 <= t(j) < P, visible to every row:
+    // within tile jt, key k is then visible to this lane's row iff k <= lim(jt).
+    // Tiles whose keys are all visible to every row of the wave skip the mask;
+    // cache slots outside [0, P) take the positional mask below.
     auto tile_lim = [&](int jt) {
         const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
         return tr.cache ? tr.valid - 1 : min(tr.valid - 1, i - tr.first);
@@ -273,6 +281,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
             for (int r = 0; r < 16; ++r)
                 if (sub * 32 + 16 * (r >> 3) + (r & 7) > d || ((lb >> (16 * sub + r)) & 1u))
                     sv[sub][r] = -INFINITY;
+    };
+    // Bits of the cache tile's keys (in stage st) whose position lies outside
+    // [0, P): a filled slot marked empty (never visible) or holding a token at
+    // or after the chunk start (visible from that position on).  A cache built
+    // by this library's insertions has none; the test costs one LDS read and a
+    // ballot per tile.
+    auto tile_irregular = [&](int jt, int st) -> uint64_t {
+        const TileRef tr = tile_ref(2 * jt + kh, cache_tiles, n, S, D, Kc, Vc, Kn, Vn);
+        if (!tr.cache) return 0ull;
+        const int tp = sPos[st][kh][lane];
+        return __ballot(lane < tr.valid && (tp < 0 || tp >= a.P));
+    };
+    // -inf for this lane's cache keys with t < 0 or t > P + i (the lane holds keys
+    // 32*sub + 16*(r/8) + 8*hh + r%8 of the tile).
+    auto apply_pos_mask = [&](f32x16 (&sv)[2], int st) {
+        const int qpos = a.P + i;
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tp = sPos[st][kh][32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7)];
+                if (tp < 0 || tp > qpos) sv[sub][r] = -INFINITY;
+            }
     };
     // Row max over both lane halves, running-max update and (rarely) the
     // rescale of O and l; returns m_run * c for the exponentials.
@@ -351,15 +382,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     f32x16 sA[2], sB[2];
     float mc = 0.f;
     if (mine > 0) {
-        issue_k(sK0[kh], 0);
+        issue_k(0, 0);
         issue_v(sV0[kh], 0);
     }
-    if (mine > 1) issue_k(sK1[kh], 1);
+    if (mine > 1) issue_k(1, 1);
     publish_lds_loads();
     if (mine > 0) {
         qk(sK0[kh], sA);
         const uint64_t ex0 = tile_excl(0);
         if (!tile_all_visible(0) || ex0 != 0) apply_mask(sA, tile_lim(0), ex0);
+        if (tile_irregular(0, 0) != 0) apply_pos_mask(sA, 0);
         mc = rescale_for(rowmax(sA));
     }
     // Iteration 0 loads K(2) into K(0)'s buffer: every wave must be done
@@ -373,11 +405,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     // stage jt&1 holds V(jt).
     auto iter = [&](auto odd_c, int jt, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
         constexpr bool odd = decltype(odd_c)::value;
-        u16* kfree = odd ? sK1[kh] : sK0[kh];
+        constexpr int st_free = odd ? 1 : 0;      // K stage of tile jt (consumed)
+        constexpr int st_next = odd ? 0 : 1;      // K stage of tile jt+1
         const u16* knext = odd ? sK0[kh] : sK1[kh];
         const u16* vcur = odd ? sV1[kh] : sV0[kh];
         u16* vnext = odd ? sV0[kh] : sV1[kh];
-        if (jt + 2 < mine) issue_k(kfree, jt + 2);
+        if (jt + 2 < mine) issue_k(st_free, jt + 2);
         if (jt + 1 < mine) issue_v(vnext, jt + 1);
         if (jt < mine) {
             const bool has_next = jt + 1 < mine;
@@ -434,6 +467,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
             if (has_next) {
                 const uint64_t exn = tile_excl(jt + 1);
                 if (!tile_all_visible(jt + 1) || exn != 0) apply_mask(snext, tile_lim(jt + 1), exn);
+                if (tile_irregular(jt + 1, st_next) != 0) apply_pos_mask(snext, st_next);
             }
             // Phase B: P V of this tile with the next tile's row max.
             const float mt = pv_max(vcur, pb, scur, snext, mc, lsum);
@@ -507,9 +541,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 // pass's K.  Each lane accumulates its 16 keys over its query column, and the
 // 32 columns are added in a fixed order at the end, so the result is
 // deterministic (no atomics).  Key blocks follow the same cache / chunk split
-// as the attention tiles.  Filled cache slots precede the chunk, so cache keys
-// are visible to every row; a chunk key is visible to the rows at or after its
-// own position, which only blocks near the diagonal have to test.
+// as the attention tiles.  A filled cache slot normally holds an earlier token
+// (0 <= t(j) < P), visible to every row; a chunk key is visible to the rows at
+// or after its own position, which only blocks near the diagonal have to test.
+// A wave whose cache keys include a slot outside [0, P) tests every row tile
+// against the positions (visible iff 0 <= t(j) <= P + i).
 //
 // Load balance: a key block's work is every row tile after its first visible
 // one; with few blocks per CU, whole blocks leave CUs idle at the end (576
@@ -571,6 +607,18 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
             kf[kbl][ks] = as_bf16x8(v);
         }
     }
+
+    // Positions of this wave's cache keys; irr: some lie outside [0, P) (none in a
+    // cache built by this library's insertions).
+    int tpos[KB];
+    bool irr_lane = false;
+#pragma unroll
+    for (int kbl = 0; kbl < KB; ++kbl) {
+        const int idx = first + 32 * kbl + lq;
+        tpos[kbl] = (is_cache && idx < limit) ? a.pos[(size_t)bg * a.NC + idx] : 0;
+        irr_lane |= tpos[kbl] < 0 || tpos[kbl] >= a.P;
+    }
+    const bool irr = __ballot(irr_lane) != 0;
 
     const int R = G * S;
     const int ntile = (R + kRowsPerTile - 1) / kRowsPerTile;
@@ -671,7 +719,7 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     // to every row of sub-tile (rt, sub)?
     const int kmax = min(first + 32 * KB - 1, limit - 1);   // largest key index of the wave
     auto full_tile = [&](int rt, int sub) {
-        if (is_cache) return true;
+        if (is_cache) return !irr;
         const int r0 = min(rt * kRowsPerTile + sub * 32, R - 1);
         const int i0 = G == 1 ? r0 : (int)__umulhi((uint32_t)r0, g_magic);
         return kmax <= i0;
@@ -682,6 +730,21 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
         __attribute__((always_inline)) {
         const int r = min(rt * kRowsPerTile + sub * 32 + lq, R - 1);
         const int ipos = G == 1 ? r : (int)__umulhi((uint32_t)r, g_magic);
+        if (is_cache) {
+            // Cache keys with positions outside [0, P): the lane's key
+            // 8*(e/4) + 4*hh + e%4 of each block has its position in lane
+            // (that key) of tpos.
+            const int qpos = a.P + ipos;
+#pragma unroll
+            for (int kbl = 0; kbl < KB; ++kbl)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int tk = __shfl(tpos[kbl], 8 * (e >> 2) + 4 * hh + (e & 3));
+                    const float p = fast_exp2(fmaf(sv[kbl][e], c, -lse2));
+                    acc[kbl][e] += (tk >= 0 && tk <= qpos) ? p : 0.f;
+                }
+            return;
+        }
         // key first + 4*hh + off is visible iff off <= dlim
         const int dlim = ipos - first - 4 * hh;
 #pragma unroll

@@ -248,6 +248,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
     constexpr int LOADS = TB / 1024 / kBwWaves;        // 1 KB loads per wave per tile
     __shared__ __attribute__((aligned(1024))) unsigned char sK[2][TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sV[2][TB];
+    __shared__ __attribute__((aligned(256))) int sPos[2][kBwKeysPerTile];   // cache tiles
 
     const int R = a.G * a.S;
     const int nrb = (R + kBwRowsPerBlock - 1) / kBwRowsPerBlock;
@@ -315,6 +316,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
             lds16(rk, &sK[stage][(it * kBwWaves + wave) * 1024], go);
             lds16(rv, &sV[stage][(it * kBwWaves + wave) * 1024], go);
         }
+        if (cache && wave == 0)
+            lds4(make_rsrc(a.pos + (size_t)bg * a.NC + first, valid * 4), &sPos[stage][0],
+                 4 * lane);
     };
     // A operand rows: physical key perm_key(lq) (+32 per sub-tile), k-step ks.
     const int prow = perm_key(lq);
@@ -338,7 +342,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
         const uint64_t ex = (cache && exrow != nullptr) ? exrow[jt] : 0ull;
         // keys k of the tile with k > lim are not visible to this lane's row
         const int lim = cache ? valid - 1 : min(valid - 1, i - first);
-        const bool all_vis = ex == 0 && valid == kBwKeysPerTile &&
+        // Cache keys whose position lies outside [0, P) are visible iff
+        // 0 <= t(j) <= P + i (none in a cache built by this library's insertions).
+        const bool irr = cache && __ballot(lane < valid && (sPos[stage][lane] < 0 ||
+                                                           sPos[stage][lane] >= a.P)) != 0;
+        const bool all_vis = ex == 0 && !irr && valid == kBwKeysPerTile &&
                              (cache || first + kBwKeysPerTile - 1 <= i_wave_min);
         const uint32_t lb = __builtin_amdgcn_perm((uint32_t)(ex >> 32), (uint32_t)ex,
                                                   hh ? 0x07050301u : 0x06040200u);
@@ -364,6 +372,13 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
             for (int r = 0; r < 16; ++r) {
                 const int kk = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
                 if (kk > lim || ((lb >> (16 * sub + r)) & 1u)) stv[r] = -INFINITY;
+            }
+            if (irr) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int tp = sPos[stage][32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7)];
+                    if (tp < 0 || tp > a.P + i) stv[r] = -INFINITY;
+                }
             }
         };
         auto pack = [&](const float (&v)[16], bf16x8 (&b)[2]) {
@@ -504,6 +519,12 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
         }
     }
 
+    // This lane's cache key position; irr: some key of the wave lies outside
+    // [0, P) and is visible iff 0 <= t(j) <= P + i (none in a cache built by this
+    // library's insertions).
+    const int tpos = (is_cache && key < limit) ? a.pos[(size_t)bg * a.NC + key] : 0;
+    const bool irr = __ballot(tpos < 0 || tpos >= a.P) != 0 && is_cache;
+
     const int R = G * S;
     const int ntile = (R + kBwRowsPerTile - 1) / kBwRowsPerTile;
     const int tile0 = is_cache ? 0 : (block_first * G) / kBwRowsPerTile;
@@ -599,16 +620,17 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
                 l2v[r] = (rows_in || rt * kBwRowsPerTile + rl < R) ? lr * kLog2e : INFINITY;
             }
         };
-        // Chunk keys near the diagonal: -inf for this lane's key at rows before it.
+        // Chunk keys near the diagonal: -inf for this lane's key at rows before it;
+        // cache keys outside [0, P): -inf where t(j) < 0 or t(j) > P + i.
         auto mask_sub = [&](int sub, f32x16& stv) {
             const int r0 = rt * kBwRowsPerTile + 32 * sub;
             const int i0 = G == 1 ? min(r0, R - 1) : (int)__umulhi((uint32_t)min(r0, R - 1), g_magic);
-            if (is_cache || kmax <= i0) return;
+            if (is_cache ? !irr : kmax <= i0) return;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int rr = r0 + 16 * (r >> 3) + 8 * hh + (r & 7);
+                const int rr = min(r0 + 16 * (r >> 3) + 8 * hh + (r & 7), R - 1);
                 const int ipos = G == 1 ? rr : (int)__umulhi((uint32_t)rr, g_magic);
-                if (key > ipos) stv[r] = -INFINITY;
+                if (is_cache ? (tpos < 0 || tpos > a.P + ipos) : key > ipos) stv[r] = -INFINITY;
             }
         };
         // P and dS = P (dP - D) of value r of a sub-tile.

@@ -161,3 +161,24 @@ def test_backward_full_size_deterministic():
     torch.cuda.synchronize()
     for name, a, b in zip(NAMES, *runs):
         assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_backward_positions_outside_chunk_start(dtype, head_dim):
+    """A cache whose filled slots include empty-marked slots (never visible) and slots
+    holding tokens at or after the chunk start (visible from their position on): the
+    backward applies the forward's positional mask."""
+    wl = W.workload(2, batch=2, n_q_heads=8, n_kv_heads=2, head_dim=head_dim, capacity=500,
+                    recent_window=64, chunk=128, seq_len=4096, heavy_count=20, dtype=dtype,
+                    sm_scale=head_dim ** -0.5)
+    s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=4)
+    n = wl.capacity - 37
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], n, s["start"])
+    st.pos[:, :, n:] = -1
+    r = np.random.default_rng(12)
+    for b in range(wl.batch):
+        for g in range(wl.n_kv_heads):
+            idx = r.choice(n, 40, replace=False)
+            st.pos[b, g, idx[:20]] = -1
+            st.pos[b, g, idx[20:]] = st.P + r.integers(0, wl.chunk + 64, 20)
+    check_backward(wl, st, W.chunk_inputs(wl, 0, 20), seed=3, where="positions")
