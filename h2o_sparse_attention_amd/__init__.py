@@ -139,6 +139,34 @@ def chunk_attn(cache: H2OCache, chunk_start: int, q, k_new, v_new, sm_scale: flo
     return out, lse, colsum_cache, colsum_new
 
 
+def chunk_attn_noalloc(cache: H2OCache, chunk_start: int, q, k_new, v_new, sm_scale: float,
+                       out, lse, colsum_cache=None, colsum_new=None, stream=None):
+    """h2o_chunk_attn_noalloc: h2o_chunk_attn with the library's static device scratch as
+    workspace (the library allocates nothing; the caller passes every output).  Both colsum
+    buffers None: no summed weights.  Returns (out, lse, colsum_cache, colsum_new)."""
+    d = cache.dims
+    B, Hq, Hkv, D, NC = d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim, d.capacity
+    S = q.shape[2]
+    _need(q, (B, Hq, S, D), d.torch_dtype, "q")
+    _need(k_new, (B, Hkv, S, D), d.torch_dtype, "k_new")
+    _need(v_new, (B, Hkv, S, D), d.torch_dtype, "v_new")
+    _need(out, (B, Hq, S, D), d.torch_dtype, "out")
+    _need(lse, (B, Hq, S), torch.float32, "lse")
+    if (colsum_cache is None) != (colsum_new is None):
+        raise ValueError("colsum_cache and colsum_new: both or neither")
+    cs_ptrs = (None, None)
+    if colsum_cache is not None:
+        _need(colsum_cache, (B, Hkv, NC), torch.float32, "colsum_cache")
+        _need(colsum_new, (B, Hkv, S), torch.float32, "colsum_new")
+        cs_ptrs = (colsum_cache.data_ptr(), colsum_new.data_ptr())
+    check(lib.h2o_chunk_attn_noalloc(ctypes.byref(d.c()), ctypes.byref(cache.c()),
+                                     int(chunk_start), S, float(sm_scale), q.data_ptr(),
+                                     k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(),
+                                     lse.data_ptr(), cs_ptrs[0], cs_ptrs[1],
+                                     _stream_ptr(stream, cache.k.device)))
+    return out, lse, colsum_cache, colsum_new
+
+
 def update_scores(cache: H2OCache, colsum_cache, stream=None):
     """h2o_update_scores: cache.score[..., :n_valid] += colsum_cache[..., :n_valid]."""
     d = cache.dims

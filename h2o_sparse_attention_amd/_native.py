@@ -66,6 +66,10 @@ _SIGNATURES = {
     "h2o_backward_workspace_bytes": (c_size_t, [POINTER(Dims), c_int32]),
     "h2o_chunk_attn_backward": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32,
                                           c_float] + [c_void_p] * 12 + [c_size_t, c_void_p]),
+    "h2o_noalloc_scratch_bytes": (c_size_t, []),
+    "h2o_chunk_attn_noalloc": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32,
+                                         c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_void_p, c_void_p]),
     "h2o_last_error": (c_char_p, []),
     "h2o_abi_version": (c_int32, []),
     "h2o_kernel_timer_start": (c_int32, [c_int32, c_int32]),

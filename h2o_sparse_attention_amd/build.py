@@ -18,7 +18,8 @@ OBJ_DIR = os.path.join(HERE, "_build")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libh2o.so")
 
-SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_bwd.hip", "evict.hip", "decode.hip"]
+SOURCES = ["api.hip", "attn_bf16.hip", "attn_f32.hip", "attn_bwd.hip", "evict.hip", "decode.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

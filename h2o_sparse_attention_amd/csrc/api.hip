@@ -241,6 +241,19 @@ size_t h2o_workspace_bytes(const h2o_dims_t* dims, int32_t chunk_len) {
 
 namespace h2o {
 
+h2o_status_t set_error(h2o_status_t st, const char* msg) { return fail(st, "%s", msg); }
+
+// Workspace: the decode partials; else the split summed-weights partials (bf16,
+// when summed weights are asked for) and the exclusion bits (buffer form).
+size_t chunk_attn_workspace_need(const h2o_dims_t* dims, int32_t chunk_len, bool summed_weights,
+                                 bool buffer_form) {
+    if (validate_dims(dims) != H2O_OK || chunk_len < 1) return 0;
+    if (uses_decode(dims, chunk_len)) return h2o_workspace_bytes(dims, chunk_len);
+    if (buffer_form) return excl_offset(dims, chunk_len) + excl_bytes(dims);
+    if (summed_weights && dims->dtype == H2O_BF16) return excl_offset(dims, chunk_len);
+    return 0;
+}
+
 // Shared body of h2o_chunk_attn and h2o_buffer_attn (freed != NULL: the
 // victims among the targets are not keys).
 h2o_status_t chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache, int64_t chunk_start,
@@ -268,12 +281,7 @@ h2o_status_t chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache, int64_
                         G, chunk_len);
     }
     const bool decode = uses_decode(dims, chunk_len);
-    // Workspace: the decode partials; else the split summed-weights partials
-    // (bf16, when summed weights are asked for) and the exclusion bits (buffer form).
-    size_t ws_need = 0;
-    if (decode) ws_need = h2o_workspace_bytes(dims, chunk_len);
-    else if (freed) ws_need = excl_offset(dims, chunk_len) + excl_bytes(dims);
-    else if (want_cs && dims->dtype == H2O_BF16) ws_need = excl_offset(dims, chunk_len);
+    const size_t ws_need = chunk_attn_workspace_need(dims, chunk_len, want_cs, freed != nullptr);
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
         return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", ws_need,
                     workspace ? workspace_bytes : (size_t)0);

@@ -92,4 +92,17 @@ void timer_end(int kernel, hipStream_t s);
 
 constexpr int kMaxCapacity = 32768;
 
+// Shared body of h2o_chunk_attn and h2o_buffer_attn (api.hip); freed != NULL is
+// the buffer form.
+h2o_status_t chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache, int64_t chunk_start,
+                        int32_t chunk_len, float sm_scale, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* freed, void* out, float* lse,
+                        float* colsum_cache, float* colsum_new, void* workspace,
+                        size_t workspace_bytes, void* stream);
+// Workspace bytes chunk_attn needs for this call (0: none, or invalid dims).
+size_t chunk_attn_workspace_need(const h2o_dims_t* dims, int32_t chunk_len, bool summed_weights,
+                                 bool buffer_form);
+// Records a non-OK status and its message for h2o_last_error (api.hip).
+h2o_status_t set_error(h2o_status_t st, const char* msg);
+
 }  // namespace h2o

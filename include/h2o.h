@@ -107,10 +107,13 @@ H2O_API size_t h2o_workspace_bytes(const h2o_dims_t *dims, int32_t chunk_len);
  * Chunk attention with summed weights ("Kernel Support Needs").
  * Query row i (0 <= i < S) sits at position P + i, P = chunk_start.  Keys are
  * the filled slots j < n_valid and the chunk's own keys (position P + i').  Key
- * j is visible to row i iff 0 <= t(j) <= P + i.  Precondition: every filled
- * slot holds a position in [0, P) (the cache only ever receives earlier
- * tokens, which h2o_evict_and_insert maintains), so every filled slot is
- * visible to every row and chunk key i' to rows i >= i'.  For every query
+ * j is visible to row i iff 0 <= t(j) <= P + i (the implicit mask
+ * -inf * 1[P+i < t(b,h,j)] of "Kernel Support Needs").  A cache filled by
+ * h2o_evict_and_insert holds earlier tokens only, 0 <= t(j) < P, each visible
+ * to every row, and chunk key i' is visible to rows i >= i'; a filled slot
+ * marked -1 is never visible, and one holding a position at or after P is
+ * visible from that row on (the kernels test positions per key tile, and take
+ * the per-element mask only for tiles that hold such slots).  For every query
  * head h:
  *   out[b,h,i]  = sum_j softmax_j(sm_scale * q.k_j) v_j     (over visible keys)
  *   lse[b,h,i]  = log sum_j exp(sm_scale * q.k_j)
@@ -198,7 +201,7 @@ H2O_API h2o_status_t h2o_select_slots(const h2o_dims_t *dims, const h2o_cache_t 
 
 /*
  * h2o_buffer_attn: the chunk attention of h2o_chunk_attn (same arguments,
- * layouts, precision and precondition) over the buffer as it stands once the
+ * layouts, precision and positional mask) over the buffer as it stands once the
  * chunk is written into freed_slots (the output of h2o_select_slots for this
  * cache, P and S): the targets below n_valid are not keys.  Equivalently, a
  * slot j of the buffer with position t(j) is visible to row i iff
@@ -276,6 +279,29 @@ H2O_API h2o_status_t h2o_chunk_attn_backward(const h2o_dims_t *dims, const h2o_c
                                      const int32_t *freed_slots, float *dq, float *dk_new,
                                      float *dv_new, float *dk_cache, float *dv_cache,
                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * h2o_chunk_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus the workspace),
+ * results, layouts, precision and errors as h2o_chunk_attn, from the same
+ * kernels, so the outputs are bit-identical.  The workspace comes from a
+ * static device array of the library, h2o_noalloc_scratch_bytes() bytes
+ * (40 MiB) on each GPU, held until the process ends; its address on a device
+ * is looked up once, at the first call on that device.  A call whose
+ * workspace (h2o_workspace_bytes for a bf16 chunk with summed weights or a
+ * decode step; none otherwise) exceeds it returns H2O_ERR_WORKSPACE before
+ * anything is launched.  Calls no allocating routine.  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind (nothing in it must
+ * start at zero): calls that overlap on one GPU (different streams, or host
+ * threads without ordering) race on it and must be serialised by the caller.
+ */
+H2O_API size_t h2o_noalloc_scratch_bytes(void);
+H2O_API h2o_status_t h2o_chunk_attn_noalloc(const h2o_dims_t *dims, const h2o_cache_t *cache,
+                                    int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                                    const void *q, const void *k_new, const void *v_new,
+                                    void *out, float *lse, float *colsum_cache,
+                                    float *colsum_new, void *stream);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 H2O_API const char *h2o_last_error(void);

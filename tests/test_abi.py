@@ -238,3 +238,33 @@ def test_python_binding_checks_shapes_before_calling():
     with pytest.raises(ValueError):
         h2o._need(q.float(), (1, 4, 64, 64), torch.bfloat16, "q")
     assert d.group == 2
+
+
+def test_noalloc_scratch_size():
+    assert h2o.lib.h2o_noalloc_scratch_bytes() == 40 << 20
+
+
+def _noalloc(dims, S, n_valid=0, cs=FAKE):
+    cache = _native.CacheStruct(FAKE, FAKE, FAKE, FAKE, n_valid)
+    return h2o.lib.h2o_chunk_attn_noalloc(ctypes.byref(dims), ctypes.byref(cache), 16384, S,
+                                          0.125, FAKE, FAKE, FAKE, FAKE, FAKE, cs, cs, None)
+
+
+def test_noalloc_rejects_workspace_beyond_scratch():
+    """A decode step of 32 sequences x 8 KV heads x 4 query heads over 16384 slots needs
+    67 MB of logits and partials, more than the 40 MiB scratch: refused before any GPU
+    call (the pointers here are fake)."""
+    dims = _dims(batch=32, n_q_heads=32, n_kv_heads=8, head_dim=128, capacity=16384)
+    need = h2o.lib.h2o_workspace_bytes(ctypes.byref(dims), 1)
+    assert need > h2o.lib.h2o_noalloc_scratch_bytes()
+    assert _noalloc(dims, 1, n_valid=16384) == _native.H2O_ERR_WORKSPACE
+    assert "scratch" in h2o.lib.h2o_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=4, n_kv_heads=3), _native.H2O_ERR_INVALID_ARG),
+    (dict(head_dim=96), _native.H2O_ERR_UNSUPPORTED),
+])
+def test_noalloc_validates_like_chunk_attn(kw, status):
+    assert _noalloc(_dims(**kw), 64) == status
+
