@@ -224,6 +224,48 @@ def update_evict_and_insert(cache: H2OCache, chunk_start: int, colsum_cache, k_n
     return freed_slots
 
 
+def chunk_step(cache: H2OCache, chunk_start: int, q, k_new, v_new, sm_scale: float,
+               score_mode="h2o", out=None, lse=None, colsum_cache=None, colsum_new=None,
+               freed_slots=None, workspace=None, stream=None):
+    """h2o_chunk_step: the whole chunk (attention with summed weights, score update,
+    eviction, insertion); returns (out, lse, colsum_cache, colsum_new, freed_slots) and
+    advances cache.n_valid / cache.next_pos."""
+    d = cache.dims
+    B, Hq, Hkv, D, NC = d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim, d.capacity
+    S = q.shape[2]
+    dev = cache.k.device
+    _need(q, (B, Hq, S, D), d.torch_dtype, "q")
+    _need(k_new, (B, Hkv, S, D), d.torch_dtype, "k_new")
+    _need(v_new, (B, Hkv, S, D), d.torch_dtype, "v_new")
+    out = torch.empty(B, Hq, S, D, dtype=d.torch_dtype, device=dev) if out is None else out
+    lse = torch.empty(B, Hq, S, dtype=torch.float32, device=dev) if lse is None else lse
+    if colsum_cache is None:
+        colsum_cache = torch.empty(B, Hkv, NC, dtype=torch.float32, device=dev)
+    if colsum_new is None:
+        colsum_new = torch.empty(B, Hkv, S, dtype=torch.float32, device=dev)
+    if freed_slots is None:
+        freed_slots = torch.empty(B, Hkv, S, dtype=torch.int32, device=dev)
+    _need(out, (B, Hq, S, D), d.torch_dtype, "out")
+    _need(lse, (B, Hq, S), torch.float32, "lse")
+    _need(colsum_cache, (B, Hkv, NC), torch.float32, "colsum_cache")
+    _need(colsum_new, (B, Hkv, S), torch.float32, "colsum_new")
+    _need(freed_slots, (B, Hkv, S), torch.int32, "freed_slots")
+    ws_need = workspace_bytes(d, S)
+    if ws_need and workspace is None:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    cs = cache.c()
+    check(lib.h2o_chunk_step(ctypes.byref(d.c()), ctypes.byref(cs), int(chunk_start), S,
+                             float(sm_scale), SCORE_MODES[score_mode], q.data_ptr(),
+                             k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                             colsum_cache.data_ptr(), colsum_new.data_ptr(),
+                             freed_slots.data_ptr(), ws_ptr, ws_len, _stream_ptr(stream, dev)))
+    cache.n_valid = cs.n_valid
+    cache.next_pos = int(chunk_start) + S
+    return out, lse, colsum_cache, colsum_new, freed_slots
+
+
 def select_slots(cache: H2OCache, chunk_start: int, chunk_len: int, freed_slots=None,
                  score_mode="h2o", stream=None):
     """h2o_select_slots: the chunk's targets [B,Hkv,S] from the current scores; the cache
@@ -366,8 +408,9 @@ def evict_and_insert_lastrec(cache: H2OCache, chunk_start: int, k_new, v_new, si
 
 def step(cache: H2OCache, q, k_new, v_new, sm_scale: float, score_mode="h2o", bufs=None,
          stream=None, policy="h2o", sink_tokens=0):
-    """One chunk at position cache.next_pos.  policy "h2o": attention with summed weights,
-    score update, eviction by ``score_mode``.  policy "h2o_buffer": the insert-first buffer
+    """One chunk at position cache.next_pos.  policy "h2o": one h2o_chunk_step call
+    (attention with summed weights, score update, eviction by ``score_mode``, insertion).
+    policy "h2o_buffer": the insert-first buffer
     form (targets from the scores before the chunk, attention over the buffer, score
     update, insertion).  policy "lastrec": attention alone, then eviction by position
     keeping the first ``sink_tokens``.  ``bufs`` (a dict holding out, lse, colsum_cache,
@@ -394,11 +437,10 @@ def step(cache: H2OCache, q, k_new, v_new, sm_scale: float, score_mode="h2o", bu
         return {"out": out, "lse": lse, "freed_slots": freed}
     if policy != "h2o":
         raise ValueError(f"unknown policy {policy!r}")
-    out, lse, cs_cache, cs_new = chunk_attn(cache, P, q, k_new, v_new, sm_scale,
-                                            b.get("out"), b.get("lse"), b.get("colsum_cache"),
-                                            b.get("colsum_new"), b.get("workspace"), stream)
-    freed = update_evict_and_insert(cache, P, cs_cache, k_new, v_new, cs_new,
-                                    b.get("freed_slots"), score_mode, stream)
+    out, lse, cs_cache, cs_new, freed = chunk_step(
+        cache, P, q, k_new, v_new, sm_scale, score_mode, b.get("out"), b.get("lse"),
+        b.get("colsum_cache"), b.get("colsum_new"), b.get("freed_slots"), b.get("workspace"),
+        stream)
     return {"out": out, "lse": lse, "colsum_cache": cs_cache, "colsum_new": cs_new,
             "freed_slots": freed}
 

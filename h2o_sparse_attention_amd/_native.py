@@ -56,6 +56,9 @@ _SIGNATURES = {
     "h2o_evict_and_insert_lastrec": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64,
                                                c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                                c_void_p]),
+    "h2o_chunk_step": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32, c_float,
+                                 c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "h2o_select_slots": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32,
                                    c_int32, c_void_p, c_void_p]),
     "h2o_buffer_attn": (c_int32, [POINTER(Dims), POINTER(CacheStruct), c_int64, c_int32, c_float,

@@ -139,6 +139,20 @@ size_t excl_bytes(const h2o_dims_t* dims) {
     return (size_t)dims->batch * dims->n_kv_heads * excl_tiles(dims->capacity) * sizeof(uint64_t);
 }
 
+// H2O_ERR_CAPACITY when k = n + S - N_C > 0 slots must go and the chunk plus the
+// protected slots (recent window, or lastrec's sink) exceed the capacity.
+h2o_status_t check_capacity(const h2o_dims_t* dims, const h2o_cache_t* cache, int32_t S,
+                            int mode, int sink) {
+    const int n = cache->n_valid, NC = dims->capacity;
+    const int k = n + S - NC;
+    const bool lastrec = mode == kModeLastrec;
+    const long long guard = lastrec ? sink : dims->recent_window;
+    if (k > 0 && (long long)S + guard > NC)
+        return fail(H2O_ERR_CAPACITY, "cannot evict %d slots: capacity %d < chunk_len %d + %s %lld",
+                    k, NC, S, lastrec ? "sink_tokens" : "recent_window", guard);
+    return H2O_OK;
+}
+
 // Shared body of the eviction entry points.  mode: h2o_score_mode_t, or
 // kModeLastrec with `sink` protected leading positions; colsum_new NULL gives
 // inserted slots score 0.  do_select / do_insert: run the selection (targets
@@ -154,13 +168,9 @@ h2o_status_t evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* cache, int64_
     if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
     if ((do_insert && (!k_new || !v_new)) || !freed_slots)
         return fail(H2O_ERR_INVALID_ARG, "k_new, v_new and freed_slots must be non-NULL");
+    if ((st = check_capacity(dims, cache, chunk_len, mode, sink)) != H2O_OK) return st;
     const int n = cache->n_valid, S = chunk_len, NC = dims->capacity;
     const int k = n + S - NC;
-    const bool lastrec = mode == kModeLastrec;
-    const long long guard = lastrec ? sink : dims->recent_window;
-    if (k > 0 && (long long)S + guard > NC)
-        return fail(H2O_ERR_CAPACITY, "cannot evict %d slots: capacity %d < chunk_len %d + %s %lld",
-                    k, NC, S, lastrec ? "sink_tokens" : "recent_window", guard);
     EvictArgs a;
     a.kc = cache->k;
     a.vc = cache->v;
@@ -260,7 +270,7 @@ h2o_status_t chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache, int64_
                         int32_t chunk_len, float sm_scale, const void* q, const void* k_new,
                         const void* v_new, const int32_t* freed, void* out, float* lse,
                         float* colsum_cache, float* colsum_new, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, const EvictArgs* ev) {
     h2o_status_t st;
 
     if ((st = validate_dims(dims)) != H2O_OK) return st;
@@ -332,7 +342,7 @@ h2o_status_t chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache, int64_
             return st;
     }
     if (decode) {
-        hipError_t e = launch_decode(a, workspace, s);     // times its two kernels
+        hipError_t e = launch_decode(a, workspace, s, ev);  // times its two kernels
         if ((st = check_hip(e, "decode attention launch")) != H2O_OK) return st;
         return ok();
     }
@@ -503,6 +513,63 @@ h2o_status_t h2o_update_evict_and_insert(const h2o_dims_t* dims, h2o_cache_t* ca
     if (!colsum_new) return fail(H2O_ERR_INVALID_ARG, "colsum_new is NULL");
     if (score_mode != H2O_SCORE_H2O && score_mode != H2O_SCORE_H2O_NORM)
         return fail(H2O_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
+    return evict_and_insert(dims, cache, chunk_start, chunk_len, score_mode, 0, k_new, v_new,
+                            colsum_new, freed_slots, stream, true, true, colsum_cache);
+}
+
+h2o_status_t h2o_chunk_step(const h2o_dims_t* dims, h2o_cache_t* cache, int64_t chunk_start,
+                            int32_t chunk_len, float sm_scale, int32_t score_mode,
+                            const void* q, const void* k_new, const void* v_new, void* out,
+                            float* lse, float* colsum_cache, float* colsum_new,
+                            int32_t* freed_slots, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    h2o_status_t st;
+    if (score_mode != H2O_SCORE_H2O && score_mode != H2O_SCORE_H2O_NORM)
+        return fail(H2O_ERR_INVALID_ARG, "unknown score_mode %d", score_mode);
+    if (!colsum_cache || !colsum_new)
+        return fail(H2O_ERR_INVALID_ARG, "colsum_cache and colsum_new must be non-NULL");
+    if (!freed_slots) return fail(H2O_ERR_INVALID_ARG, "freed_slots is NULL");
+    if ((st = validate_dims(dims)) != H2O_OK) return st;
+    if ((st = validate_cache(dims, cache)) != H2O_OK) return st;
+    if ((st = validate_chunk(chunk_start, chunk_len)) != H2O_OK) return st;
+    // Everything the eviction would refuse is refused before the attention launches.
+    if ((st = check_capacity(dims, cache, chunk_len, score_mode, 0)) != H2O_OK) return st;
+    const int n = cache->n_valid, NC = dims->capacity;
+    if (uses_decode(dims, chunk_len)) {
+        // S = 1: the update, selection and insertion run in the finishing kernel.
+        EvictArgs ev;
+        ev.kc = cache->k;
+        ev.vc = cache->v;
+        ev.pos = cache->pos;
+        ev.score = cache->score;
+        ev.kn = k_new;
+        ev.vn = v_new;
+        ev.cs_new = colsum_new;
+        ev.freed = freed_slots;
+        ev.B = dims->batch;
+        ev.Hkv = dims->n_kv_heads;
+        ev.D = dims->head_dim;
+        ev.S = 1;
+        ev.NC = NC;
+        ev.n = n;
+        ev.W = dims->recent_window;
+        ev.P = (int)chunk_start;
+        ev.elem_bytes = 2;
+        ev.score_mode = score_mode;
+        ev.sink = 0;
+        if ((st = chunk_attn(dims, cache, chunk_start, chunk_len, sm_scale, q, k_new, v_new,
+                             nullptr, out, lse, colsum_cache, colsum_new, workspace,
+                             workspace_bytes, stream, &ev)) != H2O_OK)
+            return st;
+        cache->n_valid = n + 1 < NC ? n + 1 : NC;
+        return ok();
+    }
+    if (!k_new || !v_new)
+        return fail(H2O_ERR_INVALID_ARG, "k_new, v_new and freed_slots must be non-NULL");
+    if ((st = chunk_attn(dims, cache, chunk_start, chunk_len, sm_scale, q, k_new, v_new, nullptr,
+                         out, lse, colsum_cache, colsum_new, workspace, workspace_bytes,
+                         stream)) != H2O_OK)
+        return st;
     return evict_and_insert(dims, cache, chunk_start, chunk_len, score_mode, 0, k_new, v_new,
                             colsum_new, freed_slots, stream, true, true, colsum_cache);
 }

@@ -17,6 +17,15 @@
 //      weights sum_{h in g} exp(s - LSE_h) per slot.
 //  When the caller asks for no summed weights, the logits are not stored and
 //  the finish kernel runs one workgroup per (b, kv head) for O and LSE only.
+//  For a whole step (h2o_chunk_step) the finish kernel also adds each slot's
+//  summed weight to its score, forms the eviction keys and reduces them to one
+//  (key, slot) minimum per workgroup; decode_insert_kernel (one wave per
+//  (b, kv head)) then takes the minimum of those, the victim, and writes the
+//  new token into it -- the score update, selection and insertion without a
+//  second pass over the scores.  (The hand-over between the two kernels is the
+//  kernel boundary: a device-scope fence per finishing workgroup, so that the
+//  last one could insert, writes back its XCD's L2 and measured 61 us against
+//  22 us for the separate launches.)
 //
 // P V uses ds_read_b64_tr_b16: a 16-lane group addresses four rows of four
 // consecutive bf16 (one key, four d each) and lane j receives column j%4 of
@@ -62,8 +71,10 @@ struct DecSmem {
 struct DecodeWs {
     float* logits;      // [B*Hkv][G][NCP]  log2-unit logits, -inf where masked
     float* partial;     // [B*Hkv][nsplit][G][D + 2]  (m, l, O unnormalised)
+    uint64_t* part_min; // [B*Hkv][nfin]  eviction: (key, slot) minimum per finish workgroup
     int nsplit;         // workgroups per (b, kv head) at full capacity
     int ncp;            // logit row length (capacity rounded up to kDecSub)
+    int nfin;           // finish workgroups per (b, kv head) at full capacity
 };
 
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -311,13 +322,17 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
 }
 
 // Merge the splits and the new token, write O / LSE (first workgroup of each
-// (b, g)), and form the summed weights of a range of slots.
-template <int D>
+// (b, g)), and form the summed weights of a range of slots.  EVICT: also the
+// score update, the eviction keys and this range's (key, slot) minimum (a full
+// cache: one victim), which decode_insert_kernel reduces.
+template <int D, bool EVICT>
 __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a, DecodeWs ws,
-                                                                    int nsplit_rt, int kchunks) {
+                                                                    int nsplit_rt, int kchunks,
+                                                                    EvictArgs ev) {
     __shared__ float sLse2[64];
     __shared__ float sNew[64];
     __shared__ float sM[64];
+    __shared__ uint64_t sBest[kDecWaves];
     const int bg = blockIdx.y, kc = blockIdx.x;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int G = a.G, n = a.n;
@@ -348,6 +363,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
 #pragma unroll
         for (int u = 0; u < U; ++u)
             vpre[hh][u] = (want_cs && hh < G) ? lload(hh, u) : float4{0.f, 0.f, 0.f, 0.f};
+    // EVICT: this range's scores and positions go out with the logits (zeros past n).
+    u32x4 sc4[U], ps4[U];
+    if constexpr (EVICT) {
+        const Rsrc rs = make_rsrc(ev.score + (size_t)bg * a.NC, n * 4);
+        const Rsrc rp = make_rsrc(ev.pos + (size_t)bg * a.NC, n * 4);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int off = (j0 + 4 * tid + 4 * kDecThreads * u) * 4;
+            sc4[u] = bload16(rs, off);
+            ps4[u] = bload16(rp, off);
+        }
+    }
 
     // The output merge's loads (workgroup kc == 0) go out now too, so that every
     // global read of this kernel is in flight at once: each thread's (head, d)
@@ -493,16 +520,122 @@ __global__ __launch_bounds__(kDecThreads) void decode_finish_kernel(ChunkArgs a,
                 if (j + e < j1) csr[j + e] = w[e];
         }
     }
+    if constexpr (EVICT) {
+        // Score update phi += summed weight (written back), and the eviction key of
+        // every filled slot: eligible iff t(j) < P - W; h2o-norm divides by the
+        // age t - t(j), t = P + 1.  Same operations as the separate update and
+        // selection, so the same bits.
+        const bool full = n == a.NC;                  // one victim (k = n + 1 - N_C)
+        const int thr = a.P - ev.W, t_now = a.P + 1;
+        float* scw = ev.score + (size_t)bg * a.NC;
+        uint64_t best = ~0ull;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + 4 * tid + 4 * kDecThreads * u;
+            const float c4[4] = {cs[u].x, cs[u].y, cs[u].z, cs[u].w};
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(sc4[u][e]) + c4[e];
+            if (vec && j + 3 < j1) {
+                *reinterpret_cast<float4*>(scw + j) = float4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e < j1) scw[j + e] = v[e];
+            }
+            if (full) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int pj = (int)ps4[u][e];
+                    float r = v[e];
+                    if (ev.score_mode == H2O_SCORE_H2O_NORM) r = r / (float)(t_now - pj);
+                    const uint32_t key = pj < thr ? order_key(r) : kIneligible;
+                    const uint64_t kv = ((uint64_t)key << 32) | (uint32_t)(j + e);
+                    if (j + e < j1 && kv < best) best = kv;
+                }
+            }
+        }
+        if (!full) return;                            // filling: the token goes to slot n
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t o = __shfl_xor(best, off);
+            best = o < best ? o : best;
+        }
+        if (lane == 0) sBest[wave] = best;
+        __syncthreads();
+        if (tid == 0) {
+            uint64_t m = sBest[0];
+#pragma unroll
+            for (int w = 1; w < kDecWaves; ++w) m = sBest[w] < m ? sBest[w] : m;
+            ws.part_min[(size_t)bg * ws.nfin + kc] = m;
+        }
+    }
+}
+
+// After decode_finish_kernel<EVICT>: one wave per (b, kv head) takes the
+// smallest (key, slot) of the finishing workgroups' minima (full cache) or slot
+// n (filling) and writes the new token there: K and V rows, t = P, score = the
+// token's own summed weight, freed_slots.  Same victim and contents as the
+// one-victim selection and insertion of h2o_update_evict_and_insert.
+__global__ __launch_bounds__(64) void decode_insert_kernel(ChunkArgs a, DecodeWs ws,
+                                                           int kchunks, EvictArgs ev) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const int bg = blockIdx.x, lane = threadIdx.x;
+    int slot = a.n;
+    if (a.n == a.NC) {
+        uint64_t m = lane < kchunks ? ws.part_min[(size_t)bg * ws.nfin + lane] : ~0ull;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t o = __shfl_xor(m, off);
+            m = o < m ? o : m;
+        }
+        slot = (int)(uint32_t)m;
+    }
+    const int units = a.D * 2 / 16;                   // 16-byte units of a bf16 row
+    if (lane < 2 * units) {
+        const bool is_v = lane >= units;
+        const int part = lane % units;
+        const u32x4_t* src = static_cast<const u32x4_t*>(is_v ? a.vn : a.kn) + (size_t)bg * units;
+        u32x4_t* dst = static_cast<u32x4_t*>(is_v ? ev.vc : ev.kc) +
+                       ((size_t)bg * a.NC + slot) * units;
+        dst[part] = src[part];
+    }
+    if (lane == 0) {
+        ev.freed[bg] = slot;
+        ev.pos[(size_t)bg * a.NC + slot] = a.P;
+        ev.score[(size_t)bg * a.NC + slot] = a.cs_new[bg];
+    }
+}
+
+// Workspace: logits, split partials, then (8-byte aligned) the finish
+// workgroups' minima and the arrival counters.
+struct WsSizes {
+    size_t logits, partial, part_min;
+};
+WsSizes ws_sizes(int B, int Hq, int Hkv, int NC) {
+    const int G = Hq / Hkv;
+    const size_t ncp = round_up(NC, kDecSub);
+    const size_t nsplit = (NC + kDecSplit - 1) / kDecSplit;
+    const size_t nfin = (NC + kFinishKeys - 1) / kFinishKeys;
+    const size_t D = 128;
+    WsSizes w;
+    w.logits = (size_t)B * Hkv * G * ncp * 4;
+    w.partial = (size_t)B * Hkv * nsplit * G * (D + 2) * 4;
+    w.part_min = (size_t)B * Hkv * nfin * 8;
+    return w;
 }
 
 DecodeWs ws_layout(void* base, int B, int Hq, int Hkv, int NC, int D) {
     DecodeWs w;
-    const int G = Hq / Hkv;
+    const WsSizes z = ws_sizes(B, Hq, Hkv, NC);
     w.ncp = round_up(NC, kDecSub);
     w.nsplit = (NC + kDecSplit - 1) / kDecSplit;
-    const size_t logits = (size_t)B * Hkv * G * w.ncp * 4;
-    w.logits = static_cast<float*>(base);
-    w.partial = reinterpret_cast<float*>(static_cast<char*>(base) + logits);
+    w.nfin = (NC + kFinishKeys - 1) / kFinishKeys;
+    char* p = static_cast<char*>(base);
+    w.logits = reinterpret_cast<float*>(p);
+    w.partial = reinterpret_cast<float*>(p + z.logits);
+    const size_t mins = (z.logits + z.partial + 7) / 8 * 8;
+    w.part_min = reinterpret_cast<uint64_t*>(p + mins);
     (void)D;
     return w;
 }
@@ -510,14 +643,12 @@ DecodeWs ws_layout(void* base, int B, int Hq, int Hkv, int NC, int D) {
 }  // namespace
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int NC) {
-    const int G = Hq / Hkv;
-    const size_t ncp = round_up(NC, kDecSub);
-    const size_t nsplit = (NC + kDecSplit - 1) / kDecSplit;
-    const size_t D = 128;
-    return (size_t)B * Hkv * G * ncp * 4 + (size_t)B * Hkv * nsplit * G * (D + 2) * 4;
+    const WsSizes z = ws_sizes(B, Hq, Hkv, NC);
+    return (z.logits + z.partial + 7) / 8 * 8 + z.part_min;
 }
 
-hipError_t launch_decode(const ChunkArgs& a, void* workspace, hipStream_t s) {
+hipError_t launch_decode(const ChunkArgs& a, void* workspace, hipStream_t s,
+                         const EvictArgs* ev) {
     if (a.D != 128) return hipErrorNotSupported;
     const DecodeWs ws = ws_layout(workspace, a.B, a.Hq, a.Hkv, a.NC, a.D);
     const int nsplit_rt = (a.n + kDecSplit - 1) / kDecSplit;
@@ -545,9 +676,19 @@ hipError_t launch_decode(const ChunkArgs& a, void* workspace, hipStream_t s) {
     // Without summed weights only the first workgroup of each (b, g) has work.
     const int kchunks = (a.n > 0 && a.cs_cache) ? (a.n + kFinishKeys - 1) / kFinishKeys : 1;
     timer_begin(H2O_KERNEL_DECODE_FINISH, s);
-    hipLaunchKernelGGL(decode_finish_kernel<128>, dim3(kchunks, a.B * a.Hkv), dim3(kDecThreads), 0,
-                       s, a, ws, nsplit_rt, kchunks);
+    if (ev != nullptr)
+        hipLaunchKernelGGL((decode_finish_kernel<128, true>), dim3(kchunks, a.B * a.Hkv),
+                           dim3(kDecThreads), 0, s, a, ws, nsplit_rt, kchunks, *ev);
+    else
+        hipLaunchKernelGGL((decode_finish_kernel<128, false>), dim3(kchunks, a.B * a.Hkv),
+                           dim3(kDecThreads), 0, s, a, ws, nsplit_rt, kchunks, EvictArgs{});
     timer_end(H2O_KERNEL_DECODE_FINISH, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || ev == nullptr) return e;
+    timer_begin(H2O_KERNEL_INSERT, s);
+    hipLaunchKernelGGL(decode_insert_kernel, dim3(a.B * a.Hkv), dim3(64), 0, s, a, ws, kchunks,
+                       *ev);
+    timer_end(H2O_KERNEL_INSERT, s);
     return hipGetLastError();
 }
 

@@ -84,6 +84,20 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
+// Eviction order keys: scores map to uint32 keys whose unsigned order is the
+// float order; slots that may not be evicted take the top two codes.
+constexpr uint32_t kIneligible = 0xFFFFFFFEu;   // filled slot inside the recent window
+constexpr uint32_t kAbsent = 0xFFFFFFFFu;       // slot >= n: never a victim
+constexpr uint32_t kMaxEligible = 0xFF800001u;  // just above +inf: NaN scores rank here
+
+// Monotone map float -> uint32 (a < b  =>  key(a) < key(b); -0 == +0).
+__device__ __forceinline__ uint32_t order_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return u < kMaxEligible ? u : kMaxEligible;
+}
+
 // A-operand row m of the QK^T product reads physical key perm_key(m).
 __device__ __forceinline__ int perm_key(int m) {
     return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);

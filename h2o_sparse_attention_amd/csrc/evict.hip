@@ -57,17 +57,9 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int pe
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kHistCopies = 4;
-constexpr uint32_t kIneligible = 0xFFFFFFFEu;   // filled slot inside the recent window
-constexpr uint32_t kAbsent = 0xFFFFFFFFu;       // slot >= n: never a victim
-constexpr uint32_t kMaxEligible = 0xFF800001u;  // just above +inf: NaN scores rank here
-
-// Monotone map float -> uint32 (a < b  =>  key(a) < key(b); -0 == +0).
-__device__ __forceinline__ uint32_t order_key(float v) {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return u < kMaxEligible ? u : kMaxEligible;
-}
+using dev::kIneligible;
+using dev::kAbsent;
+using dev::order_key;
 
 __device__ __forceinline__ int wave_count(bool pred) {
     return __popcll(__ballot(pred));

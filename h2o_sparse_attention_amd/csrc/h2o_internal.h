@@ -84,7 +84,11 @@ hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void*
 
 // Decode (S = 1) specialisation.
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int NC);
-hipError_t launch_decode(const ChunkArgs& a, void* ws, hipStream_t s);
+// ev != NULL (summed weights required): the finishing kernel also updates the
+// scores with the summed weights, selects the victim (full cache) and inserts
+// the new token -- h2o_update_evict_and_insert for S = 1 inside the same launch.
+hipError_t launch_decode(const ChunkArgs& a, void* ws, hipStream_t s,
+                         const EvictArgs* ev = nullptr);
 
 // Kernel timers (api.hip): bracket a launch with events when enabled.
 void timer_begin(int kernel, hipStream_t s);
@@ -98,7 +102,7 @@ h2o_status_t chunk_attn(const h2o_dims_t* dims, const h2o_cache_t* cache, int64_
                         int32_t chunk_len, float sm_scale, const void* q, const void* k_new,
                         const void* v_new, const int32_t* freed, void* out, float* lse,
                         float* colsum_cache, float* colsum_new, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        size_t workspace_bytes, void* stream, const EvictArgs* ev = nullptr);
 // Workspace bytes chunk_attn needs for this call (0: none, or invalid dims).
 size_t chunk_attn_workspace_need(const h2o_dims_t* dims, int32_t chunk_len, bool summed_weights,
                                  bool buffer_form);

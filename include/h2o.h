@@ -182,6 +182,29 @@ H2O_API h2o_status_t h2o_update_evict_and_insert(const h2o_dims_t *dims, h2o_cac
                                          void *stream);
 
 /*
+ * One whole chunk step: h2o_chunk_attn followed by h2o_update_evict_and_insert,
+ * with the same results bit for bit ("Kernel Support Needs": attention that
+ * returns the summed weights; "Improvements to H2O", item 2: accumulate them
+ * into the scores, then overwrite the slots of smallest score).  Arguments are
+ * those of the two calls: colsum_cache and colsum_new (required) receive the
+ * summed weights as from h2o_chunk_attn; the workspace is h2o_chunk_attn's
+ * (h2o_workspace_bytes); score_mode, freed_slots, the cache update and the
+ * advance of cache->n_valid are h2o_update_evict_and_insert's.  Every error of
+ * either call (H2O_ERR_CAPACITY included) is returned before anything is
+ * launched.  For S = 1 on the split decode path (bf16, d = 128) the score update,
+ * the selection of the one victim and the insertion of the token run inside the
+ * kernel that forms the summed weights, which already visits every slot: one
+ * pass over the scores instead of two, and two launches per step instead of
+ * three.
+ */
+H2O_API h2o_status_t h2o_chunk_step(const h2o_dims_t *dims, h2o_cache_t *cache,
+                            int64_t chunk_start, int32_t chunk_len, float sm_scale,
+                            int32_t score_mode, const void *q, const void *k_new,
+                            const void *v_new, void *out, float *lse, float *colsum_cache,
+                            float *colsum_new, int32_t *freed_slots, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
  * Insert-first buffer form ("Kernel Support Needs": attention over the fixed
  * N_C-slot buffer under the positional mask -inf * 1[P+i < t(b,h,j)]).  The
  * victims are chosen on the scores before the chunk and the chunk is written

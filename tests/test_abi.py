@@ -268,3 +268,21 @@ def test_noalloc_rejects_workspace_beyond_scratch():
 def test_noalloc_validates_like_chunk_attn(kw, status):
     assert _noalloc(_dims(**kw), 64) == status
 
+
+def _step(dims, n_valid=0, S=64, P=0, mode=_native.H2O_SCORE_H2O, cs=FAKE, freed=FAKE):
+    cache = _native.CacheStruct(FAKE, FAKE, FAKE, FAKE, n_valid)
+    return h2o.lib.h2o_chunk_step(ctypes.byref(dims), ctypes.byref(cache), P, S, 0.125, mode,
+                                  FAKE, FAKE, FAKE, FAKE, FAKE, cs, cs, freed, None, 0, None)
+
+
+@pytest.mark.parametrize("call,status", [
+    (dict(mode=7), _native.H2O_ERR_INVALID_ARG),
+    (dict(cs=None), _native.H2O_ERR_INVALID_ARG),
+    (dict(freed=None), _native.H2O_ERR_INVALID_ARG),
+    (dict(n_valid=257), _native.H2O_ERR_INVALID_ARG),
+    # full cache, chunk 240 + window 32 > 256 slots: refused before the attention launches
+    (dict(n_valid=256, S=240, P=1000), _native.H2O_ERR_CAPACITY),
+])
+def test_chunk_step_rejects_before_launch(call, status):
+    assert _step(_dims(), **call) == status
+    assert h2o.lib.h2o_last_error().decode()
