@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "H2O chunk-attn+score+evict TFLOP/s & tokens/s (chunk 1k, 64k ctx), % roofline"
+METRIC_CHUNK2K = "H2O chunk-attn+score+evict TFLOP/s & tokens/s (chunk 2k, 128k ctx), % roofline"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_chunk1k_ctx64k_traffic.txt")
@@ -76,13 +77,7 @@ def cpu_baseline(wl, budget_s: float):
     """The fp64 oracle on steady (full-cache) chunks of the same workload."""
     import oracle
     import workloads as W
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"),
-                      default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     c = 16
     s = W.steady_state(wl, 0, start=c * wl.chunk, seed=0)
     x = W.chunk_inputs(wl, 0, c)
@@ -263,6 +258,43 @@ def measured_peaks():
             "read_1gib_gbs": round(read, 1)}
 
 
+def blas_threads() -> int:
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        return max((i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"),
+                   default=1)
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def decode_cpu_baseline(wl, st0, budget_s: float, max_steps: int = 8):
+    """The fp64 oracle on the first decode steps of the workload (at most max_steps,
+    or fewer if budget_s runs out), from the same initial cache; per-step time
+    extrapolated linearly to the whole run."""
+    import oracle
+    import workloads as W
+    st = oracle.H2OState.from_arrays(st0["k"], st0["v"], st0["pos"], st0["phi"], st0["n"],
+                                     st0["start"])
+    t0 = time.perf_counter()
+    steps = 0
+    while steps < max_steps:
+        x = W.decode_step_inputs(wl, steps)
+        oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window)
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_step = dt / steps
+    return {"value": round(wl.batch * steps / dt, 2), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{steps} decode step(s) of {wl.name} ({wl.batch} sequences x "
+                      f"{wl.n_kv_heads} KV heads x {wl.capacity} slots, fp64 NumPy), "
+                      f"{dt:.1f} s; linear extrapolation to the {wl.seq_len}-step run: "
+                      f"{per_step * wl.seq_len:.0f} s",
+            "us_per_decode_step": round(per_step * 1e6, 1)}
+
+
 def run_decode(args):
     import torch
 
@@ -278,6 +310,7 @@ def run_decode(args):
     st = W.decode_initial_state(wl)
     snap = {k: torch.from_numpy(st[k]).to(dev, dt if k in ("k", "v") else None)
             for k in ("k", "v", "pos", "phi")}
+    st_host = st if (args.cpu_budget > 0 and args.policy == "h2o") else None
     del st
     steps_in = []
     for t in range(wl.seq_len):
@@ -354,6 +387,10 @@ def run_decode(args):
     kv_bytes = B * Hkv * NC * 2 * D * 2            # K and V rows read by the attention launch
     achieved = kv_bytes / (dec.mean_ms * 1e-3) / 1e9
     peaks = measured_peaks()
+    cpu = None
+    if st_host is not None:
+        print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
+        cpu = decode_cpu_baseline(wl, st_host, args.cpu_budget)
     line = {
         "metric": {"h2o": DECODE_METRIC, "h2o_buffer": BUFFER_DECODE_METRIC,
                    "lastrec": LASTREC_DECODE_METRIC}[args.policy],
@@ -378,7 +415,7 @@ def run_decode(args):
                      "kernel": "decode_attn_kernel<128>", "launches": dec.launches,
                      "mean_launch_us": round(dec.mean_ms * 1e3, 2)},
         "measured_peaks": peaks,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -436,6 +473,25 @@ def run_backward(args):
     pairs = pairs_per_head(NC, S)
     flops = 10.0 * D * Hq * B * pairs         # QK^T recompute, dP, dQ, dK, dV
     ms = elapsed / args.steps * 1e3
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
+        st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+        dout_h = dout.float().cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.attend_chunk_backward(st, x["q"], x["k"], x["v"], dout_h, wl.sm_scale)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_budget:
+                break
+        dtc = time.perf_counter() - t0
+        cpu = {"value": round(flops * reps / dtc / 1e12, 4), "unit": "TFLOP/s",
+               "cores": blas_threads(), "kind": "oracle",
+               "sample": f"{reps} steady chunk backward(s) of {wl.name} ({NC}+{S} keys, "
+                         f"fp64 NumPy), {dtc:.1f} s",
+               "ms_per_chunk": round(dtc / reps * 1e3, 1)}
     tflops = flops / (ms * 1e-3) / 1e12
     achieved = flops / (timer.mean_ms * 1e-3) / 1e12
     line = {
@@ -451,7 +507,7 @@ def run_backward(args):
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel": "h2o_chunk_attn_backward (row-dot, dQ, dK/dV)",
                      "launches": timer.launches, "mean_launch_us": round(timer.mean_ms * 1e3, 2)},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -727,7 +783,8 @@ def main():
     attn_flops_per_launch = f4 / wl.n_chunks          # QK^T + PV, averaged over the chunks
     attn_ms = attn.mean_ms
     achieved = attn_flops_per_launch / (attn_ms * 1e-3) / 1e12
-    traffic = read_traffic(TRAFFIC_FILE)
+    # counters were taken on the headline h2o sequence only
+    traffic = read_traffic(TRAFFIC_FILE) if (wl.key == 2 and args.policy == "h2o") else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": "attn_bf16_kernel<128>",
@@ -754,8 +811,9 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_budget)
 
     line = {
-        "metric": LASTREC_METRIC if lastrec else (BUFFER_METRIC if args.policy == "h2o_buffer"
-                                                  else METRIC), "value": round(tflops, 3),
+        "metric": LASTREC_METRIC if lastrec else (
+            BUFFER_METRIC if args.policy == "h2o_buffer" else
+            (METRIC_CHUNK2K if wl.chunk == 2048 else METRIC)), "value": round(tflops, 3),
         "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
