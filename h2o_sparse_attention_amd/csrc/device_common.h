@@ -54,8 +54,9 @@ __device__ __forceinline__ u32x4 bload16(Rsrc r, int voff) {
 __device__ __forceinline__ uint32_t bload4(Rsrc r, int voff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
 }
-// Streaming loads of data read exactly once: cache policy SC1 (device scope),
-// which skips the CU's vector L1 and sustains more bandwidth for long streams.
+// Streaming loads of data read exactly once: cache-policy operand 2, the `nt`
+// (non-temporal) bit on gfx950 (1 is sc0, 16 is sc1).  For the decode cache
+// stream it measured faster than the default policy, sc1 or nt sc1.
 constexpr int kStreamPolicy = 2;
 __device__ __forceinline__ uint32_t bload4_stream(Rsrc r, int voff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, kStreamPolicy);
