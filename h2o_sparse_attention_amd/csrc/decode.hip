@@ -321,6 +321,323 @@ void decode_attn_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
     }
 }
 
+// decode_attn_kernel for groups of at most four query heads, built on the
+// 4x4x4 MFMA (16 blocks of 4 x 4 x 4 per instruction).  Its products put one
+// slot in each lane: S = Q K^T with the heads as the four rows and the 32
+// slots of a sub-tile as the block columns (lanes 32..63 take the upper half
+// of d; one v_permlane32_swap adds the halves and leaves lane l holding heads
+// 2*(l/32) and 2*(l/32)+1 of slot l%32), and O = P V with the heads as rows
+// and 64 d columns per instruction.  O takes 8 registers instead of 64, so a
+// wave can keep the logits of all its sub-tiles in 64 registers and write
+// them in one burst once its loads are done: logit stores mixed into the
+// cache read stream slow that stream far more than their 3% of the bytes.
+constexpr int kDec4MaxSub = kDecSplit / (kDecSub * kDecWaves);   // sub-tiles per wave
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct Dec4Smem {
+    static constexpr int RB = 2 * D;                  // bytes per K / V row
+    static constexpr int K_BYTES = kDecSub * RB;
+    static constexpr int V_BYTES = kDecSub * RB;
+    static constexpr int P_BYTES = 4 * kDecSub * 2;   // P tile [4 heads][32 slots] bf16
+    static constexpr int WAVE_BYTES = K_BYTES + V_BYTES + P_BYTES;
+    // Q rows padded by 16 bytes: the four heads' reads of one instruction fall
+    // in different banks.
+    static constexpr int QROWB = 2 * D + 16;
+    static constexpr int Q_BYTES = 4 * QROWB;
+    static constexpr int MERGE_FLOATS = 8 + (D / 64) * 4 * 64;   // m[4], l[4], O
+    static constexpr int MERGE_BYTES = kDecWaves * MERGE_FLOATS * 4;
+    static constexpr int TILE_BYTES = kDecWaves * WAVE_BYTES + Q_BYTES;
+    static constexpr int BYTES = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
+};
+
+template <int D, bool HOLD>
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
+    using L = Dec4Smem<D>;
+    constexpr int RB = L::RB;
+    constexpr int CH = D / 8;                              // 16-byte chunks per row
+    constexpr int LD = kDecSub * CH / 64;                  // 16-byte loads per lane
+    constexpr int KH = D / 8;                              // QK^T k-steps over half of d
+    constexpr int NO = D / 64;                             // PV products per 4 slots
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+    const int total = nsplit_rt * a.B * a.Hkv;
+    const int t = xcd_tile(blockIdx.x, total);
+    if (t >= total) return;
+    const int bg = t / nsplit_rt, split = t % nsplit_rt;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int G = a.G, n = a.n, NC = a.NC;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int key = lane & 31, hi = lane >> 5;    // slot within a sub-tile; d half / head pair
+
+    // The group's Q rows (zero rows for heads >= G).
+    unsigned char* sQ = smem + kDecWaves * L::WAVE_BYTES;
+    const u16* Q = static_cast<const u16*>(a.q);
+    for (int idx = tid; idx < 4 * CH; idx += kDecThreads) {
+        const int h = idx / CH, ch = idx % CH;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < G) v = ld16(Q + (size_t)(b * a.Hq + g * G + h) * D + ch * 8);
+        *reinterpret_cast<u32x4*>(sQ + h * L::QROWB + 16 * ch) = v;
+    }
+    __syncthreads();
+
+    unsigned char* wbase = smem + wave * L::WAVE_BYTES;
+    unsigned char* sK = wbase;
+    unsigned char* sV = wbase + L::K_BYTES;
+    unsigned char* sP = wbase + L::K_BYTES + L::V_BYTES;
+
+    const u16* Kc = static_cast<const u16*>(a.kc) + (size_t)bg * NC * D;
+    const u16* Vc = static_cast<const u16*>(a.vc) + (size_t)bg * NC * D;
+    const int32_t* posg = a.pos + (size_t)bg * NC;
+    const int victim = a.freed != nullptr ? a.freed[bg] : -1;   // S = 1: one target
+    const int k_begin = split * kDecSplit;
+    const int k_end = min(n, k_begin + kDecSplit);
+    const int nsub = (k_end - k_begin + kDecSub - 1) / kDecSub;
+
+    // Staging: load `it` covers rows it*(64/CH) + lane/CH, 16-byte chunk lane%CH;
+    // every lane also loads the position of its own slot.
+    constexpr int RPL = 64 / CH;
+    const int row0 = lane / CH, cg = lane % CH;
+    const int goff0 = (row0 * D + cg * 8) * 2;
+    u32x4 kreg[LD], vreg[LD];
+    int pnext = 0, pcur = INT_MAX;
+    bool pvalid = false;
+    auto gload = [&](int sub) {
+        const int k0 = k_begin + sub * kDecSub;
+        // Scalar on purpose: compared with the lane's slot below, it would
+        // otherwise sit in a vector register and the buffer descriptors built
+        // from it would need waterfall loops.
+        const int valid = __builtin_amdgcn_readfirstlane(min(kDecSub, k_end - k0));
+        const Rsrc rk = make_rsrc(Kc + (size_t)k0 * D, valid * D * 2);
+        const Rsrc rv = make_rsrc(Vc + (size_t)k0 * D, valid * D * 2);
+#pragma unroll
+        for (int it = 0; it < LD; ++it) {
+            kreg[it] = bload16_stream(rk, goff0 + it * RPL * D * 2);
+            vreg[it] = bload16_stream(rv, goff0 + it * RPL * D * 2);
+        }
+        const Rsrc rp = make_rsrc(posg + k0, valid * 4);
+        pnext = (int)bload4(rp, key * 4);
+        pvalid = key < valid;
+        if (k0 + key == victim) pnext = -1;       // buffer form: the slot being overwritten
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int it = 0; it < LD; ++it) {
+            const int r = row0 + it * RPL;
+            *reinterpret_cast<u32x4*>(sK + r * RB + 16 * (cg ^ swz_k<D>(r))) = kreg[it];
+            *reinterpret_cast<u32x4*>(sV + r * RB + 16 * (cg ^ swz_v<D>(r))) = vreg[it];
+        }
+        pcur = pvalid ? pnext : INT_MAX;
+    };
+
+    // Operand addresses.  K^T (B of S): row `key`, d = hi*D/2 + 4*step, i.e.
+    // 16-byte chunk hi*D/16 + step/2 (no carry into the half bit), half step%2.
+    const int krow = key * RB;
+    const int ksw = (hi * (D / 16)) ^ swz_k<D>(key);
+    // Q (A of S): head lane%4, same d.
+    const int qoff = (lane & 3) * L::QROWB + hi * D;
+    // V (B of O) through ds_read_b64_tr_b16: 16-lane group q4, lane j addresses
+    // slot 4*t4 + j/4, d 16*q4 + 4*(j%4) (+64 per product) and receives slots
+    // 4*t4 .. 4*t4+3 of d = lane (+64).
+    const int q4 = lane >> 4, j16 = lane & 15;
+    int voff[NO];
+#pragma unroll
+    for (int nn = 0; nn < NO; ++nn)
+        voff[nn] = (j16 >> 2) * RB +
+                   16 * ((2 * q4 + ((j16 & 3) >> 1) + 8 * nn) ^ swz_v<D>(j16 >> 2)) +
+                   8 * (j16 & 1);
+    // P (A of O): head lane%4, slots 4*t4 .. 4*t4+3.
+    const int poff = (lane & 3) * (2 * kDecSub);
+
+    const float c = a.sm_scale * kLog2e;
+    const float tau_raw = kRescaleLog2 / c;
+    const int qpos = a.P;
+    // Online-softmax state of this lane's two heads (2*hi, 2*hi+1): running max
+    // (the same in every lane of a half), this lane's share of the sum, and O
+    // (lane l, register r: head r, d = l + 64*nn) for all four heads.
+    float mA = -INFINITY, mB = -INFINITY, lA = 0.f, lB = 0.f;
+    f32x4 o[NO];
+#pragma unroll
+    for (int nn = 0; nn < NO; ++nn) o[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lg[HOLD ? 2 * kDec4MaxSub : 1];
+#pragma unroll
+    for (int i = 0; i < (HOLD ? 2 * kDec4MaxSub : 1); ++i) lg[i] = 0.f;
+
+    // Wave w owns sub-tiles w, w+4, ...; the LDS region is private to the wave,
+    // whose LDS operations complete in order, so no workgroup barrier is needed.
+    int sub = wave;
+    if (sub < nsub) {
+        gload(sub);
+        lstore();
+    }
+    for (; sub < nsub; sub += kDecWaves) {
+        const int next = sub + kDecWaves;
+        __builtin_amdgcn_s_setprio(1);
+        if (next < nsub) gload(next);
+        __builtin_amdgcn_s_setprio(0);
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KH; ++st) {
+            const s16x4 qa = *reinterpret_cast<const s16x4*>(sQ + qoff + 8 * st);
+            const s16x4 kb = *reinterpret_cast<const s16x4*>(
+                sK + krow + 16 * ((st >> 1) ^ ksw) + 8 * (st & 1));
+            if (st & 1) acc1 = mfma4(qa, kb, acc1);
+            else acc0 = mfma4(qa, kb, acc0);
+        }
+        const f32x4 sp = acc0 + acc1;
+        const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sp[0]),
+                                                          __float_as_uint(sp[2]), false, false);
+        const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sp[1]),
+                                                          __float_as_uint(sp[3]), false, false);
+        const bool vis = pcur >= 0 && pcur <= qpos;
+        const float sa = vis ? __uint_as_float(x02[0]) + __uint_as_float(x02[1]) : -INFINITY;
+        const float sb = vis ? __uint_as_float(x13[0]) + __uint_as_float(x13[1]) : -INFINITY;
+        if constexpr (HOLD) {
+#pragma unroll
+            for (int i = 0; i < 2 * kDec4MaxSub - 2; ++i) lg[i] = lg[i + 2];
+            lg[2 * kDec4MaxSub - 2] = sa * c;
+            lg[2 * kDec4MaxSub - 1] = sb * c;
+        }
+        if (__any(sa > mA + tau_raw || sb > mB + tau_raw)) {
+            float ta = sa, tb = sb;
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) {
+                ta = fmaxf(ta, __shfl_xor(ta, off));
+                tb = fmaxf(tb, __shfl_xor(tb, off));
+            }
+            const float nA = fmaxf(mA, ta), nB = fmaxf(mB, tb);
+            const float mA2 = nA > mA + tau_raw ? nA : mA;
+            const float mB2 = nB > mB + tau_raw ? nB : mB;
+            const float alA = mA2 == mA ? 1.f : fast_exp2((mA - mA2) * c);
+            const float alB = mB2 == mB ? 1.f : fast_exp2((mB - mB2) * c);
+            lA *= alA;
+            lB *= alB;
+            mA = mA2;
+            mB = mB2;
+            const float r0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alA), 0));
+            const float r1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alB), 0));
+            const float r2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alA), 32));
+            const float r3 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alB), 32));
+#pragma unroll
+            for (int nn = 0; nn < NO; ++nn) {
+                o[nn][0] *= r0;
+                o[nn][1] *= r1;
+                o[nn][2] *= r2;
+                o[nn][3] *= r3;
+            }
+        }
+        const float mcA = mA == -INFINITY ? 0.f : mA * c;
+        const float mcB = mB == -INFINITY ? 0.f : mB * c;
+        const float pa = fast_exp2(fmaf(sa, c, -mcA));
+        const float pb = fast_exp2(fmaf(sb, c, -mcB));
+        lA += pa;
+        lB += pb;
+        const uint32_t pp = pack2(pa, pb);
+        u16* sPh = reinterpret_cast<u16*>(sP);
+        sPh[(2 * hi) * kDecSub + key] = (u16)(pp & 0xFFFFu);
+        sPh[(2 * hi + 1) * kDecSub + key] = (u16)(pp >> 16);
+#pragma unroll
+        for (int t4 = 0; t4 < kDecSub / 4; ++t4) {
+            const s16x4 pa4 = *reinterpret_cast<const s16x4*>(sP + poff + 8 * t4);
+#pragma unroll
+            for (int nn = 0; nn < NO; ++nn) {
+                typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+                const s16x4 vb4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4*)(sV + voff[nn] + 4 * t4 * RB));
+                o[nn] = mfma4(pa4, vb4, o[nn]);
+            }
+        }
+        if (next < nsub) lstore();
+    }
+
+    // This wave's logits, oldest sub-tile first: sub-tile `it` sits in lg[2*j], j = it + 32 - niter.
+    if constexpr (HOLD) {
+        const int niter = nsub > wave ? (nsub - wave + kDecWaves - 1) / kDecWaves : 0;
+        float* rowA = ws.logits + ((size_t)bg * G + 2 * hi) * ws.ncp;
+        const bool wA = 2 * hi < G, wB = 2 * hi + 1 < G;
+#pragma unroll
+        for (int j = 0; j < kDec4MaxSub; ++j) {
+            const int it = niter - kDec4MaxSub + j;
+            if (it >= 0) {
+                const int k0 = k_begin + (wave + kDecWaves * it) * kDecSub;
+                if (wA) rowA[k0 + key] = lg[2 * j];
+                if (wB) rowA[ws.ncp + k0 + key] = lg[2 * j + 1];
+            }
+        }
+    }
+
+    // Sums over the 32 slots of each half; then the four waves' states merge.
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+        lA += __shfl_xor(lA, off);
+        lB += __shfl_xor(lB, off);
+    }
+    float mh[4], lh[4];
+    mh[0] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mA), 0));
+    mh[1] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mB), 0));
+    mh[2] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mA), 32));
+    mh[3] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mB), 32));
+    lh[0] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lA), 0));
+    lh[1] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lB), 0));
+    lh[2] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lA), 32));
+    lh[3] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lB), 32));
+    __syncthreads();
+    constexpr int MF = L::MERGE_FLOATS;
+    float* mb = reinterpret_cast<float*>(smem) + wave * MF;
+    if (wave != 0) {
+        if (lane < 4) {
+            mb[lane] = mh[lane];
+            mb[4 + lane] = lh[lane];
+        }
+#pragma unroll
+        for (int nn = 0; nn < NO; ++nn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mb[8 + (nn * 4 + r) * 64 + lane] = o[nn][r];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // Wave 0 folds the other waves' states into its own, in wave order.
+    const float* mall = reinterpret_cast<const float*>(smem);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float m = mh[r];
+#pragma unroll
+        for (int w = 1; w < kDecWaves; ++w) m = fmaxf(m, mall[w * MF + r]);
+        const float a0 = mh[r] == -INFINITY ? 0.f : fast_exp2((mh[r] - m) * c);
+        float l = lh[r] * a0;
+#pragma unroll
+        for (int nn = 0; nn < NO; ++nn) o[nn][r] *= a0;
+#pragma unroll
+        for (int w = 1; w < kDecWaves; ++w) {
+            const float mw = mall[w * MF + r];
+            const float aw = mw == -INFINITY ? 0.f : fast_exp2((mw - m) * c);
+            l += mall[w * MF + 4 + r] * aw;
+#pragma unroll
+            for (int nn = 0; nn < NO; ++nn) o[nn][r] += mall[w * MF + 8 + (nn * 4 + r) * 64 + lane] * aw;
+        }
+        mh[r] = m;
+        lh[r] = l;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (r >= G) break;
+        float* rec = ws.partial + (((size_t)bg * ws.nsplit + split) * G + r) * (D + 2);
+        if (lane == 0) {
+            rec[0] = mh[r] == -INFINITY ? -INFINITY : mh[r] * c;    // log2 units
+            rec[1] = lh[r];
+        }
+#pragma unroll
+        for (int nn = 0; nn < NO; ++nn) rec[2 + lane + 64 * nn] = o[nn][r];
+    }
+}
+
 // Merge the splits and the new token, write O / LSE (first workgroup of each
 // (b, g)), and form the summed weights of a range of slots.  EVICT: also the
 // score update, the eviction keys and this range's (key, slot) minimum (a full
@@ -662,13 +979,28 @@ hipError_t launch_decode(const ChunkArgs& a, void* workspace, hipStream_t s,
             e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<128>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
                                     DecSmem<128>::BYTES);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(
+                    reinterpret_cast<const void*>(&decode_attn4_kernel<128, true>),
+                    hipFuncAttributeMaxDynamicSharedMemorySize, Dec4Smem<128>::BYTES);
+            if (e == hipSuccess)
+                e = hipFuncSetAttribute(
+                    reinterpret_cast<const void*>(&decode_attn4_kernel<128, false>),
+                    hipFuncAttributeMaxDynamicSharedMemorySize, Dec4Smem<128>::BYTES);
             if (e != hipSuccess) return e;
             configured |= bit;
         }
         const int total = nsplit_rt * a.B * a.Hkv;
         timer_begin(H2O_KERNEL_DECODE, s);
-        hipLaunchKernelGGL(decode_attn_kernel<128>, dim3(xcd_grid(total)), dim3(kDecThreads),
-                           DecSmem<128>::BYTES, s, a, ws, nsplit_rt);
+        if (a.G > 4)
+            hipLaunchKernelGGL(decode_attn_kernel<128>, dim3(xcd_grid(total)), dim3(kDecThreads),
+                               DecSmem<128>::BYTES, s, a, ws, nsplit_rt);
+        else if (a.cs_cache != nullptr)
+            hipLaunchKernelGGL((decode_attn4_kernel<128, true>), dim3(xcd_grid(total)),
+                               dim3(kDecThreads), Dec4Smem<128>::BYTES, s, a, ws, nsplit_rt);
+        else
+            hipLaunchKernelGGL((decode_attn4_kernel<128, false>), dim3(xcd_grid(total)),
+                               dim3(kDecThreads), Dec4Smem<128>::BYTES, s, a, ws, nsplit_rt);
         timer_end(H2O_KERNEL_DECODE, s);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
