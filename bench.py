@@ -384,8 +384,14 @@ def run_decode(args):
     slot_bytes = decode_slot_bytes(wl, args.policy)
     step_bytes = B * Hkv * NC * slot_bytes
     dec = timers["decode"]
-    kv_bytes = B * Hkv * NC * 2 * D * 2            # K and V rows read by the attention launch
-    achieved = kv_bytes / (dec.mean_ms * 1e-3) / 1e9
+    # Algorithmic bytes per slot of the attention launch: K and V rows and the
+    # position read; with summed weights, their write; under h2o the score read and
+    # written as well (the score update and eviction keys are formed in this launch).
+    kern_slot_bytes = (2 * D * 2 + 4 + (0 if args.policy == "lastrec" else 4)
+                       + (8 if args.policy == "h2o" else 0))
+    achieved = B * Hkv * NC * kern_slot_bytes / (dec.mean_ms * 1e-3) / 1e9
+    kernel_name = {"h2o": "decode_attn4_kernel<128, 3>", "h2o_buffer": "decode_attn4_kernel<128, 2>",
+                   "lastrec": "decode_attn4_kernel<128, 0>"}[args.policy]
     peaks = measured_peaks()
     cpu = None
     if st_host is not None:
@@ -411,8 +417,10 @@ def run_decode(args):
         "kernel_mean_us": {k: round(t_.mean_ms * 1e3, 2) for k, t_ in timers.items()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": read_traffic(DECODE_TRAFFIC_FILE),
-                     "kernel": "decode_attn_kernel<128>", "launches": dec.launches,
+                     "traffic": (read_traffic(DECODE_TRAFFIC_FILE) if args.policy == "h2o"
+                                 else None),
+                     "kernel": kernel_name, "bytes_per_slot": kern_slot_bytes,
+                     "launches": dec.launches,
                      "mean_launch_us": round(dec.mean_ms * 1e3, 2)},
         "measured_peaks": peaks,
         "cpu_baseline": cpu,

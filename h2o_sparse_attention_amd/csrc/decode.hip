@@ -71,7 +71,8 @@ struct DecSmem {
 struct DecodeWs {
     float* logits;      // [B*Hkv][G][NCP]  log2-unit logits, -inf where masked
     float* partial;     // [B*Hkv][nsplit][G][D + 2]  (m, l, O unnormalised)
-    uint64_t* part_min; // [B*Hkv][nfin]  eviction: (key, slot) minimum per finish workgroup
+    uint64_t* part_min; // [B*Hkv][nfin]  eviction: (key, slot) minimum per finish workgroup (split)
+    uint64_t* xch;      // [B*Hkv][nsplit][4]  LSE exchange words of the fused kernel
     int nsplit;         // workgroups per (b, kv head) at full capacity
     int ncp;            // logit row length (capacity rounded up to kDecSub)
     int nfin;           // finish workgroups per (b, kv head) at full capacity
@@ -339,6 +340,53 @@ __device__ __forceinline__ f32x4 mfma4(s16x4 a, s16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// What decode_attn4_kernel does with the logits.
+enum Dec4Mode {
+    kDec4NoWeights = 0,   // no summed weights: the logits are not kept
+    kDec4Logits = 1,      // logits to the workspace; decode_finish_kernel forms the weights
+    kDec4Fused = 2,       // summed weights formed in the kernel (LSE exchange)
+    kDec4FusedEvict = 3,  // and the score update, eviction keys and per-split minimum
+};
+
+// LSE exchange between the workgroups (splits) of one (b, kv head): one 64-bit
+// word per (split, head), (m log2 units) << 32 | l, all ones while unwritten.
+constexpr uint64_t kXchEmpty = ~0ull;
+constexpr int kXchMaxSplits = 16;          // one lane per (split, head) in the polling wave
+// Bound on the polls of a missing word (a memory round trip and s_sleep 1
+// each, well under 0.2 s in all): the launch keeps every workgroup resident at
+// once, so the wait ends as soon as the siblings publish, within microseconds;
+// the bound only guarantees that the kernel ends otherwise.
+constexpr int kXchSpinLimit = 1 << 16;
+
+// The new token's logit q.k * c (log2 units) for one head, in one wave:
+// lane-strided products, then a butterfly sum.
+template <int D>
+__device__ __forceinline__ float new_token_logit2(const u16* q, const u16* k, float c, int lane) {
+    auto bf = [](u16 x) { return __uint_as_float((uint32_t)x << 16); };
+    float dot = 0.f;
+#pragma unroll
+    for (int d = lane; d < D; d += 64) dot = fmaf(bf(q[d]), bf(k[d]), dot);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+    return dot * c;
+}
+
+// One head's log-sum-exp (log2 units) over the split states (lane sp holds
+// split sp's (m, l), -inf / 0 beyond the splits) and the new token, in one
+// wave; m_out is the merged maximum.
+__device__ __forceinline__ float merge_lse2(float mrec, float lrec, float s_new, int lane,
+                                            float& m_out) {
+    float m = fmaxf(s_new, mrec);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float l = lane == 0 ? fast_exp2(s_new - m) : 0.f;
+    if (mrec != -INFINITY) l += lrec * fast_exp2(mrec - m);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+    m_out = m;
+    return m + log2f(l);
+}
+
 template <int D>
 struct Dec4Smem {
     static constexpr int RB = 2 * D;                  // bytes per K / V row
@@ -356,9 +404,10 @@ struct Dec4Smem {
     static constexpr int BYTES = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
 };
 
-template <int D, bool HOLD>
+template <int D, int MODE>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
+void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt, EvictArgs ev) {
+    constexpr bool HOLD = MODE != kDec4NoWeights;
     using L = Dec4Smem<D>;
     constexpr int RB = L::RB;
     constexpr int CH = D / 8;                              // 16-byte chunks per row
@@ -557,9 +606,10 @@ void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
         if (next < nsub) lstore();
     }
 
-    // This wave's logits, oldest sub-tile first: sub-tile `it` sits in lg[2*j], j = it + 32 - niter.
-    if constexpr (HOLD) {
-        const int niter = nsub > wave ? (nsub - wave + kDecWaves - 1) / kDecWaves : 0;
+    // This wave's logits, oldest sub-tile first: sub-tile `it` sits in lg[2*j],
+    // j = it + 32 - niter.
+    const int niter = nsub > wave ? (nsub - wave + kDecWaves - 1) / kDecWaves : 0;
+    if constexpr (MODE == kDec4Logits) {
         float* rowA = ws.logits + ((size_t)bg * G + 2 * hi) * ws.ncp;
         const bool wA = 2 * hi < G, wB = 2 * hi + 1 < G;
 #pragma unroll
@@ -570,6 +620,28 @@ void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
                 if (wA) rowA[k0 + key] = lg[2 * j];
                 if (wB) rowA[ws.ncp + k0 + key] = lg[2 * j + 1];
             }
+        }
+    }
+    // Fused: after the halves combine, lane (key, hi) holds the summed weight
+    // of sub-tile j = 2*i + hi for i < NT; its score and position are loaded
+    // now so that they arrive during the merge and the exchange.
+    constexpr int NT = kDec4MaxSub / 2;
+    auto slot_of = [&](int i, bool& ok) {
+        const int it = niter - kDec4MaxSub + 2 * i + hi;
+        const int slot = k_begin + (wave + kDecWaves * it) * kDecSub + key;
+        ok = it >= 0 && slot < k_end;
+        return ok ? slot : k_begin;
+    };
+    uint32_t phr[MODE == kDec4FusedEvict ? NT : 1], psr[MODE == kDec4FusedEvict ? NT : 1];
+    if constexpr (MODE == kDec4FusedEvict) {
+        const Rsrc rs = make_rsrc(ev.score + (size_t)bg * NC, n * 4);
+        const Rsrc rp = make_rsrc(ev.pos + (size_t)bg * NC, n * 4);
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            bool ok;
+            const int slot = slot_of(i, ok);
+            phr[i] = bload4(rs, slot * 4);
+            psr[i] = bload4(rp, slot * 4);
         }
     }
 
@@ -588,6 +660,7 @@ void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
     lh[1] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lB), 0));
     lh[2] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lA), 32));
     lh[3] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(lB), 32));
+    __shared__ float sL2[4];
     __syncthreads();
     constexpr int MF = L::MERGE_FLOATS;
     float* mb = reinterpret_cast<float*>(smem) + wave * MF;
@@ -602,40 +675,253 @@ void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt) {
             for (int r = 0; r < 4; ++r) mb[8 + (nn * 4 + r) * 64 + lane] = o[nn][r];
     }
     __syncthreads();
-    if (wave != 0) return;
-    // Wave 0 folds the other waves' states into its own, in wave order.
-    const float* mall = reinterpret_cast<const float*>(smem);
+    if (wave == 0) {
+        // Wave 0 folds the other waves' states into its own, in wave order.
+        const float* mall = reinterpret_cast<const float*>(smem);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float m = mh[r];
+        for (int r = 0; r < 4; ++r) {
+            float m = mh[r];
 #pragma unroll
-        for (int w = 1; w < kDecWaves; ++w) m = fmaxf(m, mall[w * MF + r]);
-        const float a0 = mh[r] == -INFINITY ? 0.f : fast_exp2((mh[r] - m) * c);
-        float l = lh[r] * a0;
+            for (int w = 1; w < kDecWaves; ++w) m = fmaxf(m, mall[w * MF + r]);
+            const float a0 = mh[r] == -INFINITY ? 0.f : fast_exp2((mh[r] - m) * c);
+            float l = lh[r] * a0;
 #pragma unroll
-        for (int nn = 0; nn < NO; ++nn) o[nn][r] *= a0;
+            for (int nn = 0; nn < NO; ++nn) o[nn][r] *= a0;
 #pragma unroll
-        for (int w = 1; w < kDecWaves; ++w) {
-            const float mw = mall[w * MF + r];
-            const float aw = mw == -INFINITY ? 0.f : fast_exp2((mw - m) * c);
-            l += mall[w * MF + 4 + r] * aw;
+            for (int w = 1; w < kDecWaves; ++w) {
+                const float mw = mall[w * MF + r];
+                const float aw = mw == -INFINITY ? 0.f : fast_exp2((mw - m) * c);
+                l += mall[w * MF + 4 + r] * aw;
 #pragma unroll
-            for (int nn = 0; nn < NO; ++nn) o[nn][r] += mall[w * MF + 8 + (nn * 4 + r) * 64 + lane] * aw;
+                for (int nn = 0; nn < NO; ++nn)
+                    o[nn][r] += mall[w * MF + 8 + (nn * 4 + r) * 64 + lane] * aw;
+            }
+            mh[r] = m == -INFINITY ? -INFINITY : m * c;    // log2 units from here on
+            lh[r] = l;
         }
-        mh[r] = m;
-        lh[r] = l;
-    }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        if (r >= G) break;
-        float* rec = ws.partial + (((size_t)bg * ws.nsplit + split) * G + r) * (D + 2);
+        for (int r = 0; r < 4; ++r) {
+            if (r >= G) break;
+            float* rec = ws.partial + (((size_t)bg * ws.nsplit + split) * G + r) * (D + 2);
+            if (lane == 0) {
+                rec[0] = mh[r];
+                rec[1] = lh[r];
+            }
+#pragma unroll
+            for (int nn = 0; nn < NO; ++nn) rec[2 + lane + 64 * nn] = o[nn][r];
+        }
+        if constexpr (MODE >= kDec4Fused) {
+            // Publish this split's (m, l) per head, form the new token's logits,
+            // then wait for every split of the (b, kv head) and merge the LSE.
+            uint64_t* xw = ws.xch + ((size_t)bg * ws.nsplit + split) * 4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (lane == r && r < G)
+                    __hip_atomic_store(xw + r,
+                                       ((uint64_t)__float_as_uint(mh[r]) << 32) |
+                                           __float_as_uint(lh[r]),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const u16* Kn = static_cast<const u16*>(a.kn) + (size_t)bg * D;
+            float snew[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                snew[r] = r < G ? new_token_logit2<D>(Q + (size_t)(b * a.Hq + g * G + r) * D, Kn,
+                                                      c, lane)
+                                : 0.f;
+            const int sp = lane >> 2, hq = lane & 3;
+            const bool need = sp < nsplit_rt && hq < G;
+            const uint64_t* xr = ws.xch + ((size_t)bg * ws.nsplit + min(sp, nsplit_rt - 1)) * 4 + hq;
+            uint64_t w = kXchEmpty;
+            for (int spin = 0; spin < kXchSpinLimit; ++spin) {
+                if (need && w == kXchEmpty)
+                    w = __hip_atomic_load(xr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (__all(!need || w != kXchEmpty)) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            const int whi = (int)(uint32_t)(w >> 32), wlo = (int)(uint32_t)w;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int src = min(lane, kXchMaxSplits - 1) * 4 + r;
+                const float m0 = __int_as_float(__shfl(whi, src));
+                const float l0 = __int_as_float(__shfl(wlo, src));
+                const bool has = lane < nsplit_rt;
+                float mm;
+                const float l2 = merge_lse2(has ? m0 : -INFINITY, has ? l0 : 0.f, snew[r], lane, mm);
+                if (lane == 0) sL2[r] = r < G ? l2 : INFINITY;   // heads >= G add nothing
+            }
+        }
+    }
+    if constexpr (MODE >= kDec4Fused) {
+        __syncthreads();
+        // Summed weights sum_h exp2(s_h - LSE_h) of this lane's slots: its two heads
+        // per sub-tile, then the other half's two heads through one swap per pair
+        // of sub-tiles (heads 0+1, then 2+3 added, in every slot).
+        const float La = sL2[2 * hi], Lb = sL2[2 * hi + 1];
+        float tot[NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const float wa = fast_exp2(lg[4 * i] - La) + fast_exp2(lg[4 * i + 1] - Lb);
+            const float wb = fast_exp2(lg[4 * i + 2] - La) + fast_exp2(lg[4 * i + 3] - Lb);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(wa),
+                                                             __float_as_uint(wb), false, false);
+            tot[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        float* csr = a.cs_cache + (size_t)bg * NC;
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            bool ok;
+            const int slot = slot_of(i, ok);
+            if (ok) csr[slot] = tot[i];
+        }
+        if constexpr (MODE == kDec4FusedEvict) {
+            // Score update phi += summed weight, and the eviction key of every filled
+            // slot: eligible iff t(j) < P - W; h2o-norm divides by the age t - t(j),
+            // t = P + 1.  The same operations as the separate update and selection.
+            __shared__ uint64_t sBest[kDecWaves];
+            const bool full = n == NC;                    // one victim (k = n + 1 - N_C)
+            const int thr = a.P - ev.W, t_now = a.P + 1;
+            float* scw = ev.score + (size_t)bg * NC;
+            uint64_t best = ~0ull;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                bool ok;
+                const int slot = slot_of(i, ok);
+                const float v = __uint_as_float(phr[i]) + tot[i];
+                if (ok) scw[slot] = v;
+                const int pj = (int)psr[i];
+                float r = v;
+                if (ev.score_mode == H2O_SCORE_H2O_NORM) r = r / (float)(t_now - pj);
+                const uint32_t k = pj < thr ? order_key(r) : kIneligible;
+                const uint64_t kv = ((uint64_t)k << 32) | (uint32_t)slot;
+                if (ok && kv < best) best = kv;
+            }
+            if (!full) return;                            // filling: the token goes to slot n
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const uint64_t ot = __shfl_xor(best, off);
+                best = ot < best ? ot : best;
+            }
+            if (lane == 0) sBest[wave] = best;
+            __syncthreads();
+            if (tid == 0) {
+                uint64_t m = sBest[0];
+#pragma unroll
+                for (int w = 1; w < kDecWaves; ++w) m = sBest[w] < m ? sBest[w] : m;
+                ws.part_min[(size_t)bg * ws.nfin + split] = m;
+            }
+        }
+    }
+}
+
+// After the fused decode_attn4_kernel: one workgroup per (b, kv head) merges
+// the split partials with the new token into O and LSE (the same LSE
+// arithmetic as the fused kernel), writes the new token's own summed weight,
+// and (EVICT) takes the smallest (key, slot) of the splits' minima (full
+// cache) or slot n (filling) and writes the new token there: K and V rows,
+// t = P, score = its summed weight, freed_slots.
+template <int D, bool EVICT>
+__global__ __launch_bounds__(kDecThreads) void decode_merge_kernel(ChunkArgs a, DecodeWs ws,
+                                                                   int nsplit_rt, EvictArgs ev) {
+    constexpr int PER = 4 * D / kDecThreads;           // (head, d) outputs per thread (G <= 4)
+    constexpr int units = D * 2 / 16;                  // 16-byte units of a bf16 row
+    static_assert(2 * units <= 64, "one lane per row unit");
+    __shared__ float sLse2[4], sNew[4], sM[4];
+    const int bg = blockIdx.x;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int G = a.G;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float c = a.sm_scale * kLog2e;
+    const u16* Q = static_cast<const u16*>(a.q);
+    const u16* Kn = static_cast<const u16*>(a.kn) + (size_t)bg * D;
+    const u16* Vn = static_cast<const u16*>(a.vn) + (size_t)bg * D;
+    const size_t stride = (size_t)G * (D + 2);
+    const float* rec_bg = ws.partial + (size_t)bg * ws.nsplit * stride;
+    auto bf = [](u16 x) { return __uint_as_float((uint32_t)x << 16); };
+
+    // Every global read first, so that they are in flight together: wave hh's
+    // split records of head hh; each thread's partial outputs of its (head, d)
+    // pairs; the new value row; (EVICT) the splits' minima and the new K and V rows.
+    const int hh = wave;
+    const bool has = hh < G && lane < nsplit_rt;
+    const float mrec = has ? rec_bg[lane * stride + hh * (D + 2)] : -INFINITY;
+    const float lrec = has ? rec_bg[lane * stride + hh * (D + 2) + 1] : 0.f;
+    float pm[PER][kXchMaxSplits], po[PER][kXchMaxSplits], vn[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = min(tid + i * kDecThreads, G * D - 1);
+        const int h = idx / D, d = idx % D;
+        vn[i] = bf(Vn[d]);
+#pragma unroll
+        for (int sp = 0; sp < kXchMaxSplits; ++sp) {
+            const float* rec = rec_bg + min(sp, nsplit_rt - 1) * stride + h * (D + 2);
+            pm[i][sp] = sp < nsplit_rt ? rec[0] : -INFINITY;
+            po[i][sp] = sp < nsplit_rt ? rec[2 + d] : 0.f;
+        }
+    }
+    uint64_t mn = ~0ull;
+    u32x4 row = {0u, 0u, 0u, 0u};
+    if (EVICT && wave == 0) {
+        if (a.n == a.NC && lane < nsplit_rt) mn = ws.part_min[(size_t)bg * ws.nfin + lane];
+        if (lane < 2 * units)
+            row = static_cast<const u32x4*>(lane >= units ? a.vn : a.kn)[(size_t)bg * units +
+                                                                       lane % units];
+    }
+
+    if (hh < G) {
+        const float s_new =
+            new_token_logit2<D>(Q + (size_t)(b * a.Hq + g * G + hh) * D, Kn, c, lane);
+        float m;
+        const float l2 = merge_lse2(mrec, lrec, s_new, lane, m);
         if (lane == 0) {
-            rec[0] = mh[r] == -INFINITY ? -INFINITY : mh[r] * c;    // log2 units
-            rec[1] = lh[r];
+            sLse2[hh] = l2;
+            sNew[hh] = s_new;
+            sM[hh] = m;
         }
-#pragma unroll
-        for (int nn = 0; nn < NO; ++nn) rec[2 + lane + 64 * nn] = o[nn][r];
     }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = tid + i * kDecThreads;
+        if (idx >= G * D) break;
+        const int h = idx / D, d = idx % D;
+        const float m = sM[h];
+        float acc = vn[i] * fast_exp2(sNew[h] - m);
+#pragma unroll
+        for (int sp = 0; sp < kXchMaxSplits; ++sp)
+            if (pm[i][sp] != -INFINITY) acc += po[i][sp] * fast_exp2(pm[i][sp] - m);
+        const float inv = fast_exp2(m - sLse2[h]);         // 1 / l
+        const size_t oi = (size_t)(b * a.Hq + g * G + h) * D + d;
+        static_cast<__hip_bfloat16*>(a.out)[oi] = __float2bfloat16(acc * inv);
+        if (d == 0) a.lse[(size_t)(b * a.Hq + g * G + h)] = sLse2[h] * 0.6931471805599453f;
+    }
+    if (wave != 0) return;
+    float cs = 0.f;
+    for (int h = 0; h < G; ++h) cs += fast_exp2(sNew[h] - sLse2[h]);
+    if (lane == 0) a.cs_new[bg] = cs;
+    if constexpr (EVICT) {
+        int slot = a.n;
+        if (a.n == a.NC) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const uint64_t o = __shfl_xor(mn, off);
+                mn = o < mn ? o : mn;
+            }
+            slot = (int)(uint32_t)mn;
+        }
+        if (lane < 2 * units)
+            static_cast<u32x4*>(lane >= units ? ev.vc : ev.kc)[((size_t)bg * a.NC + slot) * units +
+                                                              lane % units] = row;
+        if (lane == 0) {
+            ev.freed[bg] = slot;
+            ev.pos[(size_t)bg * a.NC + slot] = a.P;
+            ev.score[(size_t)bg * a.NC + slot] = cs;
+        }
+    }
+}
+
+__global__ void decode_clear_kernel(uint64_t* x, int count) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
+        x[i] = kXchEmpty;
 }
 
 // Merge the splits and the new token, write O / LSE (first workgroup of each
@@ -925,9 +1211,9 @@ __global__ __launch_bounds__(64) void decode_insert_kernel(ChunkArgs a, DecodeWs
 }
 
 // Workspace: logits, split partials, then (8-byte aligned) the finish
-// workgroups' minima and the arrival counters.
+// workgroups' minima and the LSE exchange words.
 struct WsSizes {
-    size_t logits, partial, part_min;
+    size_t logits, partial, part_min, xch;
 };
 WsSizes ws_sizes(int B, int Hq, int Hkv, int NC) {
     const int G = Hq / Hkv;
@@ -939,6 +1225,7 @@ WsSizes ws_sizes(int B, int Hq, int Hkv, int NC) {
     w.logits = (size_t)B * Hkv * G * ncp * 4;
     w.partial = (size_t)B * Hkv * nsplit * G * (D + 2) * 4;
     w.part_min = (size_t)B * Hkv * nfin * 8;
+    w.xch = (size_t)B * Hkv * nsplit * 4 * 8;
     return w;
 }
 
@@ -953,6 +1240,7 @@ DecodeWs ws_layout(void* base, int B, int Hq, int Hkv, int NC, int D) {
     w.partial = reinterpret_cast<float*>(p + z.logits);
     const size_t mins = (z.logits + z.partial + 7) / 8 * 8;
     w.part_min = reinterpret_cast<uint64_t*>(p + mins);
+    w.xch = reinterpret_cast<uint64_t*>(p + mins + z.part_min);
     (void)D;
     return w;
 }
@@ -961,46 +1249,109 @@ DecodeWs ws_layout(void* base, int B, int Hq, int Hkv, int NC, int D) {
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int NC) {
     const WsSizes z = ws_sizes(B, Hq, Hkv, NC);
-    return (z.logits + z.partial + 7) / 8 * 8 + z.part_min;
+    return (z.logits + z.partial + 7) / 8 * 8 + z.part_min + z.xch;
 }
+
+namespace {
+
+template <int MODE>
+const void* dec4_fn() {
+    return reinterpret_cast<const void*>(&decode_attn4_kernel<128, MODE>);
+}
+
+// Once per device: the LDS limit of the decode kernels, and how many
+// workgroups of each fused variant the device holds at once.
+hipError_t configure_decode(int* cap_fused, int* cap_evict) {
+    static unsigned configured = 0;
+    static int cap[2][32] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 32) return hipErrorInvalidDevice;
+    const unsigned bit = 1u << dev;
+    if (!(configured & bit)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<128>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, DecSmem<128>::BYTES);
+        const void* fns[4] = {dec4_fn<kDec4NoWeights>(), dec4_fn<kDec4Logits>(),
+                              dec4_fn<kDec4Fused>(), dec4_fn<kDec4FusedEvict>()};
+        for (int m = 0; m < 4 && e == hipSuccess; ++m)
+            e = hipFuncSetAttribute(fns[m], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    Dec4Smem<128>::BYTES);
+        int cus = 0;
+        if (e == hipSuccess) e = cu_count(&cus);
+        for (int m = 0; m < 2 && e == hipSuccess; ++m) {
+            int nb = 0;
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fns[2 + m], kDecThreads,
+                                                             Dec4Smem<128>::BYTES);
+            cap[m][dev] = nb * cus;
+        }
+        if (e != hipSuccess) return e;
+        configured |= bit;
+    }
+    *cap_fused = cap[0][dev];
+    *cap_evict = cap[1][dev];
+    return hipSuccess;
+}
+
+}  // namespace
 
 hipError_t launch_decode(const ChunkArgs& a, void* workspace, hipStream_t s,
                          const EvictArgs* ev) {
     if (a.D != 128) return hipErrorNotSupported;
     const DecodeWs ws = ws_layout(workspace, a.B, a.Hq, a.Hkv, a.NC, a.D);
     const int nsplit_rt = (a.n + kDecSplit - 1) / kDecSplit;
-    if (nsplit_rt > 0) {
-        static unsigned configured = 0;
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
+    int cap_fused = 0, cap_evict = 0;
+    hipError_t e = configure_decode(&cap_fused, &cap_evict);
+    if (e != hipSuccess) return e;
+    const int total = nsplit_rt * a.B * a.Hkv;
+    const int grid = xcd_grid(total);
+
+    // Summed weights inside the attention kernel: its workgroups wait for their
+    // siblings' (m, l), so every workgroup of the launch must be resident at once.
+    // Our workgroups never hold up another kernel's, so a grid within the
+    // device's capacity for this kernel always becomes fully resident.
+    if (nsplit_rt > 0 && a.cs_cache != nullptr && a.G <= 4 && nsplit_rt <= kXchMaxSplits &&
+        grid <= (ev != nullptr ? cap_evict : cap_fused)) {
+        const int words = a.B * a.Hkv * ws.nsplit * 4;
+        hipLaunchKernelGGL(decode_clear_kernel, dim3((words + kDecThreads - 1) / kDecThreads),
+                           dim3(kDecThreads), 0, s, ws.xch, words);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
-        const unsigned bit = 1u << (dev & 31);
-        if (!(configured & bit)) {
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<128>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    DecSmem<128>::BYTES);
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(
-                    reinterpret_cast<const void*>(&decode_attn4_kernel<128, true>),
-                    hipFuncAttributeMaxDynamicSharedMemorySize, Dec4Smem<128>::BYTES);
-            if (e == hipSuccess)
-                e = hipFuncSetAttribute(
-                    reinterpret_cast<const void*>(&decode_attn4_kernel<128, false>),
-                    hipFuncAttributeMaxDynamicSharedMemorySize, Dec4Smem<128>::BYTES);
-            if (e != hipSuccess) return e;
-            configured |= bit;
-        }
-        const int total = nsplit_rt * a.B * a.Hkv;
+        timer_begin(H2O_KERNEL_DECODE, s);
+        if (ev != nullptr)
+            hipLaunchKernelGGL((decode_attn4_kernel<128, kDec4FusedEvict>), dim3(grid),
+                               dim3(kDecThreads), Dec4Smem<128>::BYTES, s, a, ws, nsplit_rt, *ev);
+        else
+            hipLaunchKernelGGL((decode_attn4_kernel<128, kDec4Fused>), dim3(grid),
+                               dim3(kDecThreads), Dec4Smem<128>::BYTES, s, a, ws, nsplit_rt,
+                               EvictArgs{});
+        timer_end(H2O_KERNEL_DECODE, s);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        timer_begin(H2O_KERNEL_DECODE_FINISH, s);
+        if (ev != nullptr)
+            hipLaunchKernelGGL((decode_merge_kernel<128, true>), dim3(a.B * a.Hkv),
+                               dim3(kDecThreads), 0, s, a, ws, nsplit_rt, *ev);
+        else
+            hipLaunchKernelGGL((decode_merge_kernel<128, false>), dim3(a.B * a.Hkv),
+                               dim3(kDecThreads), 0, s, a, ws, nsplit_rt, EvictArgs{});
+        timer_end(H2O_KERNEL_DECODE_FINISH, s);
+        return hipGetLastError();
+    }
+
+    if (nsplit_rt > 0) {
         timer_begin(H2O_KERNEL_DECODE, s);
         if (a.G > 4)
-            hipLaunchKernelGGL(decode_attn_kernel<128>, dim3(xcd_grid(total)), dim3(kDecThreads),
+            hipLaunchKernelGGL(decode_attn_kernel<128>, dim3(grid), dim3(kDecThreads),
                                DecSmem<128>::BYTES, s, a, ws, nsplit_rt);
         else if (a.cs_cache != nullptr)
-            hipLaunchKernelGGL((decode_attn4_kernel<128, true>), dim3(xcd_grid(total)),
-                               dim3(kDecThreads), Dec4Smem<128>::BYTES, s, a, ws, nsplit_rt);
+            hipLaunchKernelGGL((decode_attn4_kernel<128, kDec4Logits>), dim3(grid),
+                               dim3(kDecThreads), Dec4Smem<128>::BYTES, s, a, ws, nsplit_rt,
+                               EvictArgs{});
         else
-            hipLaunchKernelGGL((decode_attn4_kernel<128, false>), dim3(xcd_grid(total)),
-                               dim3(kDecThreads), Dec4Smem<128>::BYTES, s, a, ws, nsplit_rt);
+            hipLaunchKernelGGL((decode_attn4_kernel<128, kDec4NoWeights>), dim3(grid),
+                               dim3(kDecThreads), Dec4Smem<128>::BYTES, s, a, ws, nsplit_rt,
+                               EvictArgs{});
         timer_end(H2O_KERNEL_DECODE, s);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1015,7 +1366,7 @@ hipError_t launch_decode(const ChunkArgs& a, void* workspace, hipStream_t s,
         hipLaunchKernelGGL((decode_finish_kernel<128, false>), dim3(kchunks, a.B * a.Hkv),
                            dim3(kDecThreads), 0, s, a, ws, nsplit_rt, kchunks, EvictArgs{});
     timer_end(H2O_KERNEL_DECODE_FINISH, s);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess || ev == nullptr) return e;
     timer_begin(H2O_KERNEL_INSERT, s);
     hipLaunchKernelGGL(decode_insert_kernel, dim3(a.B * a.Hkv), dim3(64), 0, s, a, ws, kchunks,

@@ -82,6 +82,9 @@ hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void*
                                 float* drow, float* dq, float* dk_new, float* dv_new,
                                 float* dk_cache, float* dv_cache, int parts, hipStream_t s);
 
+// Compute units of the current device (api.hip), read once per device.
+hipError_t cu_count(int* cus);
+
 // Decode (S = 1) specialisation.
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int NC);
 // ev != NULL (summed weights required): the finishing kernel also updates the

@@ -191,11 +191,15 @@ H2O_API h2o_status_t h2o_update_evict_and_insert(const h2o_dims_t *dims, h2o_cac
  * (h2o_workspace_bytes); score_mode, freed_slots, the cache update and the
  * advance of cache->n_valid are h2o_update_evict_and_insert's.  Every error of
  * either call (H2O_ERR_CAPACITY included) is returned before anything is
- * launched.  For S = 1 on the split decode path (bf16, d = 128) the score update,
- * the selection of the one victim and the insertion of the token run inside the
- * kernel that forms the summed weights, which already visits every slot: one
- * pass over the scores instead of two, and two launches per step instead of
- * three.
+ * launched.  For S = 1 on the split decode path (bf16, d = 128) the score update
+ * and each split's victim candidate are formed inside the kernel that forms the
+ * summed weights, which already visits every slot, and one small launch merges
+ * the output and inserts the token: one pass over the scores instead of two.
+ * With at most four query heads per KV head, and when the device can hold the
+ * whole split grid at once, that kernel is the attention launch itself: its
+ * workgroups exchange their partial log-sum-exps within the launch (they wait
+ * only for one another, so work on other streams delays but cannot block
+ * them) and the logits never leave the chip.
  */
 H2O_API h2o_status_t h2o_chunk_step(const h2o_dims_t *dims, h2o_cache_t *cache,
                             int64_t chunk_start, int32_t chunk_len, float sm_scale,
@@ -346,7 +350,8 @@ typedef enum {
     H2O_KERNEL_SELECT = 3,    /* eligibility + victim selection                 */
     H2O_KERNEL_INSERT = 4,    /* chunk insertion                                */
     H2O_KERNEL_DECODE = 5,    /* S = 1 attention (split over slots)             */
-    H2O_KERNEL_DECODE_FINISH = 6, /* S = 1: merge of the splits, summed weights */
+    H2O_KERNEL_DECODE_FINISH = 6, /* S = 1: merge of the splits (and summed weights
+                                     when the attention launch did not form them) */
     H2O_KERNEL_BACKWARD = 7,  /* backward of the chunk attention (all its launches) */
     H2O_KERNEL_COUNT = 8
 } h2o_kernel_id_t;

@@ -268,6 +268,21 @@ def test_decode_teacher_forced_then_free_running():
     print(f"decode: near-tie swaps teacher-forced {tf}, free-running {free}")
 
 
+def test_decode_grid_beyond_resident_capacity():
+    """Decode with 160 (sequence, KV head) rows of 16384 slots: 640 split workgroups,
+    more than a 256-CU device holds at once, so the summed weights go through the
+    logit workspace and the separate finishing pass instead of the in-kernel LSE
+    exchange.  Two full-cache steps against the oracle."""
+    wl = W.workload(5, batch=40, n_q_heads=16, n_kv_heads=4)
+    s = W.decode_initial_state(wl)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    del s
+    H.run_chain(wl, range(2), lambda t: W.decode_step_inputs(wl, t), cache=cache, st=st,
+                rows="freed")
+
+
 def test_layer_stack_first_chunks():
     """36-layer stack workload: the first two chunks (n = 0, 1024) of the last layer,
     whose inputs come from that layer's own seed."""
