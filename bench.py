@@ -174,6 +174,9 @@ def check_replay(name, pairs):
             sys.exit(3)
 
 
+SPIN_CYCLES = 2_000_000      # torch.cuda._sleep: at least ~1 ms at any shader clock
+
+
 def steady_chunk(wl, dims, step_kw, bufs, reps: int = 10):
     """One chunk of the path (all its calls) on a full cache, replayed from a captured HIP
     graph and timed alone with HIP events on the replay stream: the cache is reloaded from
@@ -203,6 +206,10 @@ def steady_chunk(wl, dims, step_kw, bufs, reps: int = 10):
         reset()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        # A device-side spin ahead of the start event keeps the GPU busy while the
+        # host submits the event and the graph, so the interval holds the chunk's
+        # GPU work and not the host's submission latency.
+        torch.cuda._sleep(SPIN_CYCLES)
         e0.record()
         graph.replay()
         e1.record()

@@ -775,6 +775,9 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
 #pragma unroll
                 for (int j = 0; j < QA; ++j) qr[j] = qread(sQm, subm, j);
             }
+            // Each exponential is added one k-step later, off its latency (the
+            // same additions in the same order: 87.1 -> 85.8 us per steady chunk).
+            float pend[PER];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 if (do_mfma) {
@@ -786,9 +789,19 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
 #pragma unroll
                 for (int e = 0; e < PER; ++e) {
                     const int x = ks * PER + e;
-                    acc[x >> 4][x & 15] += fast_exp2(fmaf(sv[x >> 4][x & 15], c, -lse2));
+                    const float p = fast_exp2(fmaf(sv[x >> 4][x & 15], c, -lse2));
+                    if (ks > 0) {
+                        const int xp = x - PER;
+                        acc[xp >> 4][xp & 15] += pend[e];
+                    }
+                    pend[e] = p;
                 }
                 __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int xp = (KS - 1) * PER + e;
+                acc[xp >> 4][xp & 15] += pend[e];
             }
         } else {
             if (do_mfma) {
