@@ -453,13 +453,15 @@ def _tie_scores(phi, seed):
 
 @pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
 @pytest.mark.parametrize("case", ["decode_full", "decode_ties", "decode_filling", "prefill_steady",
-                                  "prefill_filling", "f32_plumbing"])
+                                  "prefill_filling", "prefill_partial_evict", "f32_plumbing"])
 def test_chunk_step_matches_separate_calls(case, score_mode):
     """h2o_chunk_step gives bit for bit what h2o_chunk_attn followed by
-    h2o_update_evict_and_insert gives.  For decode steps the update, the one-victim
-    selection (lowest slot among equal keys, across the finishing workgroups) and the
-    insertion run inside the finishing kernel; the victims are also checked against the
-    oracle's."""
+    h2o_update_evict_and_insert gives.  For decode steps the update and each split's
+    victim candidate are formed in the attention launch and the one-victim selection
+    (lowest slot among equal keys) and insertion in the merge launch; the victims are
+    also checked against the oracle's.  Prefill: a steady full-size chunk (1024
+    victims), a filling chunk, and prefill_partial_evict: a cache of 384 of 500 slots
+    taking 128 tokens (12 victims and 116 empty slots)."""
     if case.startswith("decode"):
         wl = W.workload(5, batch=4)
         s = W.decode_initial_state(wl)
@@ -480,14 +482,16 @@ def test_chunk_step_matches_separate_calls(case, score_mode):
         s = W.steady_state(wl, 0, start=10 * wl.chunk, seed=4, tie_fraction=0.2)
         x = W.chunk_inputs(wl, 0, 10)
     else:
-        wl = W.workload(2, batch=2, n_q_heads=8, n_kv_heads=2, capacity=512, recent_window=64,
-                        chunk=128, seq_len=2048, heavy_count=20)
+        partial = case == "prefill_partial_evict"
+        wl = W.workload(2, batch=2, n_q_heads=8, n_kv_heads=2, capacity=500 if partial else 512,
+                        recent_window=64, chunk=128, seq_len=2048, heavy_count=20)
         st0 = oracle.H2OState.empty(wl.batch, wl.n_kv_heads, wl.capacity, wl.head_dim)
-        for c in range(2):
+        c0 = 3 if partial else 2
+        for c in range(c0):
             xc = W.chunk_inputs(wl, 0, c)
             oracle.h2o_step(st0, xc["q"], xc["k"], xc["v"], wl.sm_scale, wl.recent_window)
         s = {"k": st0.K, "v": st0.V, "pos": st0.pos, "phi": st0.phi, "n": st0.n, "start": st0.P}
-        x = W.chunk_inputs(wl, 0, 2)
+        x = W.chunk_inputs(wl, 0, c0)
     st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
     fused, sep = (h2o.H2OCache(H.dims_of(wl), H.DEV) for _ in range(2))
     for c in (fused, sep):
