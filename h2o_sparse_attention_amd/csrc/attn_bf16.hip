@@ -426,9 +426,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
                 return as_bf16x8(ld16(kbase + ((kb ^ (32 * ks)) + sub * 32 * RB)));
             };
             constexpr int NEA = 24;               // exponentials in this phase (of 32)
-            bf16x8 kr[2][2];
+            // K fragments are read two k-steps ahead of their MFMAs (one ahead:
+            // 147.2 against 146.4 us per steady chunk).
+            bf16x8 kr[3][2];
             kr[0][0] = kread(0, 0);
             kr[0][1] = kread(0, 1);
+            kr[1][0] = kread(1, 0);
+            kr[1][1] = kread(1, 1);
             snext[0] = f32x16{};
             snext[1] = f32x16{};
             float p[8];
@@ -438,12 +442,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                if (ks + 1 < KS) {
-                    kr[(ks + 1) & 1][0] = kread(ks + 1, 0);
-                    kr[(ks + 1) & 1][1] = kread(ks + 1, 1);
+                if (ks + 2 < KS) {
+                    kr[(ks + 2) % 3][0] = kread(ks + 2, 0);
+                    kr[(ks + 2) % 3][1] = kread(ks + 2, 1);
                 }
-                snext[0] = mfma32(kr[ks & 1][0], qf[ks], snext[0]);
-                snext[1] = mfma32(kr[ks & 1][1], qf[ks], snext[1]);
+                snext[0] = mfma32(kr[ks % 3][0], qf[ks], snext[0]);
+                snext[1] = mfma32(kr[ks % 3][1], qf[ks], snext[1]);
 #pragma unroll
                 for (int idx = ks * NEA / KS; idx < (ks + 1) * NEA / KS; ++idx) {
                     const int q4 = idx >> 3, ee = idx & 7;

@@ -4,33 +4,37 @@
 // montaan paper page, "Kernel Support Needs" (summed attention weights and
 // the implicit positional mask) specialised to one query token per sequence,
 // the generation setting of the metallab summary's Table 7.  With one query
-// row per head the pass is bound by reading the cache once, so:
+// row per head the pass is bound by reading the cache once.  One workgroup
+// takes one (b, kv head, 4096-slot range); each of its 4 waves streams
+// 32-slot tiles through a private LDS region (no workgroup barriers in the
+// loop) and keeps an online-softmax state (m, l, O); the waves merge and the
+// workgroup writes one partial per split.
 //
-//  decode_attn_kernel  one workgroup per (b, kv head, 4096-slot range).  Each
-//      of its 4 waves streams 32-slot tiles through a private LDS region (no
-//      workgroup barriers), forms S^T = K Q^T with the G query heads of the
-//      group as MFMA columns, writes the scaled logits (log2 units) of every
-//      slot to the workspace, and keeps an online-softmax state (m, l, O);
-//      the waves merge and the workgroup writes one partial per split.
-//  decode_finish_kernel  merges the partials with the new token (its own key
-//      and value) into O and LSE, then turns the stored logits into the summed
-//      weights sum_{h in g} exp(s - LSE_h) per slot.
-//  When the caller asks for no summed weights, the logits are not stored and
-//  the finish kernel runs one workgroup per (b, kv head) for O and LSE only.
-//  For a whole step (h2o_chunk_step) the finish kernel also adds each slot's
-//  summed weight to its score, forms the eviction keys and reduces them to one
-//  (key, slot) minimum per workgroup; decode_insert_kernel (one wave per
-//  (b, kv head)) then takes the minimum of those, the victim, and writes the
-//  new token into it -- the score update, selection and insertion without a
-//  second pass over the scores.  (The hand-over between the two kernels is the
-//  kernel boundary: a device-scope fence per finishing workgroup, so that the
-//  last one could insert, writes back its XCD's L2 and measured 61 us against
-//  22 us for the separate launches.)
+//  decode_attn4_kernel  (at most four query heads per KV head) 4x4x4 MFMA
+//      blocks put one slot per lane, so a wave holds the logits of all its
+//      tiles in registers.  With summed weights and a grid that the device
+//      holds at once, the splits of a (b, kv head) exchange (m, l) within
+//      the launch, and each workgroup turns its held logits into summed
+//      weights -- and, for a whole step (h2o_chunk_step), the score update,
+//      the eviction keys and its (key, slot) minimum.  decode_merge_kernel
+//      then forms O and LSE and inserts the new token.  Otherwise the held
+//      logits go to the workspace in one burst after the loads.
+//  decode_attn_kernel  (more heads per KV head) the G query heads are the
+//      columns of 32x32x16 MFMAs; the logits go to the workspace tile by tile.
+//  decode_finish_kernel  after either of the logit-writing forms: merges the
+//      partials with the new token (its own key and value) into O and LSE,
+//      turns the stored logits into summed weights, and for a whole step
+//      adds them to the scores and reduces the eviction keys to one minimum
+//      per range; decode_insert_kernel (one wave per (b, kv head)) takes the
+//      minimum of those, the victim, and writes the new token into it.
+//  (A hand-over inside one finishing kernel -- a device-scope fence per
+//  finishing workgroup so that the last one could insert -- writes back its
+//  XCD's L2 and measured 61 us against 22 us for the separate launches.)
 //
 // P V uses ds_read_b64_tr_b16: a 16-lane group addresses four rows of four
 // consecutive bf16 (one key, four d each) and lane j receives column j%4 of
-// rows j/4, j/4+4, j/4+8, j/4+12, i.e. four keys of one d -- exactly the
-// k-slots of the MFMA A operand V^T -- so V stays row-major in LDS.
+// the pieces addressed by lanes j/4, j/4+4, j/4+8, j/4+12, i.e. four keys of
+// one d -- the k-slots of the MFMA operand V^T -- so V stays row-major in LDS.
 #include "h2o_internal.h"
 #include "device_common.h"
 
@@ -516,6 +520,8 @@ void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt, EvictArgs ev) 
 #pragma unroll
     for (int nn = 0; nn < NO; ++nn) o[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
     float lg[HOLD ? 2 * kDec4MaxSub : 1];
+    uint32_t elig = 0;
+    const int elig_thr = a.P - ev.W;
 #pragma unroll
     for (int i = 0; i < (HOLD ? 2 * kDec4MaxSub : 1); ++i) lg[i] = 0.f;
 
@@ -554,6 +560,10 @@ void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt, EvictArgs ev) 
             lg[2 * kDec4MaxSub - 2] = sa * c;
             lg[2 * kDec4MaxSub - 1] = sb * c;
         }
+        // Eviction eligibility of this lane's slot, t(j) < P - W, shifted in like
+        // the logits (h2o keys need nothing else of the position).
+        if constexpr (MODE == kDec4FusedEvict)
+            elig = (elig >> 1) | ((uint32_t)(pcur < elig_thr) << 31);
         if (__any(sa > mA + tau_raw || sb > mB + tau_raw)) {
             float ta = sa, tb = sb;
 #pragma unroll
@@ -632,16 +642,19 @@ void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt, EvictArgs ev) 
         ok = it >= 0 && slot < k_end;
         return ok ? slot : k_begin;
     };
+    // Under h2o-norm the keys also need each slot's age, so its position is read
+    // again; h2o keys use the eligibility bits kept during the loop.
+    const bool norm = ev.score_mode == H2O_SCORE_H2O_NORM;
     uint32_t phr[MODE == kDec4FusedEvict ? NT : 1], psr[MODE == kDec4FusedEvict ? NT : 1];
     if constexpr (MODE == kDec4FusedEvict) {
         const Rsrc rs = make_rsrc(ev.score + (size_t)bg * NC, n * 4);
-        const Rsrc rp = make_rsrc(ev.pos + (size_t)bg * NC, n * 4);
+        const Rsrc rp = make_rsrc(ev.pos + (size_t)bg * NC, norm ? n * 4 : 0);
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
             bool ok;
             const int slot = slot_of(i, ok);
             phr[i] = bload4(rs, slot * 4);
-            psr[i] = bload4(rp, slot * 4);
+            psr[i] = norm ? bload4(rp, slot * 4) : 0u;
         }
     }
 
@@ -788,10 +801,13 @@ void decode_attn4_kernel(ChunkArgs a, DecodeWs ws, int nsplit_rt, EvictArgs ev) 
                 const int slot = slot_of(i, ok);
                 const float v = __uint_as_float(phr[i]) + tot[i];
                 if (ok) scw[slot] = v;
-                const int pj = (int)psr[i];
-                float r = v;
-                if (ev.score_mode == H2O_SCORE_H2O_NORM) r = r / (float)(t_now - pj);
-                const uint32_t k = pj < thr ? order_key(r) : kIneligible;
+                uint32_t k;
+                if (norm) {
+                    const int pj = (int)psr[i];
+                    k = pj < thr ? order_key(v / (float)(t_now - pj)) : kIneligible;
+                } else {
+                    k = ((elig >> (2 * i + hi)) & 1u) ? order_key(v) : kIneligible;
+                }
                 const uint64_t kv = ((uint64_t)k << 32) | (uint32_t)slot;
                 if (ok && kv < best) best = kv;
             }
