@@ -252,6 +252,29 @@ def test_determinism_bitwise():
         assert (outs[0][key] == outs[1][key]).all(), key
 
 
+@pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
+def test_decode_step_determinism_bitwise(score_mode):
+    """Two runs of the same full-cache decode step (the splits exchanging their (m, l)
+    inside the attention launch) give identical bits in every output and in the cache."""
+    wl = W.workload(5, batch=4)
+    s = W.decode_initial_state(wl)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    x = W.decode_step_inputs(wl, 0)
+    dt = H.TORCH_DT[wl.dtype]
+    q, k, v = H.dev(x["q"], dt), H.dev(x["k"], dt), H.dev(x["v"], dt)
+    runs = []
+    for _ in range(2):
+        cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+        H.load_oracle_state(cache, st, wl.dtype)
+        got = h2o.chunk_step(cache, st.P, q, k, v, wl.sm_scale, score_mode)
+        torch.cuda.synchronize()
+        runs.append([t.clone() for t in got] + [cache.k.clone(), cache.v.clone(),
+                                                cache.pos.clone(), cache.score.clone()])
+    names = ("out", "lse", "colsum_cache", "colsum_new", "freed_slots", "k", "v", "pos", "score")
+    for name, a_, b_ in zip(names, runs[0], runs[1]):
+        assert torch.equal(a_, b_), name
+
+
 def test_decode_teacher_forced_then_free_running():
     """Decode workload (16 sequences, N_C 16384 full, W 512): 32 single-token steps
     teacher-forced (the oracle's scores loaded after every step), then 32 more
