@@ -539,7 +539,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 // query row of the group (G heads x S positions).  Each wave holds kColsumKB
 // blocks of 32 keys (one: at two, each Q fragment read from LDS feeds two
 // MFMAs, but the 2 waves per SIMD that the registers then allow ran slower
-// than 3 waves with one block).  K stays in registers; Q and
+// than 3 or 4 waves with one block).  K stays in registers; Q and
 // LSE tiles of 64 packed rows (row r = i*G + head) go from global memory
 // straight into double-buffered LDS, Q rows XOR-swizzled like the attention
 // pass's K.  Each lane accumulates its 16 keys over its query column, and the
@@ -565,19 +565,24 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 //      exponentials of sub-tile 1 of tile rt.
 // ---------------------------------------------------------------------------
 template <int D, bool EVEN_ROWS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kColsumKB == 1 ? 3 : 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kColsumKB == 1 ? 4 : 2)))
 void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restrict__ part_ws) {
     constexpr int KS = D / 16;
     constexpr int RB = 2 * D;                          // bytes per Q row
     constexpr int QT = kRowsPerTile * RB;              // bytes per Q tile
     constexpr int QLOADS = QT / 1024 / kWaves;         // 1 KB loads per wave per tile
     static_assert(QLOADS >= 1, "tile shape");
-    __shared__ __attribute__((aligned(1024))) unsigned char sQ0[QT];
-    __shared__ __attribute__((aligned(1024))) unsigned char sQ1[QT];
+    // The two Q tile buffers; after the loop their bytes hold the per-wave key
+    // sums, which keeps a workgroup at 33 KB of LDS: four fit on a CU, and at 126
+    // VGPRs so do their 16 waves (87.6 against 88.6 us per steady chunk with three).
+    constexpr int RED_BYTES = (int)sizeof(float) * kWaves * 32 * kColsumKB * 33;
+    __shared__ __attribute__((aligned(1024))) unsigned char sQbuf[2 * QT > RED_BYTES ? 2 * QT : RED_BYTES];
+    unsigned char* const sQ0 = sQbuf;
+    unsigned char* const sQ1 = sQbuf + QT;
     __shared__ __attribute__((aligned(16))) float sL0[kRowsPerTile];
     __shared__ __attribute__((aligned(16))) float sL1[kRowsPerTile];
     constexpr int KB = kColsumKB;
-    __shared__ float sRed[kWaves][32 * KB][33];
+    float (*const sRed)[32 * KB][33] = reinterpret_cast<float (*)[32 * KB][33]>(sQbuf);
 
     const int n = a.n, S = a.S, G = a.G;
     const int cache_blocks = (n + kKeysPerBlock - 1) / kKeysPerBlock;
@@ -922,13 +927,13 @@ size_t colsum_workspace_bytes(int B, int Hkv, int NC, int S) {
 }
 
 int colsum_parts(const ChunkArgs& a, int cus) {
-    // Key blocks as whole units of work; 3 workgroups fit on a CU (2 with two key
+    // Key blocks as whole units of work; 4 workgroups fit on a CU (2 with two key
     // blocks per wave).  Take the
     // split that needs the fewest rounds of resident workgroups, counted in
     // whole-block units (ties: the smaller split).
     const long long units = (long long)((a.n + kKeysPerBlock - 1) / kKeysPerBlock +
                                         (a.S + kKeysPerBlock - 1) / kKeysPerBlock) * a.B * a.Hkv;
-    const long long slots = (kColsumKB == 1 ? 3LL : 2LL) * cus;
+    const long long slots = (kColsumKB == 1 ? 4LL : 2LL) * cus;
     int best = 1;
     double best_t = 1e30;
     for (int p = 1; p <= kColsumMaxParts; p *= 2) {
