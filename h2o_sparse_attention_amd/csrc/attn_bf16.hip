@@ -572,17 +572,19 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     constexpr int QT = kRowsPerTile * RB;              // bytes per Q tile
     constexpr int QLOADS = QT / 1024 / kWaves;         // 1 KB loads per wave per tile
     static_assert(QLOADS >= 1, "tile shape");
-    // The two Q tile buffers; after the loop their bytes hold the per-wave key
-    // sums, which keeps a workgroup at 33 KB of LDS: four fit on a CU, and at 126
-    // VGPRs so do their 16 waves (87.6 against 88.6 us per steady chunk with three).
-    constexpr int RED_BYTES = (int)sizeof(float) * kWaves * 32 * kColsumKB * 33;
-    __shared__ __attribute__((aligned(1024))) unsigned char sQbuf[2 * QT > RED_BYTES ? 2 * QT : RED_BYTES];
-    unsigned char* const sQ0 = sQbuf;
-    unsigned char* const sQ1 = sQbuf + QT;
+    // Two separate Q tile buffers (as slices of one array the compiler could not
+    // tell a tile load into one from a read of the other, and waited for the load).
+    // After the loop their bytes hold the per-wave key sums -- waves 0 and 1 in
+    // sQ0, 2 and 3 in sQ1 -- which keeps a workgroup at 33 KB of LDS: four fit on
+    // a CU, and at 126 VGPRs so do their 16 waves.
+    __shared__ __attribute__((aligned(1024))) unsigned char sQ0[QT];
+    __shared__ __attribute__((aligned(1024))) unsigned char sQ1[QT];
+    constexpr int RED_WAVE = 32 * kColsumKB * 33;       // floats of one wave's key sums
+    constexpr bool RED_IN_Q = 2 * RED_WAVE * (int)sizeof(float) <= QT;
+    __shared__ float sRedOwn[RED_IN_Q ? 1 : kWaves * RED_WAVE];
     __shared__ __attribute__((aligned(16))) float sL0[kRowsPerTile];
     __shared__ __attribute__((aligned(16))) float sL1[kRowsPerTile];
     constexpr int KB = kColsumKB;
-    float (*const sRed)[32 * KB][33] = reinterpret_cast<float (*)[32 * KB][33]>(sQbuf);
 
     const int n = a.n, S = a.S, G = a.G;
     const int cache_blocks = (n + kKeysPerBlock - 1) / kKeysPerBlock;
@@ -868,16 +870,19 @@ void colsum_bf16_kernel(ChunkArgs a, uint32_t g_magic, int parts, float* __restr
     }
     publish_lds_loads();
 
+    float* const red = RED_IN_Q ? reinterpret_cast<float*>((wave < 2 ? sQ0 : sQ1) +
+                                                          (wave & 1) * RED_WAVE * sizeof(float))
+                                : sRedOwn + wave * RED_WAVE;
 #pragma unroll
     for (int kbl = 0; kbl < KB; ++kbl)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            sRed[wave][32 * kbl + 8 * (r >> 2) + 4 * hh + (r & 3)][lq] = acc[kbl][r];
+            red[(32 * kbl + 8 * (r >> 2) + 4 * hh + (r & 3)) * 33 + lq] = acc[kbl][r];
     __syncthreads();
     if (lane < 32 * KB) {
         float sum = 0.f;
 #pragma unroll 8
-        for (int j = 0; j < 32; ++j) sum += sRed[wave][lane][j];
+        for (int j = 0; j < 32; ++j) sum += red[lane * 33 + j];
         const int idx = first + lane;
         // Buffer form: a slot the chunk overwrites is not a key (weight 0).
         if (idx < limit) {
