@@ -18,6 +18,7 @@
 
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 namespace h2o {
 namespace {
@@ -246,9 +247,13 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
     constexpr int KS = D / 16, DT = D / 32, RB = 2 * D;
     constexpr int TB = kBwKeysPerTile * RB;            // bytes per K or V tile
     constexpr int LOADS = TB / 1024 / kBwWaves;        // 1 KB loads per wave per tile
-    __shared__ __attribute__((aligned(1024))) unsigned char sK[2][TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sV[2][TB];
-    __shared__ __attribute__((aligned(256))) int sPos[2][kBwKeysPerTile];   // cache tiles
+    // One array per stage: the compiler tells the loads in flight into one
+    // stage from the reads of the other only if they are distinct objects
+    // (reading a slice of an array that loads are filling costs a wait for
+    // every load in flight).
+    __shared__ __attribute__((aligned(1024))) unsigned char sK0[TB], sK1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[TB], sV1[TB];
+    __shared__ __attribute__((aligned(256))) int sPos0[kBwKeysPerTile], sPos1[kBwKeysPerTile];
 
     const int R = a.G * a.S;
     const int nrb = (R + kBwRowsPerBlock - 1) / kBwRowsPerBlock;
@@ -303,7 +308,10 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
     auto tile_valid = [&](int jt) {
         return min(kBwKeysPerTile, (jt < cache_tiles ? n : S) - tile_first(jt));
     };
-    auto issue = [&](int stage, int jt) {
+    auto issue = [&](auto stage_c, int jt) {
+        constexpr int stage = decltype(stage_c)::value;
+        unsigned char* dk_ = stage ? sK1 : sK0;
+        unsigned char* dv_ = stage ? sV1 : sV0;
         const bool cache = jt < cache_tiles;
         const int first = tile_first(jt), valid = tile_valid(jt);
         const Rsrc rk = make_rsrc((cache ? Kc : Kn) + (size_t)first * D, valid * RB);
@@ -313,11 +321,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
             const int off = (it * kBwWaves + wave) * 1024 + 16 * lane;
             const int r = off / RB, cp = (off % RB) / 16;
             const int go = r * RB + 16 * (cp ^ swz_k<D>(r));
-            lds16(rk, &sK[stage][(it * kBwWaves + wave) * 1024], go);
-            lds16(rv, &sV[stage][(it * kBwWaves + wave) * 1024], go);
+            lds16(rk, dk_ + (it * kBwWaves + wave) * 1024, go);
+            lds16(rv, dv_ + (it * kBwWaves + wave) * 1024, go);
         }
         if (cache && wave == 0)
-            lds4(make_rsrc(a.pos + (size_t)bg * a.NC + first, valid * 4), &sPos[stage][0],
+            lds4(make_rsrc(a.pos + (size_t)bg * a.NC + first, valid * 4), stage ? sPos1 : sPos0,
                  4 * lane);
     };
     // A operand rows: physical key perm_key(lq) (+32 per sub-tile), k-step ks.
@@ -330,22 +338,36 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x16{};
 
-    issue(0, 0);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    // Exclusion bits (buffer form) are loaded one tile ahead, so the wait that
+    // ends each iteration covers them: a wait for them in the iteration that
+    // uses them would also wait for the tile loads issued before (vmcnt counts
+    // in order).
+    auto tile_ex = [&](int jt) {
+        return (jt < cache_tiles && exrow != nullptr) ? exrow[jt] : 0ull;
+    };
+    uint64_t ex_next = tile_ex(0);
+    issue(S0{}, 0);
     publish();
-    for (int jt = 0; jt < ntiles; ++jt) {
-        const int stage = jt & 1;
-        if (jt + 1 < ntiles) issue(stage ^ 1, jt + 1);
-        const unsigned char* tk = sK[stage];
-        const unsigned char* tv = sV[stage];
+    // Tile jt sits in stage jt & 1; the loop runs two tiles per trip so that
+    // each body names its stages at compile time.
+    auto body = [&](auto stage_c, int jt) {
+        constexpr int stage = decltype(stage_c)::value;
+        if (jt + 1 < ntiles) issue(std::integral_constant<int, stage ^ 1>{}, jt + 1);
+        const uint64_t ex = ex_next;
+        ex_next = tile_ex(jt + 1);
+        const unsigned char* tk = stage ? sK1 : sK0;
+        const unsigned char* tv = stage ? sV1 : sV0;
+        const int* tpos = stage ? sPos1 : sPos0;
         const bool cache = jt < cache_tiles;
         const int first = tile_first(jt), valid = tile_valid(jt);
-        const uint64_t ex = (cache && exrow != nullptr) ? exrow[jt] : 0ull;
         // keys k of the tile with k > lim are not visible to this lane's row
         const int lim = cache ? valid - 1 : min(valid - 1, i - first);
         // Cache keys whose position lies outside [0, P) are visible iff
         // 0 <= t(j) <= P + i (none in a cache built by this library's insertions).
-        const bool irr = cache && __ballot(lane < valid && (sPos[stage][lane] < 0 ||
-                                                           sPos[stage][lane] >= a.P)) != 0;
+        const bool irr = cache && __ballot(lane < valid && (tpos[lane] < 0 ||
+                                                           tpos[lane] >= a.P)) != 0;
         const bool all_vis = ex == 0 && !irr && valid == kBwKeysPerTile &&
                              (cache || first + kBwKeysPerTile - 1 <= i_wave_min);
         const uint32_t lb = __builtin_amdgcn_perm((uint32_t)(ex >> 32), (uint32_t)ex,
@@ -376,7 +398,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
             if (irr) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int tp = sPos[stage][32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7)];
+                    const int tp = tpos[32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7)];
                     if (tp < 0 || tp > a.P + i) stv[r] = -INFINITY;
                 }
             }
@@ -442,6 +464,10 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma32(ktr[dt][s2], dsb1[s2], o[dt]);
         publish();
+    };
+    for (int jt = 0; jt < ntiles; jt += 2) {
+        body(S0{}, jt);
+        if (jt + 1 < ntiles) body(S1{}, jt + 1);
     }
     if (!row_ok) return;
     // o[dt][r] = dQ^T[d = 32dt + 8(r/4) + 4hh + r%4][row lq]
@@ -479,10 +505,11 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
     constexpr int TB = kBwRowsPerTile * RB;
     constexpr int LOADS = TB / 1024 / kBwWaves;
     constexpr int ROWS_PER_LOAD = 4096 / RB;
-    __shared__ __attribute__((aligned(1024))) unsigned char sQ[2][TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sD[2][TB];
-    __shared__ __attribute__((aligned(16))) float sL[2][kBwRowsPerTile];
-    __shared__ __attribute__((aligned(16))) float sR[2][kBwRowsPerTile];
+    // One array per stage (as in the dQ kernel).
+    __shared__ __attribute__((aligned(1024))) unsigned char sQ0[TB], sQ1[TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sD0[TB], sD1[TB];
+    __shared__ __attribute__((aligned(16))) float sL0[kBwRowsPerTile], sL1[kBwRowsPerTile];
+    __shared__ __attribute__((aligned(16))) float sR0[kBwRowsPerTile], sR1[kBwRowsPerTile];
 
     const int n = a.n, S = a.S, G = a.G;
     const int cache_blocks = (n + kBwKeysPerBlock - 1) / kBwKeysPerBlock;
@@ -543,7 +570,10 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
     };
     const int rl_base = (wave * 1024 + 16 * lane) / RB;
     const int cp = (16 * lane % RB) / 16;
-    auto issue = [&](int stage, int rt) {
+    auto issue = [&](auto stage_c, int rt) {
+        constexpr int stage = decltype(stage_c)::value;
+        unsigned char* dq_ = stage ? sQ1 : sQ0;
+        unsigned char* dd_ = stage ? sD1 : sD0;
         const Rsrc rq = make_rsrc(Qg, q_bytes), rd = make_rsrc(Dg, q_bytes);
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
@@ -552,16 +582,16 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
             int hl = 0, ipos = 0;
             row_split(min(r, R - 1), hl, ipos);
             const int off = r < R ? ((hl * S + ipos) * D) * 2 + 16 * (cp ^ swz_k<D>(rl)) : q_bytes;
-            lds16(rq, &sQ[stage][(it * kBwWaves + wave) * 1024], off);
-            lds16(rd, &sD[stage][(it * kBwWaves + wave) * 1024], off);
+            lds16(rq, dq_ + (it * kBwWaves + wave) * 1024, off);
+            lds16(rd, dd_ + (it * kBwWaves + wave) * 1024, off);
         }
         if (wave == 0) {
             const int r = rt * kBwRowsPerTile + lane;
             int hl = 0, ipos = 0;
             row_split(min(r, R - 1), hl, ipos);
             const int off = r < R ? (hl * S + ipos) * 4 : G * S * 4;
-            lds4(make_rsrc(Lg, G * S * 4), &sL[stage][0], off);
-            lds4(make_rsrc(Rg, G * S * 4), &sR[stage][0], off);
+            lds4(make_rsrc(Lg, G * S * 4), stage ? sL1 : sL0, off);
+            lds4(make_rsrc(Rg, G * S * 4), stage ? sR1 : sR0, off);
         }
     };
     const float c = a.sm_scale * kLog2e;
@@ -577,13 +607,19 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
         dv[dt] = f32x16{};
     }
     const int kmax = min(first + 31, limit - 1);
-    issue(0, t_lo);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    issue(S0{}, t_lo);
     publish();
-    for (int rt = t_lo; rt < t_hi; ++rt) {
-        const int stage = (rt - t_lo) & 1;
-        if (rt + 1 < t_hi) issue(stage ^ 1, rt + 1);
-        const unsigned char* tq = sQ[stage];
-        const unsigned char* td = sD[stage];
+    // Tile rt sits in stage (rt - t_lo) & 1; the loop runs two tiles per trip
+    // so that each body names its stages at compile time.
+    auto body = [&](auto stage_c, int rt) {
+        constexpr int stage = decltype(stage_c)::value;
+        if (rt + 1 < t_hi) issue(std::integral_constant<int, stage ^ 1>{}, rt + 1);
+        const unsigned char* tq = stage ? sQ1 : sQ0;
+        const unsigned char* td = stage ? sD1 : sD0;
+        const float* tl = stage ? sL1 : sL0;
+        const float* tr = stage ? sR1 : sR0;
         // The two 32-row sub-tiles are pipelined inside the wave (one wave per
         // SIMD): sub-tile 0's exponentials and dS run under sub-tile 1's S and dP
         // MFMAs, sub-tile 1's under sub-tile 0's dV and dK MFMAs.
@@ -615,8 +651,8 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rl = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-                const float lr = sL[stage][rl];
-                drv[r] = sR[stage][rl];
+                const float lr = tl[rl];
+                drv[r] = tr[rl];
                 l2v[r] = (rows_in || rt * kBwRowsPerTile + rl < R) ? lr * kLog2e : INFINITY;
             }
         };
@@ -710,6 +746,10 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
                 dk[dt] = mfma32(db1[s2], qtr[dt][s2], dk[dt]);
             }
         publish();
+    };
+    for (int rt = t_lo; rt < t_hi; rt += 2) {
+        body(S0{}, rt);
+        if (rt + 1 < t_hi) body(S1{}, rt + 1);
     }
     // dk[dt][r] = dK[key first + 8(r/4) + 4hh + r%4][d = 32dt + lq]
     float* dkb = is_cache ? dk_cache + (size_t)bg * a.NC * D : dk_new + (size_t)bg * S * D;

@@ -10,7 +10,12 @@ so each product carries up to about 2^-8 relative error; ds sums to zero along
 each row, so a per-element relative bound is meaningless for dQ.  The bound is
 per tensor: max |err| <= 1e-2 * max|ref| and relative L2 <= 5e-3 (1.3 x 2^-8;
 the errors of independent terms partly cancel, about 1.7e-3 is typical).
+
+The workspace is filled with NaN bytes first, so a value the kernels read from
+it without having written it shows up as NaN in the gradients.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -36,6 +41,14 @@ def _dout(wl, S, seed):
     return W.synth.bf16_round(x) if wl.dtype == "bf16" else x
 
 
+def _workspace(wl, S):
+    d = H.dims_of(wl).c()
+    ws = torch.empty(int(h2o.lib.h2o_backward_workspace_bytes(ctypes.byref(d), S)),
+                     dtype=torch.uint8, device=H.DEV)
+    ws.fill_(255)
+    return ws
+
+
 def check_backward(wl, st, x, seed=0, freed=None, where=""):
     """Forward on the GPU from oracle state ``st``, then the backward, against the oracle."""
     dt = H.TORCH_DT[wl.dtype]
@@ -51,7 +64,7 @@ def check_backward(wl, st, x, seed=0, freed=None, where=""):
         out, lse, _, _ = h2o.buffer_attn(cache, P, q, k, v, fr, wl.sm_scale, summed_weights=False)
     dout_np = _dout(wl, S, seed)
     got = h2o.chunk_attn_backward(cache, P, q, k, v, out, lse, H.dev(dout_np, dt), wl.sm_scale,
-                                  freed_slots=fr)
+                                  freed_slots=fr, workspace=_workspace(wl, S))
     torch.cuda.synchronize()
     excl = None
     if freed is not None:
