@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -125,6 +126,31 @@ hipError_t cu_count(int* cus) {
     }
     *cus = cached[dev];
     return hipSuccess;
+}
+
+// One SideStream per device, made at its first use; the lock is held from the
+// fork to the join of a call, so calls from several host threads do not mix
+// their forks on one device.
+std::mutex& side_stream_lock() {
+    static std::mutex mu;
+    return mu;
+}
+// Caller holds side_stream_lock().  nullptr if the stream or events cannot be
+// made (the call then runs its launches on the caller's stream alone).
+const SideStream* side_stream() {
+    static SideStream side[64];
+    static bool tried[64] = {false};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    if (!tried[dev]) {
+        tried[dev] = true;
+        SideStream t;
+        if (hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&t.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&t.join, hipEventDisableTiming) == hipSuccess)
+            side[dev] = t;
+    }
+    return side[dev].join != nullptr ? &side[dev] : nullptr;
 }
 
 // Workspace layout of a non-decode chunk: the split summed-weights partials
@@ -460,14 +486,9 @@ h2o_status_t h2o_chunk_attn_backward(const h2o_dims_t* dims, const h2o_cache_t* 
     timer_begin(H2O_KERNEL_BACKWARD, s);
     const size_t cstride = (size_t)a.NC * a.D, nstride = (size_t)a.S * a.D;
     if (parts == 2) {
-        if ((st = check_hip(launch_zero_f32(dk_cache, cstride, cstride, rows, 0, s),
-                            "zero dk")) != H2O_OK ||
-            (st = check_hip(launch_zero_f32(dv_cache, cstride, cstride, rows, 0, s),
-                            "zero dv")) != H2O_OK ||
-            (st = check_hip(launch_zero_f32(dk_new, nstride, nstride, rows, 0, s),
-                            "zero dk_new")) != H2O_OK ||
-            (st = check_hip(launch_zero_f32(dv_new, nstride, nstride, rows, 0, s),
-                            "zero dv_new")) != H2O_OK)
+        float* const bufs[4] = {dk_cache, dv_cache, dk_new, dv_new};
+        const size_t counts[4] = {cstride * rows, cstride * rows, nstride * rows, nstride * rows};
+        if ((st = check_hip(launch_zero_f32_list(bufs, counts, 4, s), "zero dk, dv")) != H2O_OK)
             return st;
     } else if (a.n < a.NC) {
         const size_t per = (size_t)(a.NC - a.n) * a.D;
@@ -477,11 +498,14 @@ h2o_status_t h2o_chunk_attn_backward(const h2o_dims_t* dims, const h2o_cache_t* 
                             "zero dv tail")) != H2O_OK)
             return st;
     }
-    hipError_t e = dims->dtype == H2O_BF16
-                       ? launch_backward_bf16(a, out, dout, drow, dq, dk_new, dv_new, dk_cache,
-                                              dv_cache, parts, s)
-                       : launch_backward_f32(a, out, dout, drow, dq, dk_new, dv_new, dk_cache,
-                                             dv_cache, s);
+    hipError_t e;
+    if (dims->dtype == H2O_BF16) {
+        std::lock_guard<std::mutex> lock(side_stream_lock());
+        e = launch_backward_bf16(a, out, dout, drow, dq, dk_new, dv_new, dk_cache, dv_cache, parts,
+                                 s, side_stream());
+    } else {
+        e = launch_backward_f32(a, out, dout, drow, dq, dk_new, dv_new, dk_cache, dv_cache, s);
+    }
     timer_end(H2O_KERNEL_BACKWARD, s);
     if ((st = check_hip(e, "backward launch")) != H2O_OK) return st;
     return ok();

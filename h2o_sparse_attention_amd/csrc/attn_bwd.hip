@@ -819,7 +819,8 @@ int backward_dkdv_parts(const ChunkArgs& a, int cus) {
 
 hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void* dout,
                                 float* drow, float* dq, float* dk_new, float* dv_new,
-                                float* dk_cache, float* dv_cache, int parts, hipStream_t s) {
+                                float* dk_cache, float* dv_cache, int parts, hipStream_t s,
+                                const SideStream* side) {
     const int rows = a.B * a.Hq * a.S;
     hipLaunchKernelGGL(rowdot_kernel<u16>, dim3((rows + 15) / 16), dim3(256), 0, s,
                        static_cast<const u16*>(out), static_cast<const u16*>(dout), drow, rows,
@@ -830,16 +831,36 @@ hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void*
                     (a.S + kBwKeysPerBlock - 1) / kBwKeysPerBlock;
     const uint32_t magic = a.G > 1 ? (uint32_t)((0x100000000ull + a.G - 1) / a.G) : 0u;
     const dim3 gq(xcd_grid(nrb * a.B * a.Hkv)), gk(xcd_grid(nkb * a.B * a.Hkv * parts));
-    if (a.D == 128) {
-        hipLaunchKernelGGL(bwd_dq_bf16_kernel<128>, gq, dim3(kBwThreads), 0, s, a, drow, dO, dq);
+    // The two kernels write disjoint outputs and each holds one workgroup per
+    // CU.  Side by side, the dQ kernel's long workgroups (one round) fill the
+    // CUs that the dK/dV kernel's last, partial round leaves idle.  dK/dV is
+    // enqueued first, on the caller's stream.
+    hipStream_t sq = s;
+    if (side != nullptr) {
+        hipError_t e = hipEventRecord(side->fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+        if (e != hipSuccess) return e;
+        sq = side->s;
+    }
+    if (a.D == 128)
         hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<128>, gk, dim3(kBwThreads), 0, s, a, drow, dO,
                            magic, parts, dk_new, dv_new, dk_cache, dv_cache);
-    } else {
-        hipLaunchKernelGGL(bwd_dq_bf16_kernel<64>, gq, dim3(kBwThreads), 0, s, a, drow, dO, dq);
+    else
         hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<64>, gk, dim3(kBwThreads), 0, s, a, drow, dO,
                            magic, parts, dk_new, dv_new, dk_cache, dv_cache);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.D == 128)
+        hipLaunchKernelGGL(bwd_dq_bf16_kernel<128>, gq, dim3(kBwThreads), 0, sq, a, drow, dO, dq);
+    else
+        hipLaunchKernelGGL(bwd_dq_bf16_kernel<64>, gq, dim3(kBwThreads), 0, sq, a, drow, dO, dq);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (side != nullptr) {
+        e = hipEventRecord(side->join, side->s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
     }
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace h2o

@@ -53,6 +53,25 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, int pe
     for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < per_row; j += step) row[j] = 0.f;
 }
 
+// Up to four whole buffers in one launch (blockIdx.y picks the buffer).
+struct ZeroList {
+    float* p[4];
+    size_t n[4];
+};
+__global__ __launch_bounds__(256) void zero_list_kernel(ZeroList z) {
+    float* p = z.p[blockIdx.y];
+    const size_t n = z.n[blockIdx.y];
+    const size_t step = (size_t)gridDim.x * blockDim.x;
+    const size_t first = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (((reinterpret_cast<uintptr_t>(p) & 15u) | (uintptr_t)(n & 3)) == 0) {
+        float4* p4 = reinterpret_cast<float4*>(p);
+        const float4 zero = {0.f, 0.f, 0.f, 0.f};
+        for (size_t j = first; j < n / 4; j += step) p4[j] = zero;
+        return;
+    }
+    for (size_t j = first; j < n; j += step) p[j] = 0.f;
+}
+
 // ------------------------------------------------------------------ select
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -501,6 +520,22 @@ hipError_t launch_zero_f32(float* p, size_t per_row, size_t stride, int rows, si
     if (bx > 256) bx = 256;
     hipLaunchKernelGGL(zero_kernel, dim3(bx, rows), dim3(256), 0, s, p, (int)per_row, stride,
                        offset);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32_list(float* const* p, const size_t* n, int count, hipStream_t s) {
+    if (count < 1 || count > 4) return hipErrorInvalidValue;
+    ZeroList z;
+    size_t most = 0;
+    for (int i = 0; i < 4; ++i) {
+        z.p[i] = i < count ? p[i] : p[0];
+        z.n[i] = i < count ? n[i] : 0;
+        most = z.n[i] > most ? z.n[i] : most;
+    }
+    if (most == 0) return hipSuccess;
+    int bx = (int)((most + 1023) / 1024);
+    if (bx > 512) bx = 512;
+    hipLaunchKernelGGL(zero_list_kernel, dim3(bx, count), dim3(256), 0, s, z);
     return hipGetLastError();
 }
 

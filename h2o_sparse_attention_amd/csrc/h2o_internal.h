@@ -61,6 +61,8 @@ hipError_t launch_attn_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_colsum_f32(const ChunkArgs& a, hipStream_t s);
 hipError_t launch_zero_f32(float* p, size_t count_per_row, size_t row_stride, int rows,
                            size_t offset, hipStream_t s);
+// Zero count (1..4) whole buffers of n[i] floats in one launch.
+hipError_t launch_zero_f32_list(float* const* p, const size_t* n, int count, hipStream_t s);
 hipError_t launch_update_scores(float* score, const float* cs, int rows, int NC, int n,
                                 hipStream_t s);
 hipError_t launch_select(const EvictArgs& a, hipStream_t s);
@@ -78,9 +80,19 @@ hipError_t launch_backward_f32(const ChunkArgs& a, const void* out, const void* 
 // Row parts (1 or 2) of the bf16 dK/dV kernel for `cus` compute units; with 2
 // the dK/dV outputs must be zero before the launch.
 int backward_dkdv_parts(const ChunkArgs& a, int cus);
+// A second stream of a device (default priority) and two events, to run
+// independent launches of one call side by side: `fork` is recorded on the
+// caller's stream and waited for by `s`; `join` the other way round.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+// side != nullptr: the dQ kernel runs on side->s beside the dK/dV kernel (the
+// caller serialises the use of one SideStream).
 hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void* dout,
                                 float* drow, float* dq, float* dk_new, float* dv_new,
-                                float* dk_cache, float* dv_cache, int parts, hipStream_t s);
+                                float* dk_cache, float* dv_cache, int parts, hipStream_t s,
+                                const SideStream* side = nullptr);
 
 // Compute units of the current device (api.hip), read once per device.
 hipError_t cu_count(int* cus);
