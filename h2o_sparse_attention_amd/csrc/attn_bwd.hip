@@ -33,11 +33,15 @@ __device__ __forceinline__ bool excluded(const ChunkArgs& a, int bg, int slot) {
            ((a.excl[(size_t)bg * excl_tiles(a.NC) + slot / 64] >> (slot % 64)) & 1);
 }
 
-// D_i = dO_i . O_i: 16 lanes per row, 8 elements per lane per step.
+// D_i = dO_i . O_i: 16 lanes per row, 8 elements per lane per step.  With
+// lse2 != nullptr also lse2_i = lse_i * log2(e), the row's log-sum-exp in the
+// units of the exponentials (read once per row instead of scaled per pair).
 template <typename T>
 __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o,
                                                      const T* __restrict__ dout,
-                                                     float* __restrict__ drow, int rows, int D) {
+                                                     float* __restrict__ drow,
+                                                     const float* __restrict__ lse,
+                                                     float* __restrict__ lse2, int rows, int D) {
     const int row = blockIdx.x * 16 + threadIdx.x / 16;
     const int l = threadIdx.x % 16;
     float acc = 0.f;
@@ -48,7 +52,10 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o,
     }
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-    if (row < rows && l == 0) drow[row] = acc;
+    if (row < rows && l == 0) {
+        drow[row] = acc;
+        if (lse2 != nullptr) lse2[row] = lse[row] * kLog2e;
+    }
 }
 
 // ------------------------------------------------------------------ f32 path
@@ -221,10 +228,10 @@ __device__ __forceinline__ bf16x8 ld_tr(const unsigned char* p0, const unsigned 
     return as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 // Byte offset, in a row-major tile of RB-byte rows whose 16-byte chunks are
-// XOR-swizzled by swz_k, of row r, 16-byte chunk c, 8-byte half h.
+// XOR-swizzled by swz_kt, of row r, 16-byte chunk c, 8-byte half h.
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int c, int h) {
-    return r * (2 * D) + 16 * (c ^ swz_k<D>(r)) + 8 * h;
+    return r * (2 * D) + 16 * (c ^ swz_kt<D>(r)) + 8 * h;
 }
 // This lane's two transposed-read offsets for rows 8hh..8hh+7 (plus a multiple
 // of 16) and columns 32*dt + lq: XOR 64*dt selects dt, adding 16*RB moves 16 rows.
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
         for (int it = 0; it < LOADS; ++it) {
             const int off = (it * kBwWaves + wave) * 1024 + 16 * lane;
             const int r = off / RB, cp = (off % RB) / 16;
-            const int go = r * RB + 16 * (cp ^ swz_k<D>(r));
+            const int go = r * RB + 16 * (cp ^ swz_kt<D>(r));
             lds16(rk, dk_ + (it * kBwWaves + wave) * 1024, go);
             lds16(rv, dv_ + (it * kBwWaves + wave) * 1024, go);
         }
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
     };
     // A operand rows: physical key perm_key(lq) (+32 per sub-tile), k-step ks.
     const int prow = perm_key(lq);
-    const int kb = prow * RB + 16 * (hh ^ swz_k<D>(prow));
+    const int kb = prow * RB + 16 * (hh ^ swz_kt<D>(prow));
     int t0, t1;
     tr_offsets<D>(lane, t0, t1);
 
@@ -498,9 +505,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
 // 2.25 rounds of work; halves take 2.5.)
 template <int D>
 __global__ __launch_bounds__(kBwThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint32_t g_magic,
-                          int parts, float* dk_new, float* dv_new, float* dk_cache,
-                          float* dv_cache) {
+void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, const u16* dout,
+                          uint32_t g_magic, int parts, float* dk_new, float* dv_new,
+                          float* dk_cache, float* dv_cache) {
     constexpr int KS = D / 16, DT = D / 32, RB = 2 * D;
     constexpr int TB = kBwRowsPerTile * RB;
     constexpr int LOADS = TB / 1024 / kBwWaves;
@@ -561,7 +568,7 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
     if (t_lo >= t_hi) return;                 // nothing to add (parts > 1 only)
     const u16* Qg = static_cast<const u16*>(a.q) + (size_t)(b * a.Hq + g * G) * S * D;
     const u16* Dg = dout + (size_t)(b * a.Hq + g * G) * S * D;
-    const float* Lg = a.lse + (size_t)(b * a.Hq + g * G) * S;
+    const float* Lg = lse2 + (size_t)(b * a.Hq + g * G) * S;
     const float* Rg = drow + (size_t)(b * a.Hq + g * G) * S;
     const int q_bytes = G * S * D * 2;
     auto row_split = [&](int r, int& hl, int& ipos) {
@@ -581,7 +588,7 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
             const int r = rt * kBwRowsPerTile + rl;
             int hl = 0, ipos = 0;
             row_split(min(r, R - 1), hl, ipos);
-            const int off = r < R ? ((hl * S + ipos) * D) * 2 + 16 * (cp ^ swz_k<D>(rl)) : q_bytes;
+            const int off = r < R ? ((hl * S + ipos) * D) * 2 + 16 * (cp ^ swz_kt<D>(rl)) : q_bytes;
             lds16(rq, dq_ + (it * kBwWaves + wave) * 1024, off);
             lds16(rd, dd_ + (it * kBwWaves + wave) * 1024, off);
         }
@@ -596,7 +603,7 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
     };
     const float c = a.sm_scale * kLog2e;
     const int prow = perm_key(lq);
-    const int qb = prow * RB + 16 * (hh ^ swz_k<D>(prow));
+    const int qb = prow * RB + 16 * (hh ^ swz_kt<D>(prow));
     int t0, t1;
     tr_offsets<D>(lane, t0, t1);
 
@@ -643,17 +650,17 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
                     qtr[dt][s2] = ld_tr(tq + o0, tq + o1);
                 }
         };
-        const bool rows_in = rt * kBwRowsPerTile + kBwRowsPerTile <= R;
-        // log2-scaled LSE (+inf past the last row: weight 0) and D of the lane's
-        // rows 32*sub + 16*(r/8) + 8*hh + r%8; read unconditionally (in LDS bounds).
+        // log2-scaled LSE and D of the lane's rows 32*sub + 16*(r/8) + 8*hh + r%8.
+        // Rows past the last read zeros (out-of-range loads), and so do their Q
+        // and dO: the weight exp2(0) = 1 multiplies dO = 0 and dS = 1 * (0 - 0)
+        // multiplies Q = 0, so those rows add nothing.
         float l2v[16], drv[16];
         auto read_ld = [&](int sub) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rl = 32 * sub + 16 * (r >> 3) + 8 * hh + (r & 7);
-                const float lr = tl[rl];
+                l2v[r] = tl[rl];
                 drv[r] = tr[rl];
-                l2v[r] = (rows_in || rt * kBwRowsPerTile + rl < R) ? lr * kLog2e : INFINITY;
             }
         };
         // Chunk keys near the diagonal: -inf for this lane's key at rows before it;
@@ -779,6 +786,10 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const u16* dout, uint3
 }  // namespace
 
 size_t backward_workspace_bytes(int B, int Hq, int S) {
+    return 2 * backward_lse2_offset(B, Hq, S);
+}
+
+size_t backward_lse2_offset(int B, int Hq, int S) {
     return ((size_t)B * Hq * S * sizeof(float) + 255) / 256 * 256;
 }
 
@@ -788,7 +799,8 @@ hipError_t launch_backward_f32(const ChunkArgs& a, const void* out, const void* 
     const int rows = a.B * a.Hq * a.S;
     hipLaunchKernelGGL(rowdot_kernel<float>, dim3((rows + 15) / 16), dim3(256), 0, s,
                        static_cast<const float*>(out), static_cast<const float*>(dout), drow,
-                       rows, a.D);
+                       static_cast<const float*>(nullptr), static_cast<float*>(nullptr), rows,
+                       a.D);
     const float* dO = static_cast<const float*>(dout);
     const int nrb = (a.G * a.S + kItems - 1) / kItems;
     const int nkb = (a.n + a.S + kItems - 1) / kItems;
@@ -822,9 +834,11 @@ hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void*
                                 float* dk_cache, float* dv_cache, int parts, hipStream_t s,
                                 const SideStream* side) {
     const int rows = a.B * a.Hq * a.S;
+    // lse * log2(e) per row, for the dK/dV kernel, after D in the workspace
+    float* lse2 = drow + backward_lse2_offset(a.B, a.Hq, a.S) / sizeof(float);
     hipLaunchKernelGGL(rowdot_kernel<u16>, dim3((rows + 15) / 16), dim3(256), 0, s,
-                       static_cast<const u16*>(out), static_cast<const u16*>(dout), drow, rows,
-                       a.D);
+                       static_cast<const u16*>(out), static_cast<const u16*>(dout), drow,
+                       static_cast<const float*>(a.lse), lse2, rows, a.D);
     const u16* dO = static_cast<const u16*>(dout);
     const int nrb = (a.G * a.S + kBwRowsPerBlock - 1) / kBwRowsPerBlock;
     const int nkb = (a.n + kBwKeysPerBlock - 1) / kBwKeysPerBlock +
@@ -843,11 +857,11 @@ hipError_t launch_backward_bf16(const ChunkArgs& a, const void* out, const void*
         sq = side->s;
     }
     if (a.D == 128)
-        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<128>, gk, dim3(kBwThreads), 0, s, a, drow, dO,
-                           magic, parts, dk_new, dv_new, dk_cache, dv_cache);
+        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<128>, gk, dim3(kBwThreads), 0, s, a, drow, lse2,
+                           dO, magic, parts, dk_new, dv_new, dk_cache, dv_cache);
     else
-        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<64>, gk, dim3(kBwThreads), 0, s, a, drow, dO,
-                           magic, parts, dk_new, dv_new, dk_cache, dv_cache);
+        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<64>, gk, dim3(kBwThreads), 0, s, a, drow, lse2,
+                           dO, magic, parts, dk_new, dv_new, dk_cache, dv_cache);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.D == 128)

@@ -84,6 +84,13 @@ template <int D>
 __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+// For tiles read both ways (the backward's Q, dO and K): swz_k ^ swz_v.  Over
+// 16 consecutive rows it still takes every value once (x = 4a + b maps to
+// 4(a ^ b) + b), as the row reads need; and over 4 consecutive rows its bits
+// 2-3 (D = 128; bit 2 over rows two apart, D = 64) still differ, as the
+// transposed reads need.
+template <int D>
+__device__ __forceinline__ int swz_kt(int r) { return swz_k<D>(r) ^ swz_v<D>(r); }
 
 // Eviction order keys: scores map to uint32 keys whose unsigned order is the
 // float order; slots that may not be evicted take the top two codes.

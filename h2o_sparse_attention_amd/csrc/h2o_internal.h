@@ -72,8 +72,10 @@ hipError_t launch_insert(const EvictArgs& a, hipStream_t s);
 // k = 1 and S = 1 (decode on a full cache): selection and insertion in one launch.
 hipError_t launch_select1_insert(const EvictArgs& a, hipStream_t s);
 
-// Backward of the chunk attention (fp32 gradients).  drow: B*Hq*S floats.
+// Backward of the chunk attention (fp32 gradients).  Workspace: D per row
+// (drow, B*Hq*S floats), then at backward_lse2_offset the rows' lse * log2(e).
 size_t backward_workspace_bytes(int B, int Hq, int S);
+size_t backward_lse2_offset(int B, int Hq, int S);
 hipError_t launch_backward_f32(const ChunkArgs& a, const void* out, const void* dout,
                                float* drow, float* dq, float* dk_new, float* dv_new,
                                float* dk_cache, float* dv_cache, hipStream_t s);
