@@ -382,13 +382,14 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
         // The two 32-key sub-tiles are pipelined inside the wave (one wave per SIMD):
         // sub-tile 0's dS runs under sub-tile 1's S and dP MFMAs, sub-tile 1's under
         // sub-tile 0's dQ MFMAs.  Invisible keys get score -inf (weight 0) first.
-        auto read_kv = [&](int sub, bf16x8 (&ka)[KS], bf16x8 (&va)[KS]) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int ob = (kb ^ (32 * ks)) + sub * 32 * RB;
-                ka[ks] = as_bf16x8(ld16(tk + ob));
-                va[ks] = as_bf16x8(ld16(tv + ob));
-            }
+        // K and V rows of k-step ks of a sub-tile (the A operands of S^T and
+        // dP^T).  They are read two k-steps ahead of their MFMAs through a ring
+        // of three: all KS at once held 64 more registers per sub-tile, and the
+        // pressure moved the S and dP tiles through AGPRs (copies per value).
+        auto kv_at = [&](int sub, int ks, bf16x8& ka, bf16x8& va) {
+            const int ob = (kb ^ (32 * ks)) + sub * 32 * RB;
+            ka = as_bf16x8(ld16(tk + ob));
+            va = as_bf16x8(ld16(tv + ob));
         };
         auto ktr_of = [&](int sub, int dt, int s2) {
             const int rows = (sub * 32 + 16 * s2) * RB;
@@ -417,17 +418,20 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
                                         pack2(v[8 * s2 + 4], v[8 * s2 + 5]), pack2(v[8 * s2 + 6], v[8 * s2 + 7])});
         };
         // A: sub-tile 0's S and dP.
-        bf16x8 ka0[KS], va0[KS];
-        read_kv(0, ka0, va0);
-        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 kw[3], vw[3];
+        kv_at(0, 0, kw[0], vw[0]);
+        kv_at(0, 1, kw[1], vw[1]);
         f32x16 st0 = f32x16{}, dp0 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            st0 = mfma32(ka0[ks], qf[ks], st0);
-            dp0 = mfma32(va0[ks], df[ks], dp0);
+            if (ks + 2 < KS) kv_at(0, ks + 2, kw[(ks + 2) % 3], vw[(ks + 2) % 3]);
+            st0 = mfma32(kw[ks % 3], qf[ks], st0);
+            dp0 = mfma32(vw[ks % 3], df[ks], dp0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        bf16x8 ka1[KS], va1[KS], ktr[DT][2];
-        read_kv(1, ka1, va1);
+        bf16x8 ktr[DT][2];
+        kv_at(1, 0, kw[0], vw[0]);
+        kv_at(1, 1, kw[1], vw[1]);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -439,8 +443,9 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
         f32x16 st1 = f32x16{}, dp1 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            st1 = mfma32(ka1[ks], qf[ks], st1);
-            dp1 = mfma32(va1[ks], df[ks], dp1);
+            if (ks + 2 < KS) kv_at(1, ks + 2, kw[(ks + 2) % 3], vw[(ks + 2) % 3]);
+            st1 = mfma32(kw[ks % 3], qf[ks], st1);
+            dp1 = mfma32(vw[ks % 3], df[ks], dp1);
 #pragma unroll
             for (int r = 16 * ks / KS; r < 16 * (ks + 1) / KS; ++r)
                 dsv[r] = fast_exp2(fmaf(st0[r], c, -lse2)) * (dp0[r] - Di);
@@ -630,13 +635,13 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
         // The two 32-row sub-tiles are pipelined inside the wave (one wave per
         // SIMD): sub-tile 0's exponentials and dS run under sub-tile 1's S and dP
         // MFMAs, sub-tile 1's under sub-tile 0's dV and dK MFMAs.
-        auto read_qd = [&](int sub, bf16x8 (&qa)[KS], bf16x8 (&da)[KS]) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int ob = (qb ^ (32 * ks)) + sub * 32 * RB;
-                qa[ks] = as_bf16x8(ld16(tq + ob));
-                da[ks] = as_bf16x8(ld16(td + ob));
-            }
+        // Q and dO rows of k-step ks of a sub-tile (the A operands of S and dP),
+        // read two k-steps ahead of their MFMAs through a ring of three (as in
+        // the dQ kernel).
+        auto qd_at = [&](int sub, int ks, bf16x8& qa, bf16x8& da) {
+            const int ob = (qb ^ (32 * ks)) + sub * 32 * RB;
+            qa = as_bf16x8(ld16(tq + ob));
+            da = as_bf16x8(ld16(td + ob));
         };
         // The transposed operands of dV and dK for one sub-tile.
         auto read_tr = [&](int sub, bf16x8 (&dtr)[DT][2], bf16x8 (&qtr)[DT][2]) {
@@ -689,17 +694,20 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
         };
 
         // A: sub-tile 0's S and dP.
-        bf16x8 qa0[KS], da0[KS];
-        read_qd(0, qa0, da0);
-        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 qw[3], dw[3];
+        qd_at(0, 0, qw[0], dw[0]);
+        qd_at(0, 1, qw[1], dw[1]);
         f32x16 st0 = f32x16{}, dp0 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            st0 = mfma32(qa0[ks], kf[ks], st0);
-            dp0 = mfma32(da0[ks], vf[ks], dp0);
+            if (ks + 2 < KS) qd_at(0, ks + 2, qw[(ks + 2) % 3], dw[(ks + 2) % 3]);
+            st0 = mfma32(qw[ks % 3], kf[ks], st0);
+            dp0 = mfma32(dw[ks % 3], vf[ks], dp0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        bf16x8 qa1[KS], da1[KS], dtr[DT][2], qtr[DT][2];
-        read_qd(1, qa1, da1);
+        bf16x8 dtr[DT][2], qtr[DT][2];
+        qd_at(1, 0, qw[0], dw[0]);
+        qd_at(1, 1, qw[1], dw[1]);
         read_tr(0, dtr, qtr);
         read_ld(0);
         __builtin_amdgcn_sched_barrier(0);
@@ -709,8 +717,9 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
         f32x16 st1 = f32x16{}, dp1 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            st1 = mfma32(qa1[ks], kf[ks], st1);
-            dp1 = mfma32(da1[ks], vf[ks], dp1);
+            if (ks + 2 < KS) qd_at(1, ks + 2, qw[(ks + 2) % 3], dw[(ks + 2) % 3]);
+            st1 = mfma32(qw[ks % 3], kf[ks], st1);
+            dp1 = mfma32(dw[ks % 3], vf[ks], dp1);
 #pragma unroll
             for (int r = 16 * ks / KS; r < 16 * (ks + 1) / KS; ++r) pds(st0, dp0, r, pv[r], dsv[r]);
             __builtin_amdgcn_sched_barrier(0);
