@@ -429,13 +429,8 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
             dp0 = mfma32(vw[ks % 3], df[ks], dp0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        bf16x8 ktr[DT][2];
         kv_at(1, 0, kw[0], vw[0]);
         kv_at(1, 1, kw[1], vw[1]);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) ktr[dt][s2] = ktr_of(0, dt, s2);
         __builtin_amdgcn_sched_barrier(0);
         mask_sub(0, st0);
         // B: sub-tile 1's S and dP with sub-tile 0's dS.
@@ -455,14 +450,22 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
         pack(dsv, dsb0);
         __builtin_amdgcn_sched_barrier(0);
         mask_sub(1, st1);
-        // C: sub-tile 0's dQ^T += K^T dS^T (K^T columns d = 32*dt + lq, keys
-        // 16*s2 + 8*hh.. of the sub-tile) with sub-tile 1's dS; each of sub-tile 1's
-        // K^T operands is read into the registers the MFMA has just taken its own from.
+        // The K^T operands of the dQ product (K^T columns d = 32*dt + lq, keys
+        // 16*s2 + 8*hh.. of a sub-tile), step x = 8*sub + 2*dt + s2 of the
+        // sixteen, go through a ring of three, two steps ahead.
+        bf16x8 ktw[3];
+        auto ktr_at = [&](int x) {
+            return ktr_of(x / (2 * DT), (x % (2 * DT)) >> 1, x & 1);
+        };
+        ktw[0] = ktr_at(0);
+        ktw[1] = ktr_at(1);
+        __builtin_amdgcn_sched_barrier(0);
+        // C: sub-tile 0's dQ^T += K^T dS^T with sub-tile 1's dS.
 #pragma unroll
         for (int x = 0; x < 2 * DT; ++x) {
             const int dt = x >> 1, s2 = x & 1;
-            o[dt] = mfma32(ktr[dt][s2], dsb0[s2], o[dt]);
-            ktr[dt][s2] = ktr_of(1, dt, s2);
+            ktw[(x + 2) % 3] = ktr_at(x + 2);
+            o[dt] = mfma32(ktw[x % 3], dsb0[s2], o[dt]);
 #pragma unroll
             for (int r = 16 * x / (2 * DT); r < 16 * (x + 1) / (2 * DT); ++r)
                 dsv[r] = fast_exp2(fmaf(st1[r], c, -lse2)) * (dp1[r] - Di);
@@ -472,9 +475,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
         pack(dsv, dsb1);
         // E: sub-tile 1's dQ.
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma32(ktr[dt][s2], dsb1[s2], o[dt]);
+        for (int x = 2 * DT; x < 4 * DT; ++x) {
+            if (x + 2 < 4 * DT) ktw[(x + 2) % 3] = ktr_at(x + 2);
+            o[(x - 2 * DT) >> 1] = mfma32(ktw[x % 3], dsb1[x & 1], o[(x - 2 * DT) >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         publish();
     };
     for (int jt = 0; jt < ntiles; jt += 2) {
@@ -643,18 +648,6 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
             qa = as_bf16x8(ld16(tq + ob));
             da = as_bf16x8(ld16(td + ob));
         };
-        // The transposed operands of dV and dK for one sub-tile.
-        auto read_tr = [&](int sub, bf16x8 (&dtr)[DT][2], bf16x8 (&qtr)[DT][2]) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int rows = (sub * 32 + 16 * s2) * RB;
-                    const int o0 = (t0 + rows) ^ (64 * dt), o1 = (t1 + rows) ^ (64 * dt);
-                    dtr[dt][s2] = ld_tr(td + o0, td + o1);
-                    qtr[dt][s2] = ld_tr(tq + o0, tq + o1);
-                }
-        };
         // log2-scaled LSE and D of the lane's rows 32*sub + 16*(r/8) + 8*hh + r%8.
         // Rows past the last read zeros (out-of-range loads), and so do their Q
         // and dO: the weight exp2(0) = 1 multiplies dO = 0 and dS = 1 * (0 - 0)
@@ -705,10 +698,8 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
             dp0 = mfma32(dw[ks % 3], vf[ks], dp0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        bf16x8 dtr[DT][2], qtr[DT][2];
         qd_at(1, 0, qw[0], dw[0]);
         qd_at(1, 1, qw[1], dw[1]);
-        read_tr(0, dtr, qtr);
         read_ld(0);
         __builtin_amdgcn_sched_barrier(0);
         mask_sub(0, st0);
@@ -728,23 +719,28 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
         pack(pv, pb0);
         pack(dsv, db0);
         read_ld(1);
+        // The transposed operands of the dV and dK products (dO / Q columns
+        // 32*dt + lq, rows 16*s2 + 8*hh.. of a sub-tile), step x = 8*sub + 2*dt +
+        // s2 of the sixteen, go through a ring of three, two steps ahead.
+        bf16x8 dtw[3], qtw[3];
+        auto tr_at = [&](int x, bf16x8& dtv, bf16x8& qtv) {
+            const int sub = x / (2 * DT), dt = (x % (2 * DT)) >> 1, s2 = x & 1;
+            const int rows = (sub * 32 + 16 * s2) * RB;
+            const int o0 = (t0 + rows) ^ (64 * dt), o1 = (t1 + rows) ^ (64 * dt);
+            dtv = ld_tr(td + o0, td + o1);
+            qtv = ld_tr(tq + o0, tq + o1);
+        };
+        tr_at(0, dtw[0], qtw[0]);
+        tr_at(1, dtw[1], qtw[1]);
         __builtin_amdgcn_sched_barrier(0);
         mask_sub(1, st1);
-        // C: sub-tile 0's dV and dK (B operands dO / Q columns 32*dt + lq, rows
-        // 16*s2 + 8*hh.. of the sub-tile, read transposed) with sub-tile 1's P and dS.
-        // (each transposed operand of sub-tile 1 is read into the registers the
-        // MFMAs of sub-tile 0 have just taken theirs from)
+        // C: sub-tile 0's dV and dK with sub-tile 1's P and dS.
 #pragma unroll
         for (int x = 0; x < 2 * DT; ++x) {
             const int dt = x >> 1, s2 = x & 1;
-            dv[dt] = mfma32(pb0[s2], dtr[dt][s2], dv[dt]);
-            dk[dt] = mfma32(db0[s2], qtr[dt][s2], dk[dt]);
-            {
-                const int rows = (32 + 16 * s2) * RB;
-                const int o0 = (t0 + rows) ^ (64 * dt), o1 = (t1 + rows) ^ (64 * dt);
-                dtr[dt][s2] = ld_tr(td + o0, td + o1);
-                qtr[dt][s2] = ld_tr(tq + o0, tq + o1);
-            }
+            tr_at(x + 2, dtw[(x + 2) % 3], qtw[(x + 2) % 3]);
+            dv[dt] = mfma32(pb0[s2], dtw[x % 3], dv[dt]);
+            dk[dt] = mfma32(db0[s2], qtw[x % 3], dk[dt]);
 #pragma unroll
             for (int r = 16 * x / (2 * DT); r < 16 * (x + 1) / (2 * DT); ++r)
                 pds(st1, dp1, r, pv[r], dsv[r]);
@@ -755,12 +751,13 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
         pack(dsv, db1);
         // E: sub-tile 1's dV and dK.
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                dv[dt] = mfma32(pb1[s2], dtr[dt][s2], dv[dt]);
-                dk[dt] = mfma32(db1[s2], qtr[dt][s2], dk[dt]);
-            }
+        for (int x = 2 * DT; x < 4 * DT; ++x) {
+            const int dt = (x - 2 * DT) >> 1, s2 = x & 1;
+            if (x + 2 < 4 * DT) tr_at(x + 2, dtw[(x + 2) % 3], qtw[(x + 2) % 3]);
+            dv[dt] = mfma32(pb1[s2], dtw[x % 3], dv[dt]);
+            dk[dt] = mfma32(db1[s2], qtw[x % 3], dk[dt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         publish();
     };
     for (int rt = t_lo; rt < t_hi; rt += 2) {
@@ -770,12 +767,14 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
     // dk[dt][r] = dK[key first + 8(r/4) + 4hh + r%4][d = 32dt + lq]
     float* dkb = is_cache ? dk_cache + (size_t)bg * a.NC * D : dk_new + (size_t)bg * S * D;
     float* dvb = is_cache ? dv_cache + (size_t)bg * a.NC * D : dv_new + (size_t)bg * S * D;
+    // The wave's 32 keys lie in one 64-slot word of the exclusion bits.
+    const uint64_t exw = (is_cache && a.excl != nullptr)
+                             ? a.excl[(size_t)bg * excl_tiles(a.NC) + first / 64] : 0ull;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int kk = first + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (kk >= limit) continue;
-        const bool ex = is_cache && a.excl != nullptr &&
-                        ((a.excl[(size_t)bg * excl_tiles(a.NC) + kk / 64] >> (kk % 64)) & 1);
+        const bool ex = (exw >> (kk % 64)) & 1;
         if (parts == 1) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
