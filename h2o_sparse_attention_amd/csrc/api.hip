@@ -147,8 +147,14 @@ const SideStream* side_stream() {
         SideStream t;
         if (hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&t.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&t.join, hipEventDisableTiming) == hipSuccess)
+            hipEventCreateWithFlags(&t.join, hipEventDisableTiming) == hipSuccess) {
             side[dev] = t;
+        } else {
+            // release whatever was made; the error is not left for the next call
+            if (t.fork) (void)hipEventDestroy(t.fork);
+            if (t.s) (void)hipStreamDestroy(t.s);
+            (void)hipGetLastError();
+        }
     }
     return side[dev].join != nullptr ? &side[dev] : nullptr;
 }
