@@ -330,25 +330,27 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(EvictArgs a) {
 }
 
 // ------------------------------------------------------------- exclusion masks
-// One thread per (b, kv head, 64-slot tile): the targets are ascending, so the
-// victims in the tile form one run, found by binary search.
-__global__ __launch_bounds__(256) void build_excl_kernel(const int32_t* __restrict__ freed,
-                                                         uint64_t* __restrict__ excl, int S,
-                                                         int n, int ntc, int rows) {
-    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= rows * ntc) return;
-    const int bg = idx / ntc, t = idx % ntc;
+// One workgroup per (b, kv head): the row's words are cleared in LDS, every
+// thread ORs in the bits of its targets below n (the slots >= n it gets are
+// empty, not keys), and the row is written out.  One load per target and no
+// dependent chain (OR does not depend on the order).
+constexpr int kExclThreads = 1024;
+constexpr int kExclMaxWords = (kMaxCapacity + 63) / 64;
+__global__ __launch_bounds__(kExclThreads) void build_excl_kernel(const int32_t* __restrict__ freed,
+                                                                  uint64_t* __restrict__ excl,
+                                                                  int S, int n, int ntc) {
+    __shared__ unsigned long long sW[kExclMaxWords];
+    const int bg = blockIdx.x;
+    for (int t = threadIdx.x; t < ntc; t += kExclThreads) sW[t] = 0ull;
+    __syncthreads();
     const int32_t* f = freed + (size_t)bg * S;
-    const int lo_slot = 64 * t, hi_slot = min(n, 64 * t + 64);
-    int lo = 0, hi = S;                     // first target >= lo_slot
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (f[mid] < lo_slot) lo = mid + 1;
-        else hi = mid;
+    for (int i = threadIdx.x; i < S; i += kExclThreads) {
+        const int slot = f[i];
+        if (slot >= 0 && slot < n) atomicOr(&sW[slot >> 6], 1ull << (slot & 63));
     }
-    uint64_t bits = 0;
-    for (int i = lo; i < S && f[i] < hi_slot; ++i) bits |= 1ull << (f[i] - lo_slot);
-    excl[idx] = bits;
+    __syncthreads();
+    uint64_t* out = excl + (size_t)bg * ntc;
+    for (int t = threadIdx.x; t < ntc; t += kExclThreads) out[t] = sW[t];
 }
 
 // ------------------------------------------------------------------ insert
@@ -566,9 +568,9 @@ hipError_t launch_select(const EvictArgs& a, hipStream_t s) {
 
 hipError_t launch_build_excl(const ChunkArgs& a, uint64_t* excl, hipStream_t s) {
     const int rows = a.B * a.Hkv, ntc = excl_tiles(a.NC);
-    const int total = rows * ntc;
-    hipLaunchKernelGGL(build_excl_kernel, dim3((total + 255) / 256), dim3(256), 0, s, a.freed,
-                       excl, a.S, a.n, ntc, rows);
+    if (ntc > kExclMaxWords) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(build_excl_kernel, dim3(rows), dim3(kExclThreads), 0, s, a.freed, excl,
+                       a.S, a.n, ntc);
     return hipGetLastError();
 }
 
