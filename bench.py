@@ -673,7 +673,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 5; 50 with --backward, whose step is one call)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default 2; 10 with --backward)")
+                    help="untimed steps first (default 2; 100 with --backward: the clocks take "
+                         "some tens of calls under 1 ms to settle)")
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
@@ -692,7 +693,7 @@ def main():
     if args.steps is None:
         args.steps = 50 if args.backward else 5
     if args.warmup is None:
-        args.warmup = 10 if args.backward else 2
+        args.warmup = 100 if args.backward else 2
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
