@@ -361,6 +361,11 @@ __global__ __launch_bounds__(kBwThreads) void bwd_dq_bf16_kernel(ChunkArgs a, co
     // each body names its stages at compile time.
     auto body = [&](auto stage_c, int jt) {
         constexpr int stage = decltype(stage_c)::value;
+        // The dQ accumulators only meet MFMAs inside the loop: keep them in AGPRs
+        // across the two bodies (left to itself the compiler moved all 64 values
+        // between VGPRs and AGPRs once per trip).
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) asm volatile("" : "+a"(o[dt]));
         if (jt + 1 < ntiles) issue(std::integral_constant<int, stage ^ 1>{}, jt + 1);
         const uint64_t ex = ex_next;
         ex_next = tile_ex(jt + 1);
