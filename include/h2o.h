@@ -296,7 +296,12 @@ H2O_API h2o_status_t h2o_evict_and_insert_lastrec(const h2o_dims_t *dims, h2o_ca
  * All gradients are float32; dk_cache and dv_cache are 0 for j >= n_valid and
  * at excluded slots.  bf16: MFMA inputs bf16 (the weights and ds rounded to
  * bf16 for their products), accumulation fp32.  The workspace must hold
- * h2o_backward_workspace_bytes(dims, chunk_len) bytes.
+ * h2o_backward_workspace_bytes(dims, chunk_len) bytes.  bf16 runs the dq
+ * kernel on a second stream of the library (one per device, default
+ * priority), forked from `stream` by an event and joined back to it before the
+ * call returns: all the call's work is ordered with respect to `stream`, also
+ * under HIP graph capture.  Concurrent calls on one device are serialised on
+ * the host while they enqueue.
  */
 H2O_API size_t h2o_backward_workspace_bytes(const h2o_dims_t *dims, int32_t chunk_len);
 H2O_API h2o_status_t h2o_chunk_attn_backward(const h2o_dims_t *dims, const h2o_cache_t *cache,
