@@ -75,7 +75,11 @@ __device__ __forceinline__ TileRef tile_ref(int tile, int cache_tiles, int n, in
 // head g*G + hl at chunk position i.  Eight waves: waves 0-3 and 4-7 (the two
 // halves) own the same four 32-row groups and split the key tiles between
 // them (tiles 0, 2, 4, ... and 1, 3, 5, ...); the two partial softmax states
-// are merged through LDS at the end.
+// are merged through LDS at the end.  When the blocks tile the rows exactly,
+// a block's four groups are two from the front of the chunk and their mirror
+// images from the back, which evens out the blocks' work: with contiguous
+// groups the last block of a 1k chunk sees 1024 more chunk keys than the
+// first, and a launch of one round of blocks lasts as long as its slowest.
 //
 // Staging.  K and V tiles go from global memory straight into LDS (buffer
 // loads with the LDS destination, 16 bytes per lane, lane-linear in LDS), so
@@ -159,10 +163,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     const int lane = tid & 63;
     // wave-uniform by construction; readfirstlane lets the compiler keep it scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kh = wave >> 2, rw = wave & 3;
+    // Row-group slot rw: the second half takes the slots in the order 2, 3, 0, 1,
+    // so waves w and w + 4, which share a SIMD, hold one front and one back row
+    // group (with both halves in slot order the balanced rows gained nothing).
+    const int kh = wave >> 2, rw = (wave & 3) ^ (2 * kh);
     const int lq = lane & 31, hh = lane >> 5;
     const int g16 = lane >> 4, j16 = lane & 15;
-    const int row = rb * kRowsPerBlock + rw * 32 + lq;
+    // Row group (32 packed rows) of slot rw.  When the blocks tile the rows
+    // exactly, block rb takes groups 2rb, 2rb+1 from the front of the chunk and
+    // their mirror images from the back.  A chunk key is visible to the rows at
+    // or after its position, so a block's front groups see few chunk tiles and
+    // its back groups many; the front groups' waves skip the tiles they cannot
+    // see, and their SIMD partners run those alone.
+    const int nrg = (R + 31) / 32;
+    const bool mirror = R % kRowsPerBlock == 0;
+    auto group_of = [&](int slot) {
+        if (!mirror) return rb * 4 + slot;
+        return slot < 2 ? 2 * rb + slot : nrg - 4 + slot - 2 * rb;
+    };
+    const int row = group_of(rw) * 32 + lq;
     const bool row_ok = row < R;
     const int i = row_ok ? row / a.G : a.S - 1;
     const int h = g * a.G + (row_ok ? row % a.G : 0);
@@ -179,11 +198,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
 
     const int n = a.n, S = a.S;
     const int cache_tiles = (n + kKeysPerTile - 1) / kKeysPerTile;
-    const int last_row = min(R - 1, rb * kRowsPerBlock + kRowsPerBlock - 1);
+    // Key tiles of the block (what its last row sees; group_of(3) holds it) and
+    // of this wave's own rows.  A half loads tiles kh, kh+2, ... of the block's
+    // range; a wave computes those within its own range (the rest are masked
+    // in full for its rows and would add nothing).
+    const int last_row = min(R - 1, group_of(3) * 32 + 31);
     const int ntiles = cache_tiles + (last_row / a.G) / kKeysPerTile + 1;
     const int steps = (ntiles + 1) / 2;
     const int mine = (ntiles - kh + 1) / 2;       // tiles of this half: kh, kh+2, ...
-    const int wave_row0 = min(R - 1, rb * kRowsPerBlock + rw * 32);
+    const int wave_row0 = min(R - 1, group_of(rw) * 32);
+    const int wave_last = min(R - 1, group_of(rw) * 32 + 31);
+    const int mine_c = (cache_tiles + (wave_last / a.G) / kKeysPerTile + 1 - kh + 1) / 2;
     const int qpos_wave_min = a.P + wave_row0 / a.G;
 
     const u16* Kc = static_cast<const u16*>(a.kc) + (size_t)bg * a.NC * D;
@@ -387,7 +412,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
     }
     if (mine > 1) issue_k(1, 1);
     publish_lds_loads();
-    if (mine > 0) {
+    if (mine_c > 0) {
         qk(sK0[kh], sA);
         const uint64_t ex0 = tile_excl(0);
         if (!tile_all_visible(0) || ex0 != 0) apply_mask(sA, tile_lim(0), ex0);
@@ -412,8 +437,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_bf16_kernel(ChunkArgs a) {
         u16* vnext = odd ? sV0[kh] : sV1[kh];
         if (jt + 2 < mine) issue_k(st_free, jt + 2);
         if (jt + 1 < mine) issue_v(vnext, jt + 1);
-        if (jt < mine) {
-            const bool has_next = jt + 1 < mine;
+        if (jt < mine_c) {
+            const bool has_next = jt + 1 < mine_c;
             bf16x8 pb[2][2];
             float lsum = 0.f;
             // Phase A: QK^T of the next tile interleaved with this tile's
