@@ -671,9 +671,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 5; 50 with --backward, whose step is one call)")
+                    help="timed steps (default 10 whole sequences; 50 with --backward, whose "
+                         "step is one call)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default 2; 100 with --backward: the clocks take "
+                    help="untimed steps first (default 3; 100 with --backward: the clocks take "
                          "some tens of calls under 1 ms to settle)")
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -691,9 +692,9 @@ def main():
                     help="lastrec: leading tokens kept (beta); the pages give no value")
     args = ap.parse_args()
     if args.steps is None:
-        args.steps = 50 if args.backward else 5
+        args.steps = 50 if args.backward else 10
     if args.warmup is None:
-        args.warmup = 100 if args.backward else 2
+        args.warmup = 100 if args.backward else 3
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
