@@ -90,12 +90,17 @@ def test_steady_chunk_full_size(key):
          recent_window=4, seq_len=90),
     dict(dtype="bf16", head_dim=128, n_q_heads=16, n_kv_heads=2, capacity=70, chunk=1,
          recent_window=4, seq_len=90),
+    dict(dtype="bf16", head_dim=128, n_q_heads=6, n_kv_heads=2, capacity=300, chunk=128,
+         recent_window=10, seq_len=768),
+    dict(dtype="bf16", head_dim=64, n_q_heads=2, n_kv_heads=2, capacity=400, chunk=256,
+         recent_window=8, seq_len=1024),
 ], ids=["bf16_d64_g3_S100", "bf16_mha_S33", "bf16_S1", "f32_d128_S65", "f32_S1", "bf16_S1_g3",
-        "bf16_S1_g8"])
+        "bf16_S1_g8", "bf16_g3_S128", "bf16_mha_S256"])
 def test_ragged_shapes(case):
     """Chunk lengths and capacities that are not tile multiples, MHA and GQA 3/4/8,
     single-token chunks (decode) at GQA 3, 4 and 8, and capacities that are not multiples
-    of the chunk."""
+    of the chunk.  GQA 3 at S = 128 and MHA at S = 256 fill whole 128-row attention blocks,
+    which then pair front and back row groups of the chunk (3 and 2 blocks per KV head)."""
     wl = W.workload(2, batch=2, heavy_count=4, sm_scale=case["head_dim"] ** -0.5, **case)
     H.run_chain(wl, range(wl.n_chunks), _chunk_getter(wl))
 
