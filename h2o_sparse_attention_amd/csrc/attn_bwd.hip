@@ -592,10 +592,39 @@ void bwd_dkdv_bf16_kernel(ChunkArgs a, const float* drow, const float* lse2, con
     };
     const int rl_base = (wave * 1024 + 16 * lane) / RB;
     const int cp = (16 * lane % RB) / 16;
+    // When a tile holds whole positions (G divides 64) and the chunk whole tiles,
+    // row rl of tile rt is head rl % G at position rt*64/G + rl/G: each load's
+    // offset is a fixed per-lane value past a base that moves by 64/G positions a
+    // tile, and no row lies past the end.  Otherwise each row is split per load.
+    const int ppt = kBwRowsPerTile / G;
+    const bool even = kBwRowsPerTile % G == 0 && S % ppt == 0;
+    int qoff[LOADS];
+#pragma unroll
+    for (int it = 0; it < LOADS; ++it) {
+        const int rl = rl_base + it * ROWS_PER_LOAD;
+        qoff[it] = (((rl % G) * S + rl / G) * D) * 2 + 16 * (cp ^ swz_kt<D>(rl));
+    }
+    const int loff = ((lane % G) * S + lane / G) * 4;
     auto issue = [&](auto stage_c, int rt) {
         constexpr int stage = decltype(stage_c)::value;
         unsigned char* dq_ = stage ? sQ1 : sQ0;
         unsigned char* dd_ = stage ? sD1 : sD0;
+        if (even) {
+            const size_t p0 = (size_t)rt * ppt;
+            const int rem = q_bytes - (int)p0 * D * 2;
+            const Rsrc rq = make_rsrc(Qg + p0 * D, rem), rd = make_rsrc(Dg + p0 * D, rem);
+#pragma unroll
+            for (int it = 0; it < LOADS; ++it) {
+                lds16(rq, dq_ + (it * kBwWaves + wave) * 1024, qoff[it]);
+                lds16(rd, dd_ + (it * kBwWaves + wave) * 1024, qoff[it]);
+            }
+            if (wave == 0) {
+                const int lrem = (G * S - (int)p0) * 4;
+                lds4(make_rsrc(Lg + p0, lrem), stage ? sL1 : sL0, loff);
+                lds4(make_rsrc(Rg + p0, lrem), stage ? sR1 : sR0, loff);
+            }
+            return;
+        }
         const Rsrc rq = make_rsrc(Qg, q_bytes), rd = make_rsrc(Dg, q_bytes);
 #pragma unroll
         for (int it = 0; it < LOADS; ++it) {
