@@ -75,6 +75,46 @@ def test_steady_chunk_full_size(key):
     H.run_chain(wl, [c], _chunk_getter(wl), cache=cache, st=st)
 
 
+def test_large_logits_lazy_rescale():
+    """Logits far past the attention kernel's lazy rescale: queries scaled by 16 and keys by
+    1 + 9 t / 512 for a key at position t, so a row's scores grow from its oldest cache
+    slots (first in the kernel's key order) to the chunk's own keys by a few hundred log2
+    units, well past the 2^8 the kernel lets its running maximum grow before it rescales O
+    and l, and most weights underflow.  bf16, d=128, GQA 4, N_C=256, S=128: chunks on an
+    empty, a half-full and a full cache (teacher-forced: the cache is loaded from the
+    oracle's state before each chunk); O, LSE and both summed weights against the oracle."""
+    wl = W.workload(2, batch=1, n_q_heads=4, n_kv_heads=1, capacity=256, recent_window=16,
+                    chunk=128, seq_len=512, heavy_count=4, sm_scale=128 ** -0.5)
+    st = oracle.H2OState.empty(wl.batch, wl.n_kv_heads, wl.capacity, wl.head_dim)
+    dt = H.TORCH_DT[wl.dtype]
+    for c in range(wl.n_chunks):
+        P = c * wl.chunk
+        x = dict(W.chunk_inputs(wl, 0, c))
+        t = P + np.arange(wl.chunk, dtype=np.float32)
+        x["q"] = W.synth.bf16_round(x["q"] * np.float32(16.0))
+        x["k"] = W.synth.bf16_round(x["k"] * (1 + 9 * t / wl.seq_len)[:, None])
+        if st.n >= 64:
+            # the growth this case is for: a row's best chunk key over its best key among
+            # the first 64 cache slots, in log2 units (fp64)
+            q = x["q"][0].astype(np.float64)                        # (Hq, S, d)
+            s_cache = np.einsum("hsd,jd->hsj", q, st.K[0, 0, :64]) * wl.sm_scale
+            s_new = np.einsum("hsd,jd->hsj", q, x["k"][0, 0].astype(np.float64)) * wl.sm_scale
+            s_new = np.where(np.tril(np.ones((wl.chunk, wl.chunk), bool)), s_new, -np.inf)
+            growth = ((s_new.max(-1) - s_cache.max(-1)) * np.log2(np.e)).max()
+            assert growth > 256, f"chunk {c}: growth {growth:.0f} log2 units: the case is too mild"
+        cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+        H.load_oracle_state(cache, st, wl.dtype)
+        out, lse, cs_c, cs_n = h2o.chunk_attn(cache, P, H.dev(x["q"], dt), H.dev(x["k"], dt),
+                                              H.dev(x["v"], dt), wl.sm_scale)
+        torch.cuda.synchronize()
+        r_out, r_lse, r_cc, r_cn = oracle.attend_chunk(st, x["q"], x["k"], x["v"], wl.sm_scale)
+        g = {"out": H.host(out), "lse": H.host(lse), "colsum_cache": H.host(cs_c),
+             "colsum_new": H.host(cs_n)}
+        r = {"out": r_out, "lse": r_lse, "colsum_cache": r_cc, "colsum_new": r_cn}
+        H.compare_attention(g, r, st.n, wl.dtype, where=f"chunk {c}:")
+        oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window)
+
+
 @pytest.mark.parametrize("case", [
     dict(dtype="bf16", head_dim=64, n_q_heads=6, n_kv_heads=2, capacity=300, chunk=100,
          recent_window=10, seq_len=700),
