@@ -336,6 +336,34 @@ def test_decode_teacher_forced_then_free_running():
     print(f"decode: near-tie swaps teacher-forced {tf}, free-running {free}")
 
 
+def test_decode_large_logits():
+    """Decode steps whose scores span hundreds of log2 units across the split-KV partials:
+    cache keys scaled by 1 + 9 j / N_C at slot j and the query by 16, so the four
+    4096-slot splits' maxima differ by 500-700 log2 units (the merge scales the lower
+    partials to zero) and most weights underflow.  One sequence, GQA 4, N_C 16384 full;
+    O, LSE and the summed weights against the oracle for two teacher-forced steps."""
+    wl = W.workload(5, batch=1, n_q_heads=4, n_kv_heads=1)
+    s = W.decode_initial_state(wl)
+    ramp = (1 + 9 * np.arange(wl.capacity, dtype=np.float32) / wl.capacity)[:, None]
+    s["k"] = W.synth.bf16_round(s["k"] * ramp)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    dt = H.TORCH_DT[wl.dtype]
+    for t in range(2):
+        x = dict(W.decode_step_inputs(wl, t))
+        x["q"] = W.synth.bf16_round(x["q"] * np.float32(16.0))
+        cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+        H.load_oracle_state(cache, st, wl.dtype)
+        out, lse, cs_c, cs_n = h2o.chunk_attn(cache, st.P, H.dev(x["q"], dt), H.dev(x["k"], dt),
+                                              H.dev(x["v"], dt), wl.sm_scale)
+        torch.cuda.synchronize()
+        r_out, r_lse, r_cc, r_cn = oracle.attend_chunk(st, x["q"], x["k"], x["v"], wl.sm_scale)
+        g = {"out": H.host(out), "lse": H.host(lse), "colsum_cache": H.host(cs_c),
+             "colsum_new": H.host(cs_n)}
+        r = {"out": r_out, "lse": r_lse, "colsum_cache": r_cc, "colsum_new": r_cn}
+        H.compare_attention(g, r, st.n, wl.dtype, where=f"step {t}:")
+        oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window)
+
+
 def test_decode_grid_beyond_resident_capacity():
     """Decode with 160 (sequence, KV head) rows of 16384 slots: 640 split workgroups,
     more than a 256-CU device holds at once, so the summed weights go through the
