@@ -75,6 +75,17 @@ def test_steady_chunk_full_size(key):
     H.run_chain(wl, [c], _chunk_getter(wl), cache=cache, st=st)
 
 
+def test_steady_chunk_max_capacity():
+    """One evicting 1k chunk on a full cache at the largest capacity the library takes
+    (32768 slots, W 512, 8 query / 2 KV heads): 513 key tiles per attention block, the
+    summed weights' row split at that size, and the 32-slots-per-thread selection."""
+    wl = W.workload(2, batch=1, n_q_heads=8, n_kv_heads=2, capacity=32768, recent_window=512,
+                    chunk=1024, seq_len=65536)
+    c = 40
+    cache, st = _steady(wl, start=c * wl.chunk)
+    H.run_chain(wl, [c], _chunk_getter(wl), cache=cache, st=st)
+
+
 def test_large_logits_lazy_rescale():
     """Logits far past the attention kernel's lazy rescale: queries scaled by 16 and keys by
     1 + 9 t / 512 for a key at position t, so a row's scores grow from its oldest cache
