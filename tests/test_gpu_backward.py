@@ -195,3 +195,13 @@ def test_backward_positions_outside_chunk_start(dtype, head_dim):
             st.pos[b, g, idx[:20]] = -1
             st.pos[b, g, idx[20:]] = st.P + r.integers(0, wl.chunk + 64, 20)
     check_backward(wl, st, W.chunk_inputs(wl, 0, 20), seed=3, where="positions")
+
+
+def test_backward_max_capacity():
+    """Chunk 1k from a full cache at the largest capacity (32768 slots, 4 query heads on
+    one KV head): 512 cache key tiles per dQ block and 256 key blocks for dK/dV."""
+    wl = W.workload(2, batch=1, n_q_heads=4, n_kv_heads=1, capacity=32768, recent_window=512,
+                    chunk=1024, seq_len=65536)
+    s = W.steady_state(wl, 0, start=40 * wl.chunk)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    check_backward(wl, st, W.chunk_inputs(wl, 0, 40), seed=40)

@@ -183,3 +183,16 @@ def test_buffer_decode_full_cache():
     H.load_oracle_state(cache, st, wl.dtype)
     del s
     run_buffer_chain(wl, range(3), lambda t: W.decode_step_inputs(wl, t), cache=cache, st=st)
+
+
+def test_buffer_steady_chunk_max_capacity():
+    """The buffer form at the largest capacity (32768 slots, chunk 1k, 8 query / 2 KV
+    heads): 1024 of 32768 slots excluded, the exclusion bits at their 512-word limit."""
+    wl = W.workload(2, batch=1, n_q_heads=8, n_kv_heads=2, capacity=32768, recent_window=512,
+                    chunk=1024, seq_len=65536)
+    c = 40
+    s = W.steady_state(wl, 0, start=c * wl.chunk)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    run_buffer_chain(wl, [c], _chunks(wl), cache=cache, st=st)
