@@ -152,6 +152,26 @@ def check_exact_when_no_eviction(orc, seed=2, S=8):
     np.testing.assert_allclose(phi_by_pos, colsum, rtol=1e-12, atol=1e-12)
 
 
+def check_large_logits(orc, seed=15, S=8):
+    """Logits in the thousands (queries scaled by 300): with each row's maximum taken out
+    before the exponentials, output and lse still equal torch's fp64 SDPA and logsumexp of
+    the causal logits; without it the exponentials overflow."""
+    q, k, v = random_problem(seed, N=40)
+    q = q * 300.0
+    sm = 0.37
+    N = q.shape[2]
+    st, steps = run_chain(orc, q, k, v, S, NC=64, W=3, sm_scale=sm)
+    out = np.concatenate([r["out"] for r in steps], axis=2)
+    lse = np.concatenate([r["lse"] for r in steps], axis=2)
+    G = q.shape[1] // k.shape[1]
+    logits = torch.from_numpy(q) @ torch.from_numpy(np.repeat(k, G, axis=1)).transpose(-1, -2)
+    logits = (logits * sm).masked_fill(~torch.ones(N, N, dtype=torch.bool).tril(), float("-inf"))
+    want_lse = torch.logsumexp(logits, dim=-1).numpy()
+    assert np.abs(want_lse).max() > 1000, "logits not large enough for this check"
+    np.testing.assert_allclose(out, exact_causal_sdpa(q, k, v, sm), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, want_lse, rtol=1e-13, atol=0)
+
+
 def check_chunk_size_invariance(orc, seed=3):
     """Without eviction the results do not depend on the chunk length (1, 7, 16)."""
     q, k, v = random_problem(seed, N=32)
@@ -537,6 +557,7 @@ def check_backward_finite_differences(orc, seed=14):
 
 
 ALL_CHECKS = [check_golden, check_rows_normalised, check_exact_when_no_eviction,
+              check_large_logits,
               check_chunk_size_invariance, check_uniform_closed_form,
               check_bruteforce_selection, check_decode_is_argmin, check_dense_masked_replay,
               check_conservation_and_monotonicity, check_slot_permutation_invariance,

@@ -35,6 +35,8 @@ MUTANTS = [
      "keys used as values"),
     ("lse[b, h] = row_max[:, 0] + np.log(row_sum[:, 0])", "lse[b, h] = np.log(row_sum[:, 0])",
      "lse without the row max"),
+    ("row_max = s.max(axis=1, keepdims=True)", "row_max = np.zeros_like(s[:, :1])",
+     "softmax without its max subtraction"),
     ("victims[b, g] = np.sort(eligible[order[:k]])", "victims[b, g] = np.sort(eligible[order[-k:]])",
      "largest scores evicted"),
     ("np.arange(state.n, n_new)", "np.arange(state.n + 1, n_new + 1)", "empty slots off by one"),
