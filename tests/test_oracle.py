@@ -43,6 +43,8 @@ MUTANTS = [
     ("state.pos[b, g, j] = state.P + i", "state.pos[b, g, j] = state.P + i + 1",
      "inserted position off by one"),
     ("t_now = state.P + S", "t_now = state.P", "h2o-norm age off by S"),
+    ("return state.phi / (t_now - state.pos).astype(np.float64)",
+     "return state.phi / (t_now - state.pos + 1).astype(np.float64)", "h2o-norm age plus one"),
     ("state.pos[b, g, :n] >= beta", "state.pos[b, g, :n] > beta", "lastrec sink off by one"),
     ("np.sort(eligible[oldest[:k]])", "np.sort(eligible[oldest[-k:]])", "lastrec evicts newest"),
     ("    update_scores(state, colsum)\n", "    update_scores(state, colsum * 0.5)\n",
