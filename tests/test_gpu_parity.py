@@ -375,6 +375,25 @@ def test_decode_large_logits():
         oracle.h2o_step(st, x["q"], x["k"], x["v"], wl.sm_scale, wl.recent_window)
 
 
+@pytest.mark.parametrize("score_mode", ["h2o", "h2o_norm"])
+def test_decode_max_capacity(score_mode):
+    """Decode on a full cache at the largest capacity (32768 slots, two sequences, 8 query /
+    2 KV heads): each row's slots go in eight 4096-slot splits through the in-kernel LSE
+    exchange, and the victim is the argmin over 32768 - 512 eligible slots.  Two
+    teacher-forced steps, then two free-running ones."""
+    wl = W.workload(5, batch=2, n_q_heads=8, n_kv_heads=2, capacity=32768)
+    s = W.decode_initial_state(wl)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    del s
+    steps = lambda t: W.decode_step_inputs(wl, t)  # noqa: E731
+    H.run_chain(wl, range(2), steps, cache=cache, st=st, resync="scores",
+                score_mode=score_mode, rows="freed")
+    H.run_chain(wl, range(2, 4), steps, cache=cache, st=st, score_mode=score_mode,
+                rows="freed")
+
+
 def test_decode_grid_beyond_resident_capacity():
     """Decode with 160 (sequence, KV head) rows of 16384 slots: 640 split workgroups,
     more than a 256-CU device holds at once, so the summed weights go through the
