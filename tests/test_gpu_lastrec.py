@@ -102,16 +102,22 @@ def test_lastrec_one_victim_with_empty_targets():
             assert set(H.host(cache.pos)[b, g].tolist()) == want
 
 
-@pytest.mark.parametrize("key,sink", [(2, 64), (3, 1000)])
+@pytest.mark.parametrize("key,sink", [(2, 64), (3, 1000), ("max", 4)])
 def test_lastrec_isolated_full_size(key, sink):
-    """Eviction alone from a full cache in random slot order (chunk 1k / N_C 8192 and
-    chunk 2k / N_C 16384): same victims, rows, positions and zero scores as the oracle."""
-    wl = W.WORKLOADS[key]
-    s = W.steady_state(wl, 0, start=20 * wl.chunk, seed=key)
+    """Eviction alone from a full cache in random slot order (chunk 1k / N_C 8192,
+    chunk 2k / N_C 16384, and chunk 1k at the 32768-slot maximum with 8 query / 2 KV
+    heads): same victims, rows, positions and zero scores as the oracle."""
+    if key == "max":
+        wl = W.workload(2, batch=1, n_q_heads=8, n_kv_heads=2, capacity=32768,
+                        recent_window=512, chunk=1024, seq_len=65536)
+        c, seed = 40, 4
+    else:
+        wl, c, seed = W.WORKLOADS[key], 20, key
+    s = W.steady_state(wl, 0, start=c * wl.chunk, seed=seed)
     st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
     cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
     H.load_oracle_state(cache, st, wl.dtype)
-    x = W.chunk_inputs(wl, 0, 20)
+    x = W.chunk_inputs(wl, 0, c)
     k, v = H.dev(x["k"], torch.bfloat16), H.dev(x["v"], torch.bfloat16)
     freed = h2o.evict_and_insert_lastrec(cache, st.P, k, v, sink)
     torch.cuda.synchronize()
@@ -134,6 +140,21 @@ def test_lastrec_decode_full_cache():
     run_lastrec_chain(wl, range(3), lambda t: W.decode_step_inputs(wl, t), 4, cache=cache,
                       st=st)
     assert (H.host(cache.pos)[:, :, 4:7] == np.arange(16384, 16387)).all()
+
+
+def test_lastrec_decode_max_capacity():
+    """Decode at the 32768-slot maximum (two sequences, 8 query / 2 KV heads), beta = 4:
+    three single-token steps over eight 4096-slot splits, each evicting the oldest
+    non-sink slot."""
+    wl = W.workload(5, batch=2, n_q_heads=8, n_kv_heads=2, capacity=32768)
+    s = W.decode_initial_state(wl)
+    st = oracle.H2OState.from_arrays(s["k"], s["v"], s["pos"], s["phi"], s["n"], s["start"])
+    cache = h2o.H2OCache(H.dims_of(wl), H.DEV)
+    H.load_oracle_state(cache, st, wl.dtype)
+    del s
+    run_lastrec_chain(wl, range(3), lambda t: W.decode_step_inputs(wl, t), 4, cache=cache,
+                      st=st)
+    assert (H.host(cache.pos)[:, :, 4:7] == np.arange(32768, 32771)).all()
 
 
 def _attn_both_ways(wl, cache, x):
