@@ -58,6 +58,9 @@ MUTANTS = [
      "backward without the row term"),
     ("dkeys += sm_scale * (ds.T @ q[b, h])", "dkeys += ds.T @ q[b, h]", "backward dK unscaled"),
     ("dvalues += m.T @ dout[b, h]", "dvalues += 0.5 * (m.T @ dout[b, h])", "backward dV halved"),
+    ("dq[b, h] = sm_scale * (ds @ keys)", "dq[b, h] = ds @ keys", "backward dQ unscaled"),
+    ("h = g * G + hh", "h = hh * Hkv + g", "query heads interleaved over the KV heads"),
+    ("return max(0, n + S - NC)", "return max(0, n + S - NC + 1)", "one eviction too many"),
 ]
 
 
