@@ -10,7 +10,10 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libh2o.so")
+# H2O_LIB_PATH loads another build of the same library (for instance the host-sanitizer
+# build that the CPU tests make); by default the in-tree build.
+LIB_PATH = os.environ.get("H2O_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libh2o.so")
 
 H2O_OK = 0
 H2O_ERR_INVALID_ARG = -1

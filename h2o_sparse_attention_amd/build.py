@@ -69,5 +69,44 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer, on the host pass only (the
+# device code is built as usual); the runtime is linked as a shared library, which the
+# process that loads this build must preload (clang -print-file-name gives its path).
+HOST_SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+
+
+def asan_runtime() -> str:
+    """Path of the shared ASan runtime of ROCm's clang (it carries the UBSan handlers too)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "lib", "llvm",
+                         "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    out = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout.strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise RuntimeError(f"ASan runtime not found (clang printed {out!r})")
+    return out
+
+
+def build_host_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """Build the same sources into out_dir/libh2o_san.so with the host code under ASan and
+    UBSan (-O1 -g, frame pointers kept); return its path. Loading it needs the ASan
+    runtime preloaded (LD_PRELOAD=asan_runtime())."""
+    hipcc = _hipcc()
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f for f in CXXFLAGS if f != "-O3"] + ["-O1", "-g", "-fno-omit-frame-pointer"]
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(out_dir, src.replace(".hip", ".san.o"))
+        objs.append(obj)
+        cmds.append([hipcc, *flags, *HOST_SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    lib = os.path.join(out_dir, "libh2o_san.so")
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan", *HOST_SAN_FLAGS,
+          "-o", lib, *objs], verbose)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="--verbose" in sys.argv))
